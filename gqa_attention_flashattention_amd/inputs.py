@@ -1,0 +1,139 @@
+"""Seeded synthetic inputs for the GQA attention workloads.
+
+This module holds no attention arithmetic: it only draws random tensors and
+rounds them to the storage type, so that the HIP path and the CPU oracle can
+be fed the very same bytes.  It imports nothing else from this package.
+
+Recipe (identical for every workload):
+  rng = numpy.random.default_rng(seed)          # PCG64, default seed 0
+  kv_len   (varlen decode only) rng.integers(lo, hi, endpoint=True, size=B)
+  Q, K, V  rng.standard_normal(shape, dtype=float32), drawn in that order
+  bf16 workloads: each value rounded to bfloat16, round-to-nearest-even.
+The shapes are the Llama3-70B attention geometry the ADR-0060 page uses
+(section 0, reference dimensions: H_q = 64, H_kv = 8, d = 128), plus one tiny
+fp32 case.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str               # "prefill" or "decode"
+    dtype: str              # "bf16" or "f32"
+    B: int
+    H_q: int
+    H_kv: int
+    d: int
+    T_q: int = 1            # prefill only
+    S_kv: int = 0           # prefill keys, or fixed decode length
+    causal: bool = False
+    q_offset: int = 0
+    kv_len_range: tuple | None = None   # varlen decode: (lo, hi) inclusive
+
+    @property
+    def G(self) -> int:
+        return self.H_q // self.H_kv
+
+    @property
+    def scale(self) -> float:
+        return float(1.0 / np.sqrt(self.d))
+
+
+WORKLOADS = {
+    w.name: w for w in [
+        Workload("prefill_tiny_f32", "prefill", "f32", B=1, H_q=8, H_kv=1, d=64,
+                 T_q=128, S_kv=128, causal=True),
+        Workload("decode_8k", "decode", "bf16", B=1, H_q=64, H_kv=8, d=128, S_kv=8192),
+        Workload("decode_varlen_b16", "decode", "bf16", B=16, H_q=64, H_kv=8, d=128,
+                 kv_len_range=(1024, 32768)),
+        Workload("prefill_8k_causal", "prefill", "bf16", B=1, H_q=64, H_kv=8, d=128,
+                 T_q=8192, S_kv=8192, causal=True),
+        Workload("decode_128k", "decode", "bf16", B=1, H_q=64, H_kv=8, d=128, S_kv=131072),
+        Workload("prefill_chunk_64k", "prefill", "bf16", B=1, H_q=64, H_kv=8, d=128,
+                 T_q=2048, S_kv=67584, causal=True, q_offset=65536),
+    ]
+}
+
+
+def bf16_round_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest, ties to even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    bias = ((u >> 16) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> the exactly equal float32 values."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclasses.dataclass
+class Inputs:
+    """q, k, v as float32 arrays holding exactly the stored values, plus the
+    raw storage bits (uint16 for bf16, the float32 arrays themselves for f32)."""
+    workload: Workload
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    q_store: np.ndarray
+    k_store: np.ndarray
+    v_store: np.ndarray
+    kv_len: np.ndarray | None = None    # int32 [B], decode only
+
+
+def kv_lengths(w: Workload, rng: np.random.Generator) -> np.ndarray:
+    if w.kind != "decode":
+        return None
+    if w.kv_len_range is not None:
+        lo, hi = w.kv_len_range
+        return rng.integers(lo, hi, endpoint=True, size=w.B).astype(np.int32)
+    return np.full((w.B,), w.S_kv, np.int32)
+
+
+def shapes(w: Workload, kv_len: np.ndarray | None):
+    if w.kind == "prefill":
+        return ((w.B, w.T_q, w.H_q, w.d), (w.B, w.S_kv, w.H_kv, w.d))
+    total = int(np.asarray(kv_len, np.int64).sum())
+    return ((w.B, w.H_q, w.d), (total, w.H_kv, w.d))
+
+
+def make(w: Workload | str, seed: int = 0) -> Inputs:
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    rng = np.random.default_rng(seed)
+    kv_len = kv_lengths(w, rng)
+    qs, ks = shapes(w, kv_len)
+    q = rng.standard_normal(qs, dtype=np.float32)
+    k = rng.standard_normal(ks, dtype=np.float32)
+    v = rng.standard_normal(ks, dtype=np.float32)
+    if w.dtype == "bf16":
+        qb, kb, vb = bf16_round_bits(q), bf16_round_bits(k), bf16_round_bits(v)
+        return Inputs(w, bf16_bits_to_f32(qb), bf16_bits_to_f32(kb), bf16_bits_to_f32(vb),
+                      qb, kb, vb, kv_len)
+    return Inputs(w, q, k, v, q, k, v, kv_len)
+
+
+def random_case(kind: str, dtype: str, *, B: int, H_q: int, H_kv: int, d: int, T_q: int = 1,
+                S_kv: int = 0, kv_len=None, seed: int = 0, q_scale: float = 1.0) -> Inputs:
+    """A seeded case of arbitrary shape (tests).  ``q_scale`` multiplies Q
+    before rounding (peaky softmax inputs)."""
+    w = Workload("custom", kind, dtype, B=B, H_q=H_q, H_kv=H_kv, d=d, T_q=T_q, S_kv=S_kv)
+    rng = np.random.default_rng(seed)
+    if kind == "decode":
+        kv_len = np.asarray(kv_len if kv_len is not None else [S_kv] * B, np.int32)
+    qs, ks = shapes(w, kv_len)
+    q = rng.standard_normal(qs, dtype=np.float32) * np.float32(q_scale)
+    k = rng.standard_normal(ks, dtype=np.float32)
+    v = rng.standard_normal(ks, dtype=np.float32)
+    if dtype == "bf16":
+        qb, kb, vb = bf16_round_bits(q), bf16_round_bits(k), bf16_round_bits(v)
+        return Inputs(w, bf16_bits_to_f32(qb), bf16_bits_to_f32(kb), bf16_bits_to_f32(vb),
+                      qb, kb, vb, kv_len)
+    return Inputs(w, q, k, v, q, k, v, kv_len)

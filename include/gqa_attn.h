@@ -1,0 +1,159 @@
+/*
+ * gqa_attn.h -- C ABI of libgqa_attn.so: grouped-query fused attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (ADR-0060 page, "AHBM GQA Fused Attention kernel
+ * (Llama3-70B)"): every KV head serves G = H_q / H_kv query heads, query
+ * head h reading KV head h / G (TL;DR pseudocode and section 5.2: the G
+ * query heads are folded into the M dimension of both matrix products, K and
+ * V are never broadcast).  Per query row the result is
+ *     O = softmax(scale * q K^T + mask) V,   LSE = ln sum_j exp(scale * q.k_j)
+ * over the keys the row may see, computed FlashAttention-style: K/V tiles
+ * are streamed, an online softmax keeps a running max m, running sum l and
+ * running output O (section 3, per-tile op sequence) and the score matrix is
+ * never stored.  Causal prefill skips key tiles that lie wholly in the future
+ * and masks only boundary tiles (section 5.4).  Decode splits each sequence's
+ * keys across work-groups, each returning an unnormalised partial (m, l, O),
+ * and a log-sum-exp merge reduces them (section 4, FlashDecoding).
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers (HIP global memory) unless marked
+ *    HOST.  All tensors are dense, row-major, with no padding.  The caller
+ *    allocates and owns every buffer passed in; the library never frees or
+ *    retains them after the call returns.  q, k, v are only read.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
+ *    enqueued on it and the call returns without synchronising; outputs are
+ *    valid once the stream has reached that point.
+ *  - Return value: GQA_OK (0) or a gqa_status code.  Argument errors are
+ *    detected on the host before anything is enqueued, so a failed call has
+ *    no effect on device memory.  No entry point aborts, throws or prints.
+ *  - dtype: GQA_BF16 (storage bf16, fp32 accumulation and softmax state) or
+ *    GQA_F32 (fp32 storage and arithmetic throughout, no reduced-precision
+ *    matrix instructions).  Head dim d must be 64 or 128.
+ *  - Calls are thread-safe with respect to each other except that
+ *    gqa_attn_decode's internal workspace is per device and per process:
+ *    concurrent gqa_attn_decode calls on different streams of one device
+ *    must be serialised by the caller (or use gqa_attn_decode_split /
+ *    gqa_attn_decode_combine with caller-owned workspaces).
+ */
+#ifndef GQA_ATTN_H
+#define GQA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GQA_OK = 0,
+    GQA_ERR_NULL = 1,        /* a required pointer is NULL */
+    GQA_ERR_SHAPE = 2,       /* sizes < 1, H_q % H_kv != 0, kv_len[b] < 1, too large */
+    GQA_ERR_UNSUPPORTED = 3, /* head dim / dtype combination not built */
+    GQA_ERR_RANGE = 4,       /* causal q_offset out of range, workspace too small */
+    GQA_ERR_HIP = 5          /* the HIP runtime reported an error (launch, alloc) */
+} gqa_status;
+
+typedef enum { GQA_BF16 = 0, GQA_F32 = 1 } gqa_dtype;
+
+/* Human-readable text for a gqa_status value (static storage, never NULL). */
+const char *gqa_attn_status_string(int status);
+
+/* Library version as an integer MAJOR*10000 + MINOR*100 + PATCH. */
+int gqa_attn_version(void);
+
+/*
+ * Prefill / chunked prefill (ADR-0060 sections 3, 5.4).
+ *   q   [B, T_q, H_q, d]     o [B, T_q, H_q, d]        (dtype)
+ *   k,v [B, S_kv, H_kv, d]                              (dtype)
+ *   lse [B, T_q, H_q] fp32, natural log of sum_j exp(scale q.k_j); may be NULL.
+ * causal != 0: the query at row t sits at absolute position q_offset + t and
+ * sees key j iff j <= q_offset + t (diagonal included; requires
+ * 0 <= q_offset and q_offset + T_q <= S_kv).  causal == 0: every query sees
+ * all S_kv keys and q_offset is ignored.  `scale` multiplies q.k before the
+ * softmax (1/sqrt(d) for standard attention).
+ * Errors: GQA_ERR_NULL (q, k, v or o NULL), GQA_ERR_SHAPE, GQA_ERR_UNSUPPORTED,
+ * GQA_ERR_RANGE (bad q_offset), GQA_ERR_HIP.
+ */
+int gqa_attn_prefill(const void *q, const void *k, const void *v, void *o, float *lse,
+                     int B, int T_q, int S_kv, int H_q, int H_kv, int d, float scale,
+                     int causal, int q_offset, int dtype, void *stream);
+
+/*
+ * Decode, one new token per sequence (ADR-0060 sections 4, 5.2, 5.3).
+ *   q   [B, H_q, d]            o [B, H_q, d]            (dtype)
+ *   k,v [sum_b kv_len[b], H_kv, d], sequences packed back to back: sequence b
+ *       occupies rows off_b .. off_b + kv_len[b] - 1, off_b = sum_{b'<b} kv_len[b'].
+ *   kv_len: HOST array [B] of int32, every entry >= 1.
+ * Each query attends to all keys of its sequence (no mask).  The keys of each
+ * (sequence, KV head) are cut into contiguous splits as gqa_attn_decode_plan
+ * describes: num_splits > 0 caps the splits per sequence at that number,
+ * num_splits <= 0 lets the library choose.  Launches the
+ * split kernel then the combine kernel on `stream`, using a workspace that the
+ * library allocates on first use per device and grows on demand (a hipMalloc
+ * may therefore happen inside this call; use gqa_attn_decode_split/_combine
+ * with a caller-owned workspace to avoid that).
+ * Errors: GQA_ERR_NULL, GQA_ERR_SHAPE, GQA_ERR_UNSUPPORTED, GQA_ERR_HIP.
+ */
+int gqa_attn_decode(const void *q, const void *k, const void *v, void *o, int B, int H_q,
+                    int H_kv, int d, const int32_t *kv_len, float scale, int num_splits,
+                    int dtype, void *stream);
+
+/*
+ * Split plan (host only, no device access).  Sequence b is cut into
+ * n_b = ceil(kv_len[b] / L_b) splits of L_b keys (the last may be shorter),
+ * split s covering keys [s*L_b, min((s+1)*L_b, kv_len[b])):
+ *   num_splits > 0:  L_b = ceil(kv_len[b] / min(num_splits, kv_len[b])), so
+ *                    n_b <= num_splits (fewer when the division rounds up);
+ *   num_splits <= 0: L_b = L for all b, a multiple of 64 chosen so that
+ *                    H_kv * sum_b n_b is about four work-groups per compute
+ *                    unit, with L between 128 and 8192.
+ * Writes (every output pointer may be NULL):
+ *   splits[b]        n_b (HOST array [B]),
+ *   *split_len       L_b of the longest split over all sequences,
+ *   *total_splits    sum_b n_b,
+ *   *max_splits      max_b n_b,
+ *   *workspace_bytes total_splits * H_q * (d + 2) * 4, the partials workspace
+ *                    gqa_attn_decode_split needs.
+ * Errors: GQA_ERR_NULL (kv_len NULL), GQA_ERR_SHAPE.
+ */
+int gqa_attn_decode_plan(int B, int H_q, int H_kv, int d, const int32_t *kv_len,
+                         int num_splits, int32_t *splits, int *split_len,
+                         int64_t *total_splits, int *max_splits, size_t *workspace_bytes);
+
+/*
+ * Decode step 1 of 2 (FlashDecoding split, ADR-0060 section 5.3): for every
+ * (sequence b, KV head, split) writes the unnormalised partial of its G query
+ * heads into `workspace` (device, fp32, at least workspace_bytes of
+ * gqa_attn_decode_plan for the same arguments, 256-byte aligned):
+ *   m [total_splits][H_q], l [total_splits][H_q], O [total_splits][H_q][d]
+ * where split p = (sum_{b'<b} n_b') + s runs over sequences in order and
+ * splits in key order (gqa_attn_decode_plan gives n_b);
+ * m is the running max of scale * q.k in base-2 units (scores multiplied by
+ * log2(e)), l = sum 2^(s2 - m), O = sum 2^(s2 - m) v.
+ * Errors: as gqa_attn_decode, plus GQA_ERR_RANGE if workspace_bytes is too small.
+ */
+int gqa_attn_decode_split(const void *q, const void *k, const void *v, void *workspace,
+                          size_t workspace_bytes, int B, int H_q, int H_kv, int d,
+                          const int32_t *kv_len, float scale, int num_splits, int dtype,
+                          void *stream);
+
+/*
+ * Decode step 2 of 2 (log-sum-exp combine, ADR-0060 section 4 merge): for
+ * every (b, query head) merges the partials of its splits, in split order,
+ * normalises once and writes o [B, H_q, d] (dtype) and, if lse != NULL,
+ * lse [B, H_q] fp32 (natural log).  `workspace` must hold what
+ * gqa_attn_decode_split wrote for the same B, H_q, H_kv, d, kv_len, num_splits.
+ * Errors: GQA_ERR_NULL, GQA_ERR_SHAPE, GQA_ERR_UNSUPPORTED, GQA_ERR_RANGE,
+ * GQA_ERR_HIP.
+ */
+int gqa_attn_decode_combine(const void *workspace, size_t workspace_bytes, void *o,
+                            float *lse, int B, int H_q, int H_kv, int d,
+                            const int32_t *kv_len, int num_splits, int dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_ATTN_H */

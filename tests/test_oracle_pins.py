@@ -1,0 +1,80 @@
+"""The fp64 oracle against facts fixed by mathematics (CPU only)."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import oracle_np
+
+from oracle_pins import ALL_PINS
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
+def test_c_oracle_pin(pin):
+    pin(oracle)
+
+
+class _NumpyOracle:
+    """The NumPy formulation, exposed with the same call shape as the C one."""
+
+    @staticmethod
+    def prefill(q, k, v, *, causal, q_offset=0, scale=None):
+        return oracle_np.prefill(q, k, v, causal=causal, q_offset=q_offset, scale=scale)
+
+    @staticmethod
+    def decode(q, k, v, kv_len, *, scale=None, num_splits=0):
+        # the NumPy form has no split path; it answers the unsplit definition
+        return oracle_np.decode(q, k, v, kv_len, scale=scale)
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
+def test_numpy_oracle_pin(pin):
+    pin(_NumpyOracle)
+
+
+@pytest.mark.parametrize("causal,q_offset,T,S", [(True, 0, 33, 33), (True, 17, 16, 40),
+                                                  (False, 0, 21, 50)])
+def test_c_matches_numpy(causal, q_offset, T, S):
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((2, T, 8, 32)).astype(np.float32)
+    k = rng.standard_normal((2, S, 2, 32)).astype(np.float32)
+    v = rng.standard_normal((2, S, 2, 32)).astype(np.float32)
+    o, lse = oracle.prefill(q, k, v, causal=causal, q_offset=q_offset)
+    o2, lse2 = oracle_np.prefill(q, k, v, causal=causal, q_offset=q_offset)
+    assert np.max(np.abs(o - o2)) <= 1e-12
+    assert np.max(np.abs(lse - lse2)) <= 1e-12
+
+
+def test_rows_subset_matches_full():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((2, 10, 4, 8)).astype(np.float32)
+    k = rng.standard_normal((2, 12, 2, 8)).astype(np.float32)
+    v = rng.standard_normal((2, 12, 2, 8)).astype(np.float32)
+    o, lse = oracle.prefill(q, k, v, causal=True, q_offset=2)
+    rows = np.array([0, 5, 79, 33], np.int64)
+    os_, ls_ = oracle.prefill(q, k, v, causal=True, q_offset=2, rows=rows)
+    assert np.array_equal(os_, o.reshape(-1, 8)[rows])
+    assert np.array_equal(ls_, lse.reshape(-1)[rows])
+    kv_len = np.array([3, 9], np.int32)
+    kd = rng.standard_normal((12, 2, 8)).astype(np.float32)
+    vd = rng.standard_normal((12, 2, 8)).astype(np.float32)
+    qd = rng.standard_normal((2, 4, 8)).astype(np.float32)
+    o, lse = oracle.decode(qd, kd, vd, kv_len)
+    rows = np.array([7, 1], np.int64)
+    os_, ls_ = oracle.decode(qd, kd, vd, kv_len, rows=rows)
+    assert np.array_equal(os_, o.reshape(-1, 8)[rows])
+    assert np.array_equal(ls_, lse.reshape(-1)[rows])
+
+
+def test_oracle_rejects_bad_arguments():
+    q = np.zeros((1, 4, 3, 8), np.float32)
+    k = np.zeros((1, 4, 2, 8), np.float32)
+    with pytest.raises(ValueError):
+        oracle.prefill(q, k, k, causal=True)            # H_q % H_kv != 0
+    q = np.zeros((1, 4, 4, 8), np.float32)
+    with pytest.raises(ValueError):
+        oracle.prefill(q, k, k, causal=True, q_offset=1)   # q_offset + T_q > S_kv
+    with pytest.raises(ValueError):
+        oracle.decode(np.zeros((1, 4, 8), np.float32), np.zeros((3, 2, 8), np.float32),
+                      np.zeros((3, 2, 8), np.float32), np.array([0], np.int32))
+    with pytest.raises(ValueError):
+        oracle.prefill(np.full((1, 1, 2, 2), 0.1), k[:, :, :, :2], k[:, :, :, :2], causal=False)
