@@ -1,0 +1,219 @@
+"""ctypes binding of libgqa_attn.so (C ABI in include/gqa_attn.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the library.  Tensors are torch tensors that live on the GPU;
+torch supplies device memory and the current stream.  There is no fallback:
+if the library is missing or a call fails, GQAError is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libgqa_attn.so"
+
+GQA_BF16 = 0
+GQA_F32 = 1
+
+_lib = None
+
+
+class GQAError(RuntimeError):
+    """Raised when the library is missing or returns a nonzero gqa_status."""
+
+    def __init__(self, msg: str, status: int | None = None):
+        super().__init__(msg)
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, _LIB_NAME)
+
+
+def load_library():
+    """Load libgqa_attn.so (once).  Raises GQAError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise GQAError(f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; "
+                       f"g.build()'` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    vp, i, f, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int64, ctypes.c_size_t
+    lib.gqa_attn_status_string.restype = ctypes.c_char_p
+    lib.gqa_attn_status_string.argtypes = [i]
+    lib.gqa_attn_version.restype = i
+    lib.gqa_attn_version.argtypes = []
+    lib.gqa_attn_prefill.restype = i
+    lib.gqa_attn_prefill.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp]
+    lib.gqa_attn_decode.restype = i
+    lib.gqa_attn_decode.argtypes = [vp, vp, vp, vp, i, i, i, i, vp, f, i, i, vp]
+    lib.gqa_attn_decode_plan.restype = i
+    lib.gqa_attn_decode_plan.argtypes = [i, i, i, i, vp, i, vp, vp, vp, vp, vp]
+    lib.gqa_attn_decode_split.restype = i
+    lib.gqa_attn_decode_split.argtypes = [vp, vp, vp, vp, sz, i, i, i, i, vp, f, i, i, vp]
+    lib.gqa_attn_decode_combine.restype = i
+    lib.gqa_attn_decode_combine.argtypes = [vp, sz, vp, vp, i, i, i, i, vp, i, i, vp]
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        msg = load_library().gqa_attn_status_string(rc).decode()
+        raise GQAError(f"{what} failed: {msg} (status {rc})", rc)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GQA_BF16
+    if t.dtype == torch.float32:
+        return GQA_F32
+    raise GQAError(f"unsupported dtype {t.dtype}", 3)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require(t, name: str, ndim: int):
+    if t.dim() != ndim:
+        raise GQAError(f"{name} must have {ndim} dimensions, got {tuple(t.shape)}", 2)
+    if not t.is_cuda:
+        raise GQAError(f"{name} must be a GPU tensor", 1)
+    if not t.is_contiguous():
+        raise GQAError(f"{name} must be contiguous", 2)
+
+
+def _kv_len_array(kv_len, B: int) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(kv_len, torch.Tensor):
+            kv_len = kv_len.detach().cpu().numpy()
+    except ImportError:
+        pass
+    a = np.ascontiguousarray(np.asarray(kv_len), dtype=np.int32)
+    if a.shape != (B,):
+        raise GQAError(f"kv_len must have shape [{B}]", 2)
+    return a
+
+
+def prefill(q, k, v, *, causal: bool, q_offset: int = 0, scale: float | None = None,
+            out=None, lse=None, return_lse: bool = True):
+    """Fused GQA prefill.  q [B,T_q,H_q,d], k/v [B,S_kv,H_kv,d] (bf16 or fp32).
+
+    Returns (o, lse): o like q, lse fp32 [B,T_q,H_q] (None if return_lse is
+    False and no lse buffer was given)."""
+    import torch
+    _require(q, "q", 4)
+    _require(k, "k", 4)
+    _require(v, "v", 4)
+    B, T_q, H_q, d = q.shape
+    S_kv, H_kv = k.shape[1], k.shape[2]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        raise GQAError("k and v must be [B, S_kv, H_kv, d] matching q", 2)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise GQAError("q, k, v must share one dtype", 3)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require(out, "out", 4)
+    if lse is None and return_lse:
+        lse = torch.empty((B, T_q, H_q), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _require(lse, "lse", 3)
+    rc = load_library().gqa_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, T_q,
+                                         S_kv, H_q, H_kv, d, float(scale), int(bool(causal)),
+                                         int(q_offset), _dtype_code(q), _stream(q.device))
+    _check(rc, "gqa_attn_prefill")
+    return out, lse
+
+
+def decode_plan(B: int, H_q: int, H_kv: int, d: int, kv_len, num_splits: int = 0) -> dict:
+    """Host-only split plan (no GPU needed)."""
+    a = _kv_len_array(kv_len, B)
+    splits = np.zeros(B, np.int32)
+    split_len = ctypes.c_int(0)
+    total = ctypes.c_int64(0)
+    mx = ctypes.c_int(0)
+    ws = ctypes.c_size_t(0)
+    rc = load_library().gqa_attn_decode_plan(B, H_q, H_kv, d, a.ctypes.data, int(num_splits),
+                                             splits.ctypes.data, ctypes.addressof(split_len),
+                                             ctypes.addressof(total), ctypes.addressof(mx),
+                                             ctypes.addressof(ws))
+    _check(rc, "gqa_attn_decode_plan")
+    return {"splits": splits, "split_len": split_len.value, "total_splits": total.value,
+            "max_splits": mx.value, "workspace_bytes": ws.value}
+
+
+def decode_workspace_bytes(B, H_q, H_kv, d, kv_len, num_splits: int = 0) -> int:
+    return decode_plan(B, H_q, H_kv, d, kv_len, num_splits)["workspace_bytes"]
+
+
+def _decode_shapes(q, k, v, kv_len):
+    _require(q, "q", 3)
+    _require(k, "k", 3)
+    _require(v, "v", 3)
+    B, H_q, d = q.shape
+    if k.shape != v.shape or k.shape[2] != d:
+        raise GQAError("k and v must be [sum(kv_len), H_kv, d] matching q", 2)
+    a = _kv_len_array(kv_len, B)
+    if int(a.astype(np.int64).sum()) != k.shape[0]:
+        raise GQAError("k/v rows must equal sum(kv_len)", 2)
+    return B, H_q, k.shape[1], d, a
+
+
+def decode(q, k, v, kv_len, *, scale: float | None = None, num_splits: int = 0, out=None):
+    """Split-KV GQA decode.  q [B,H_q,d] bf16, k/v packed [sum(kv_len),H_kv,d]."""
+    import torch
+    B, H_q, H_kv, d, a = _decode_shapes(q, k, v, kv_len)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    rc = load_library().gqa_attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H_q, H_kv, d,
+                                        a.ctypes.data, float(scale), int(num_splits),
+                                        _dtype_code(q), _stream(q.device))
+    _check(rc, "gqa_attn_decode")
+    return out
+
+
+def decode_split(q, k, v, kv_len, workspace, *, scale: float | None = None, num_splits: int = 0):
+    """Decode step 1: partials (m, l, O) into ``workspace`` (a uint8/float GPU tensor)."""
+    B, H_q, H_kv, d, a = _decode_shapes(q, k, v, kv_len)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = load_library().gqa_attn_decode_split(_ptr(q), _ptr(k), _ptr(v), _ptr(workspace), nbytes,
+                                              B, H_q, H_kv, d, a.ctypes.data, float(scale),
+                                              int(num_splits), _dtype_code(q), _stream(q.device))
+    _check(rc, "gqa_attn_decode_split")
+
+
+def decode_combine(workspace, kv_len, *, H_q: int, H_kv: int, d: int, out, lse=None,
+                   num_splits: int = 0):
+    """Decode step 2: merge the partials, normalise, write ``out`` [B,H_q,d]
+    (and ``lse`` [B,H_q] fp32 if given)."""
+    _require(out, "out", 3)
+    B = out.shape[0]
+    a = _kv_len_array(kv_len, B)
+    nbytes = workspace.numel() * workspace.element_size()
+    if lse is not None:
+        _require(lse, "lse", 2)
+    rc = load_library().gqa_attn_decode_combine(_ptr(workspace), nbytes, _ptr(out), _ptr(lse), B,
+                                                H_q, H_kv, d, a.ctypes.data, int(num_splits),
+                                                _dtype_code(out), _stream(out.device))
+    _check(rc, "gqa_attn_decode_combine")

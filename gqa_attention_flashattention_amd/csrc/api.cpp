@@ -1,0 +1,320 @@
+// api.cpp -- the C ABI of libgqa_attn.so (declared in include/gqa_attn.h):
+// argument validation, the decode split plan, the decode workspace cache and
+// kernel launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "gqa_attn.h"
+#include "launch.h"
+
+namespace {
+
+using gqa::DecodePlanChunk;
+using gqa::DecodeWorkspace;
+
+constexpr int kTargetSplitWorkgroups = 1024;   // about four per compute unit on MI355X
+constexpr int kMinSplitLen = 128;
+constexpr int kMaxSplitLen = 8192;
+constexpr int kSplitAlign = 64;
+
+bool finite_positive(float x) { return isfinite(x) && x > 0.f; }
+
+int check_heads(int H_q, int H_kv, int d) {
+    if (H_q < 1 || H_kv < 1 || (H_q % H_kv) != 0) return GQA_ERR_SHAPE;
+    if (d != 64 && d != 128) return GQA_ERR_UNSUPPORTED;
+    return GQA_OK;
+}
+
+// Per-sequence split lengths L_b and counts n_b (see gqa_attn_decode_plan).
+struct Plan {
+    int64_t total = 0;
+    int max_splits = 0;
+    int max_len = 0;
+};
+
+int env_split_len() {
+    static int cached = -1;
+    if (cached < 0) {
+        const char* s = getenv("GQA_ATTN_SPLIT_LEN");
+        int v = s ? atoi(s) : 0;
+        cached = v > 0 ? v : 0;
+    }
+    return cached;
+}
+
+int make_plan(int B, int H_q, int H_kv, const int32_t* kv_len, int num_splits, int32_t* splits,
+              int32_t* lens, Plan* out) {
+    if (kv_len == nullptr) return GQA_ERR_NULL;
+    if (B < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv) return GQA_ERR_SHAPE;
+    int64_t total_keys = 0;
+    for (int b = 0; b < B; ++b) {
+        if (kv_len[b] < 1) return GQA_ERR_SHAPE;
+        total_keys += kv_len[b];
+    }
+    const int G = H_q / H_kv;
+    const int n_hg = (G + 15) / 16;
+    int64_t auto_len = 0;
+    if (num_splits <= 0) {
+        int forced = env_split_len();
+        if (forced > 0) {
+            auto_len = forced;
+        } else {
+            int64_t per = (total_keys * H_kv * n_hg + kTargetSplitWorkgroups - 1) /
+                          kTargetSplitWorkgroups;
+            per = (per + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+            if (per < kMinSplitLen) per = kMinSplitLen;
+            if (per > kMaxSplitLen) per = kMaxSplitLen;
+            auto_len = per;
+        }
+    }
+    Plan p;
+    for (int b = 0; b < B; ++b) {
+        const int64_t len = kv_len[b];
+        int64_t L;
+        if (num_splits > 0) {
+            const int64_t ns = num_splits < len ? num_splits : len;
+            L = (len + ns - 1) / ns;
+        } else {
+            L = auto_len;
+        }
+        const int64_t n = (len + L - 1) / L;
+        if (splits) splits[b] = (int32_t)n;
+        if (lens) lens[b] = (int32_t)L;
+        p.total += n;
+        if (n > p.max_splits) p.max_splits = (int)n;
+        if (L > p.max_len) p.max_len = (int)(L < len ? L : len);
+    }
+    if (p.total > (int64_t)1 << 30) return GQA_ERR_SHAPE;
+    *out = p;
+    return GQA_OK;
+}
+
+size_t workspace_bytes_for(int64_t total, int H_q, int d) {
+    return (size_t)total * (size_t)H_q * (size_t)(d + 2) * sizeof(float);
+}
+
+DecodeWorkspace carve(void* base, int64_t total, int H_q) {
+    float* f = (float*)base;
+    DecodeWorkspace ws;
+    ws.m = f;
+    ws.l = f + total * H_q;
+    ws.o = f + 2 * total * H_q;
+    return ws;
+}
+
+int check_decode_args(const void* q, const void* k, const void* v, int B, int H_q, int H_kv,
+                      int d, const int32_t* kv_len, float scale, int dtype) {
+    if (!q || !k || !v || !kv_len) return GQA_ERR_NULL;
+    if (B < 1) return GQA_ERR_SHAPE;
+    int rc = check_heads(H_q, H_kv, d);
+    if (rc) return rc;
+    if (dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+    if (!finite_positive(scale)) return GQA_ERR_RANGE;
+    return GQA_OK;
+}
+
+// Split the batch into launches of at most kDecodeSeqPerLaunch sequences and
+// call fn(chunk) for each.
+template <typename Fn>
+int for_each_chunk(int B, const int32_t* kv_len, const int32_t* splits, const int32_t* lens,
+                   Fn fn) {
+    int64_t key_off = 0, split_base = 0;
+    for (int b0 = 0; b0 < B; b0 += gqa::kDecodeSeqPerLaunch) {
+        DecodePlanChunk c;
+        memset(&c, 0, sizeof(c));
+        c.nseq = B - b0 < gqa::kDecodeSeqPerLaunch ? B - b0 : gqa::kDecodeSeqPerLaunch;
+        c.seq0 = b0;
+        if (split_base > 0x7fffffff) return GQA_ERR_SHAPE;
+        c.split_base = (int)split_base;
+        int units = 0;
+        for (int i = 0; i < c.nseq; ++i) {
+            c.key_off[i] = key_off;
+            c.len[i] = kv_len[b0 + i];
+            c.split_len[i] = lens[b0 + i];
+            c.unit_base[i] = units;
+            units += splits[b0 + i];
+            key_off += kv_len[b0 + i];
+        }
+        c.unit_base[c.nseq] = units;
+        c.units = units;
+        split_base += units;
+        hipError_t e = fn(c);
+        if (e != hipSuccess) return GQA_ERR_HIP;
+    }
+    return GQA_OK;
+}
+
+struct HostPlan {
+    int32_t* splits = nullptr;
+    int32_t* lens = nullptr;
+    Plan p;
+    ~HostPlan() {
+        free(splits);
+        free(lens);
+    }
+    int build(int B, int H_q, int H_kv, const int32_t* kv_len, int num_splits) {
+        splits = (int32_t*)malloc(sizeof(int32_t) * (size_t)B);
+        lens = (int32_t*)malloc(sizeof(int32_t) * (size_t)B);
+        if (!splits || !lens) return GQA_ERR_SHAPE;
+        return make_plan(B, H_q, H_kv, kv_len, num_splits, splits, lens, &p);
+    }
+};
+
+// Per-device decode workspace owned by the library (gqa_attn_decode only).
+constexpr int kMaxDevices = 64;
+struct CachedWorkspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+CachedWorkspace g_ws[kMaxDevices];
+
+int get_workspace(size_t bytes, void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GQA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    CachedWorkspace& w = g_ws[dev];
+    if (w.bytes < bytes) {
+        if (w.ptr) {
+            // the old buffer may still be read by queued kernels
+            if (hipDeviceSynchronize() != hipSuccess) return GQA_ERR_HIP;
+            (void)hipFree(w.ptr);
+            w.ptr = nullptr;
+            w.bytes = 0;
+        }
+        size_t want = bytes < (1u << 20) ? (1u << 20) : bytes;
+        if (hipMalloc(&w.ptr, want) != hipSuccess) {
+            w.ptr = nullptr;
+            return GQA_ERR_HIP;
+        }
+        w.bytes = want;
+    }
+    *out = w.ptr;
+    return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gqa_attn_status_string(int status) {
+    switch (status) {
+        case GQA_OK: return "ok";
+        case GQA_ERR_NULL: return "a required pointer is NULL";
+        case GQA_ERR_SHAPE: return "invalid sizes (B, T_q, S_kv, heads, kv_len)";
+        case GQA_ERR_UNSUPPORTED: return "unsupported head dim or dtype";
+        case GQA_ERR_RANGE: return "argument out of range (q_offset, scale, workspace size)";
+        case GQA_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int gqa_attn_version(void) { return 100; }
+
+int gqa_attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int T_q, int S_kv, int H_q, int H_kv, int d, float scale, int causal,
+                     int q_offset, int dtype, void* stream) {
+    if (!q || !k || !v || !o) return GQA_ERR_NULL;
+    if (B < 1 || T_q < 1 || S_kv < 1) return GQA_ERR_SHAPE;
+    int rc = check_heads(H_q, H_kv, d);
+    if (rc) return rc;
+    if (dtype != GQA_BF16 && dtype != GQA_F32) return GQA_ERR_UNSUPPORTED;
+    if (!finite_positive(scale)) return GQA_ERR_RANGE;
+    if (causal && (q_offset < 0 || (int64_t)q_offset + T_q > S_kv)) return GQA_ERR_RANGE;
+    if ((int64_t)T_q * (H_q / H_kv) > 0x7fffffff - 256) return GQA_ERR_SHAPE;
+    gqa::PrefillArgs a{q, k, v, o, lse, B, T_q, S_kv, H_q, H_kv, d, scale, causal ? 1 : 0,
+                       causal ? q_offset : 0};
+    (void)hipGetLastError();
+    hipError_t e = dtype == GQA_BF16 ? gqa::launch_prefill_bf16(a, (hipStream_t)stream)
+                                     : gqa::launch_prefill_f32(a, (hipStream_t)stream);
+    return e == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+int gqa_attn_decode_plan(int B, int H_q, int H_kv, int d, const int32_t* kv_len, int num_splits,
+                         int32_t* splits, int* split_len, int64_t* total_splits, int* max_splits,
+                         size_t* workspace_bytes) {
+    if (kv_len == nullptr) return GQA_ERR_NULL;
+    if (B < 1) return GQA_ERR_SHAPE;
+    int rc = check_heads(H_q, H_kv, d);
+    if (rc) return rc;
+    HostPlan hp;
+    rc = hp.build(B, H_q, H_kv, kv_len, num_splits);
+    if (rc) return rc;
+    if (splits) memcpy(splits, hp.splits, sizeof(int32_t) * (size_t)B);
+    if (split_len) *split_len = hp.p.max_len;
+    if (total_splits) *total_splits = hp.p.total;
+    if (max_splits) *max_splits = hp.p.max_splits;
+    if (workspace_bytes) *workspace_bytes = workspace_bytes_for(hp.p.total, H_q, d);
+    return GQA_OK;
+}
+
+int gqa_attn_decode_split(const void* q, const void* k, const void* v, void* workspace,
+                          size_t workspace_bytes, int B, int H_q, int H_kv, int d,
+                          const int32_t* kv_len, float scale, int num_splits, int dtype,
+                          void* stream) {
+    int rc = check_decode_args(q, k, v, B, H_q, H_kv, d, kv_len, scale, dtype);
+    if (rc) return rc;
+    if (!workspace) return GQA_ERR_NULL;
+    HostPlan hp;
+    rc = hp.build(B, H_q, H_kv, kv_len, num_splits);
+    if (rc) return rc;
+    if (workspace_bytes < workspace_bytes_for(hp.p.total, H_q, d)) return GQA_ERR_RANGE;
+    DecodeWorkspace ws = carve(workspace, hp.p.total, H_q);
+    (void)hipGetLastError();
+    return for_each_chunk(B, kv_len, hp.splits, hp.lens, [&](const DecodePlanChunk& c) {
+        return gqa::launch_decode_split_bf16(q, k, v, ws, c, H_q, H_kv, d, scale,
+                                             (hipStream_t)stream);
+    });
+}
+
+int gqa_attn_decode_combine(const void* workspace, size_t workspace_bytes, void* o, float* lse,
+                            int B, int H_q, int H_kv, int d, const int32_t* kv_len,
+                            int num_splits, int dtype, void* stream) {
+    if (!workspace || !o || !kv_len) return GQA_ERR_NULL;
+    if (B < 1) return GQA_ERR_SHAPE;
+    int rc = check_heads(H_q, H_kv, d);
+    if (rc) return rc;
+    if (dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+    HostPlan hp;
+    rc = hp.build(B, H_q, H_kv, kv_len, num_splits);
+    if (rc) return rc;
+    if (workspace_bytes < workspace_bytes_for(hp.p.total, H_q, d)) return GQA_ERR_RANGE;
+    DecodeWorkspace ws = carve((void*)workspace, hp.p.total, H_q);
+    (void)hipGetLastError();
+    return for_each_chunk(B, kv_len, hp.splits, hp.lens, [&](const DecodePlanChunk& c) {
+        return gqa::launch_decode_combine_bf16(ws, c, o, lse, H_q, d, (hipStream_t)stream);
+    });
+}
+
+int gqa_attn_decode(const void* q, const void* k, const void* v, void* o, int B, int H_q,
+                    int H_kv, int d, const int32_t* kv_len, float scale, int num_splits,
+                    int dtype, void* stream) {
+    int rc = check_decode_args(q, k, v, B, H_q, H_kv, d, kv_len, scale, dtype);
+    if (rc) return rc;
+    if (!o) return GQA_ERR_NULL;
+    HostPlan hp;
+    rc = hp.build(B, H_q, H_kv, kv_len, num_splits);
+    if (rc) return rc;
+    const size_t need = workspace_bytes_for(hp.p.total, H_q, d);
+    void* base = nullptr;
+    rc = get_workspace(need, &base);
+    if (rc) return rc;
+    DecodeWorkspace ws = carve(base, hp.p.total, H_q);
+    (void)hipGetLastError();
+    rc = for_each_chunk(B, kv_len, hp.splits, hp.lens, [&](const DecodePlanChunk& c) {
+        return gqa::launch_decode_split_bf16(q, k, v, ws, c, H_q, H_kv, d, scale,
+                                             (hipStream_t)stream);
+    });
+    if (rc) return rc;
+    return for_each_chunk(B, kv_len, hp.splits, hp.lens, [&](const DecodePlanChunk& c) {
+        return gqa::launch_decode_combine_bf16(ws, c, o, nullptr, H_q, d, (hipStream_t)stream);
+    });
+}
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// launch.h -- host-side launchers of the gfx950 kernels (internal to the
+// library; the public interface is include/gqa_attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+struct PrefillArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int B, T_q, S_kv, H_q, H_kv, d;
+    float scale;
+    int causal;
+    int q_offset;
+};
+
+// Sequences described per decode launch (kernel-argument plan).
+constexpr int kDecodeSeqPerLaunch = 64;
+
+struct DecodePlanChunk {
+    int nseq;                                // sequences in this launch
+    int split_base;                          // global split index of this launch's first split
+    int units;                               // sum of splits over this launch's sequences
+    int64_t key_off[kDecodeSeqPerLaunch];    // first key row of each sequence
+    int32_t len[kDecodeSeqPerLaunch];        // kv_len
+    int32_t split_len[kDecodeSeqPerLaunch];  // L_b
+    int32_t unit_base[kDecodeSeqPerLaunch + 1];  // prefix of splits within the launch
+    int32_t seq0;                            // batch index of the first sequence
+};
+
+struct DecodeWorkspace {
+    float* m;   // [total_splits][H_q]
+    float* l;   // [total_splits][H_q]
+    float* o;   // [total_splits][H_q][d]
+};
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
+
+hipError_t launch_decode_split_bf16(const void* q, const void* k, const void* v,
+                                    const DecodeWorkspace& ws, const DecodePlanChunk& plan,
+                                    int H_q, int H_kv, int d, float scale, hipStream_t stream);
+hipError_t launch_decode_combine_bf16(const DecodeWorkspace& ws, const DecodePlanChunk& plan,
+                                      void* o, float* lse, int H_q, int d, hipStream_t stream);
+
+}  // namespace gqa

@@ -1,0 +1,134 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/gqa_attn.h declares, validates arguments (returning a status before
+anything reaches the GPU) and computes the decode split plan."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+import gqa_attention_flashattention_amd as gq
+from gqa_attention_flashattention_amd import binding
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "gqa_attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ["gqa_attn_prefill", "gqa_attn_decode", "gqa_attn_decode_split",
+              "gqa_attn_decode_combine", "gqa_attn_decode_plan", "gqa_attn_status_string",
+              "gqa_attn_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = gq.load_library()
+    for name in _declared_functions():
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_status_strings():
+    lib = gq.load_library()
+    for code in range(6):
+        assert lib.gqa_attn_status_string(code)
+    assert lib.gqa_attn_status_string(99) == b"unknown status"
+
+
+P = ctypes.c_void_p(16)   # never dereferenced: validation fails before any device access
+
+
+def _prefill(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, T=4, S=8, Hq=8, Hkv=2, d=128, scale=0.1,
+             causal=1, qoff=0, dtype=0)
+    a.update(kw)
+    return gq.load_library().gqa_attn_prefill(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"],
+                                              a["T"], a["S"], a["Hq"], a["Hkv"], a["d"],
+                                              a["scale"], a["causal"], a["qoff"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1),
+    (dict(B=0), 2), (dict(T=0), 2), (dict(S=0), 2), (dict(Hq=7), 2), (dict(Hkv=0), 2),
+    (dict(d=96), 3), (dict(d=256), 3), (dict(dtype=2), 3),
+    (dict(qoff=-1), 4), (dict(qoff=5), 4), (dict(scale=0.0), 4), (dict(scale=float("nan")), 4),
+    (dict(scale=-1.0), 4),
+])
+def test_prefill_rejects(kw, code):
+    assert _prefill(**kw) == code
+
+
+def _decode(kv_len, **kw):
+    a = dict(q=P, k=P, v=P, o=P, B=len(kv_len), Hq=8, Hkv=2, d=128, scale=0.1, ns=0, dtype=0)
+    a.update(kw)
+    arr = np.asarray(kv_len, np.int32)
+    return gq.load_library().gqa_attn_decode(a["q"], a["k"], a["v"], a["o"], a["B"], a["Hq"],
+                                             a["Hkv"], a["d"], arr.ctypes.data if kv_len else None,
+                                             a["scale"], a["ns"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kv_len,kw,code", [
+    ([4], dict(q=None), 1), ([4], dict(o=None), 1), ([], dict(B=1), 1),
+    ([4, 0], {}, 2), ([4, -3], {}, 2), ([4], dict(B=0), 2), ([4], dict(Hq=9), 2),
+    ([4], dict(d=32), 3), ([4], dict(dtype=1), 3), ([4], dict(scale=float("inf")), 4),
+])
+def test_decode_rejects(kv_len, kw, code):
+    assert _decode(kv_len, **kw) == code
+
+
+def test_split_and_combine_reject_small_workspace():
+    lib = gq.load_library()
+    kv = np.array([1000], np.int32)
+    need = gq.decode_workspace_bytes(1, 64, 8, 128, kv)
+    assert lib.gqa_attn_decode_split(P, P, P, P, need - 4, 1, 64, 8, 128, kv.ctypes.data, 0.1, 0,
+                                     0, None) == 4
+    assert lib.gqa_attn_decode_combine(P, need - 1, P, None, 1, 64, 8, 128, kv.ctypes.data, 0, 0,
+                                       None) == 4
+    assert lib.gqa_attn_decode_split(P, P, P, None, need, 1, 64, 8, 128, kv.ctypes.data, 0.1, 0,
+                                     0, None) == 1
+
+
+def test_binding_raises():
+    with pytest.raises(binding.GQAError):
+        gq.decode_plan(2, 64, 8, 128, [5, 0])
+    with pytest.raises(binding.GQAError):
+        gq.decode_plan(1, 64, 8, 100, [5])
+
+
+@pytest.mark.parametrize("kv_len,num_splits", [
+    ([8192], 0), ([1, 2, 3], 0), ([1024, 32768, 5000], 0), ([131072], 0),
+    ([37, 1, 64], 7), ([10], 4), ([10], 6), ([10], 100), ([5, 9], 1),
+])
+def test_decode_plan_covers_every_key_once(kv_len, num_splits):
+    """Every key of every sequence falls in exactly one split; splits are
+    contiguous, non-empty, and follow the documented rule."""
+    p = gq.decode_plan(len(kv_len), 64, 8, 128, kv_len, num_splits)
+    assert p["total_splits"] == int(p["splits"].sum())
+    assert p["workspace_bytes"] == p["total_splits"] * 64 * 130 * 4
+    for n, ns_b in zip(kv_len, p["splits"]):
+        if num_splits > 0:
+            L = -(-n // min(num_splits, n))
+            assert ns_b <= num_splits
+        else:
+            L = p["split_len"] if len(set(kv_len)) == 1 else None
+        if L is not None:
+            assert ns_b == -(-n // L)
+            covered = np.zeros(n, np.int32)
+            for s in range(ns_b):
+                lo, hi = s * L, min((s + 1) * L, n)
+                assert hi > lo
+                covered[lo:hi] += 1
+            assert np.all(covered == 1)
+
+
+def test_auto_plan_targets_occupancy():
+    # decode_8k: 8 KV heads x splits should give several work-groups per CU
+    p = gq.decode_plan(1, 64, 8, 128, [8192])
+    assert p["split_len"] % 64 == 0 and 128 <= p["split_len"] <= 8192
+    assert p["total_splits"] * 8 >= 256

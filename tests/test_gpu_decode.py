@@ -1,0 +1,119 @@
+"""GPU parity of the split-KV decode path (C ABI gqa_attn_decode and the
+split/combine pair) against the fp64 oracle, element by element."""
+import numpy as np
+import pytest
+
+import oracle
+from gqa_attention_flashattention_amd import inputs as gin
+
+from gpu_util import assert_close, to_f64, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(inp):
+    return tuple(to_gpu(x, "bf16") for x in (inp.q_store, inp.k_store, inp.v_store))
+
+
+def _decode(inp, num_splits=0):
+    import gqa_attention_flashattention_amd as gq
+    import torch
+    q, k, v = _dev(inp)
+    o = gq.decode(q, k, v, inp.kv_len, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return to_f64(o)
+
+
+def _decode_with_lse(inp, num_splits=0):
+    import gqa_attention_flashattention_amd as gq
+    import torch
+    q, k, v = _dev(inp)
+    B, Hq, d = q.shape
+    Hkv = k.shape[1]
+    nbytes = gq.decode_workspace_bytes(B, Hq, Hkv, d, inp.kv_len, num_splits)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    gq.decode_split(q, k, v, inp.kv_len, ws, num_splits=num_splits)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    gq.decode_combine(ws, inp.kv_len, H_q=Hq, H_kv=Hkv, d=d, out=o, lse=lse, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return to_f64(o), to_f64(lse)
+
+
+@pytest.mark.parametrize("kv_len,Hq,Hkv,d", [
+    ([1, 2, 31, 32, 33, 63, 64, 65, 1000], 64, 8, 128),
+    ([1, 2, 31, 32, 33, 130, 4097], 64, 8, 64),
+    ([77, 300, 5], 12, 4, 128),          # G = 3
+    ([129, 17], 32, 1, 128),             # G = 32: two 16-head groups
+    ([250], 20, 1, 64),                  # G = 20: partial second head group
+    ([513, 1], 8, 8, 128),               # G = 1
+])
+def test_decode_parity(kv_len, Hq, Hkv, d):
+    inp = gin.random_case("decode", "bf16", B=len(kv_len), H_q=Hq, H_kv=Hkv, d=d, kv_len=kv_len,
+                          seed=sum(kv_len))
+    og = _decode(inp)
+    oref, _ = oracle.decode(inp.q, inp.k, inp.v, inp.kv_len)
+    assert_close(og, oref, name=f"decode {kv_len} {Hq}/{Hkv} d={d}")
+
+
+@pytest.mark.parametrize("num_splits", [1, 2, 3, 7, 64, 1000])
+def test_split_count_invariance(num_splits):
+    kv_len = [1000, 1, 257]
+    inp = gin.random_case("decode", "bf16", B=3, H_q=64, H_kv=8, d=128, kv_len=kv_len, seed=2)
+    og, lg = _decode_with_lse(inp, num_splits)
+    oref, lref = oracle.decode(inp.q, inp.k, inp.v, inp.kv_len)
+    assert_close(og, oref, lg, lref, name=f"decode splits={num_splits}")
+    o1, l1 = _decode_with_lse(inp, 1)
+    assert np.abs(og - o1).max() <= 1e-2 and np.abs(lg - l1).max() <= 1e-3
+
+
+def test_many_sequences_two_launches():
+    """More sequences than one launch describes (64): chunked launches."""
+    rng = np.random.default_rng(3)
+    kv_len = rng.integers(1, 300, size=70).tolist()
+    inp = gin.random_case("decode", "bf16", B=70, H_q=16, H_kv=2, d=128, kv_len=kv_len, seed=6)
+    og, lg = _decode_with_lse(inp)
+    oref, lref = oracle.decode(inp.q, inp.k, inp.v, inp.kv_len)
+    assert_close(og, oref, lg, lref, name="decode B=70")
+
+
+def test_uniform_scores_mean_of_v():
+    kv_len = [5, 700, 64]
+    inp = gin.random_case("decode", "bf16", B=3, H_q=64, H_kv=8, d=128, kv_len=kv_len, seed=8)
+    inp.q_store[...] = 0
+    inp.q[...] = 0
+    og, lg = _decode_with_lse(inp)
+    oref, lref = oracle.decode(inp.q, inp.k, inp.v, inp.kv_len)
+    assert np.abs(lref - np.log(np.array(kv_len))[:, None]).max() < 1e-12
+    assert_close(og, oref, lg, lref, name="decode uniform")
+
+
+def test_peaky_decode():
+    inp = gin.random_case("decode", "bf16", B=2, H_q=64, H_kv=8, d=128, kv_len=[3000, 70], seed=9,
+                          q_scale=8.0)
+    og, lg = _decode_with_lse(inp)
+    oref, lref = oracle.decode(inp.q, inp.k, inp.v, inp.kv_len)
+    assert_close(og, oref, lg, lref, name="decode peaky")
+
+
+def test_decode_deterministic():
+    import gqa_attention_flashattention_amd as gq
+    import torch
+    inp = gin.random_case("decode", "bf16", B=2, H_q=64, H_kv=8, d=128, kv_len=[5000, 333], seed=10)
+    q, k, v = _dev(inp)
+    o1 = gq.decode(q, k, v, inp.kv_len)
+    o2 = gq.decode(q, k, v, inp.kv_len)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("name", ["decode_8k", "decode_varlen_b16", "decode_128k"])
+def test_full_size_workloads(name):
+    """Full-size decode workloads in the benchmark's launch configuration,
+    every output element against the oracle."""
+    inp = gin.make(name)
+    og, lg = _decode_with_lse(inp)
+    oref, lref = oracle.decode(inp.q, inp.k, inp.v, inp.kv_len)
+    assert_close(og, oref, lg, lref, name=name)
+    og2 = _decode(inp)
+    assert np.array_equal(og2, og)
