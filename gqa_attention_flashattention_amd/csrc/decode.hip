@@ -19,13 +19,14 @@
 //    each wave streams its K rows straight from HBM into MFMA A operands
 //    (v_mfma_f32_16x16x32_bf16, S^T = K Q^T with the G heads as the 16 MFMA
 //    columns), so each lane owns one query head and the softmax state is
-//    lane-local.  V rows are loaded with 16-byte coalesced loads and
-//    transposed into a per-wave LDS tile (V^T), the A operand of
-//    O^T = V^T P^T.  The next tile's loads are issued before the current
+//    lane-local.  V rows are loaded with 16-byte coalesced loads into a
+//    per-wave row-major LDS tile and read back with ds_read_b64_tr_b16 as
+//    the V^T A operand of O^T = V^T P^T.  The next tile's loads are issued before the current
 //    tile's math.  At the end the four wave partials are merged through LDS
 //    and one partial per (split, query head) is written.
-//  * Combine kernel: one wave per (sequence, query head); partials are read
-//    in split order (fixed order, no atomics: bitwise reproducible).
+//  * Combine kernel: one wave per (sequence, query head, 32 dims of O); the
+//    partials of all splits are read in parallel and reduced in a fixed order
+//    (no atomics: bitwise reproducible).
 #include "common.h"
 #include "launch.h"
 
@@ -40,20 +41,29 @@ constexpr int kCols = 16;       // query heads per MFMA column block
 
 template <int D>
 struct DecodeSmem {
-    static constexpr int VS = kTile + 8;              // V^T row stride (elements)
-    static constexpr int VT_ELEMS = D * VS;            // per wave
+    static constexpr int VS = D + 16;                 // V row stride (elements): tr16 reads 2-way
+    static constexpr int VT_ELEMS = kTile * VS;       // per wave
 };
 
-// Key (within a 32-key tile) that A-operand row m of 16-key block blk loads,
-// chosen so that the 8 P values a lane holds are keys 8 * (lane / 16) + 0..7.
-__device__ __forceinline__ int tile_key(int m, int blk) { return (m >> 2) * 8 + blk * 4 + (m & 3); }
+// Key (within a 32-key tile) that A-operand row m of 16-key block blk loads.
+// With it, P slot j (= 4 blk + i) of lane group g4 = m / 4 holds key g4 + 4 j,
+// so each transposed V read of a 16-lane group touches 4 rows spaced by 4.
+__device__ __forceinline__ int tile_key(int m, int blk) { return (m >> 2) + 16 * blk + 4 * (m & 3); }
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(8))) short s16x8;
+
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(p));
+}
 
 template <int D>
 struct WaveTile {
     static constexpr int KSTEPS = D / 32;     // MFMA k-steps over the head dim
-    static constexpr int KPL = D / 16;        // V keys per lane (8 for D = 128, 4 for D = 64)
+    static constexpr int KPL = D / 16;        // V rows per lane (8 for D = 128, 4 for D = 64)
     u32x4 kf[2][KSTEPS];                      // K A operands, two 16-key blocks
-    u32x4 vr[KPL];                            // V rows: KPL keys x 8 dims
+    u32x4 vr[KPL];                            // V chunks: KPL rows x 8 dims
 };
 
 template <int D>
@@ -73,41 +83,27 @@ __device__ __forceinline__ void load_wave_tile(WaveTile<D>& w, const uint16_t* _
         }
     }
     constexpr int CPR = D / 8;                // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;             // rows per wave instruction
     const int dc = lane % CPR, kg = lane / CPR;
 #pragma unroll
     for (int e = 0; e < WaveTile<D>::KPL; ++e) {
-        const int kk = key0 + kg * WaveTile<D>::KPL + e;
+        const int kk = key0 + e * RPI + kg;
         u32x4 val = {0u, 0u, 0u, 0u};
         if (kk < key_end) val = *(const u32x4*)(vseq + (int64_t)kk * row_stride + dc * 8);
         w.vr[e] = val;
     }
 }
 
-// Transpose the lane's KPL keys x 8 dims into V^T[dim][key] in LDS.
+// V tile into the wave's LDS area, row-major (key rows, head dims contiguous).
 template <int D>
-__device__ __forceinline__ void store_vt(const WaveTile<D>& w, uint16_t* __restrict__ vt, int lane) {
+__device__ __forceinline__ void store_v(const WaveTile<D>& w, uint16_t* __restrict__ vt, int lane) {
     using SM = DecodeSmem<D>;
-    constexpr int KPL = WaveTile<D>::KPL;
     constexpr int CPR = D / 8;
+    constexpr int RPI = 64 / CPR;
     const int dc = lane % CPR, kg = lane / CPR;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {            // dim pair (2p, 2p + 1)
-        uint32_t lo[KPL / 2], hi[KPL / 2];
-#pragma unroll
-        for (int e = 0; e < KPL; e += 2) {
-            lo[e / 2] = __builtin_amdgcn_perm(w.vr[e + 1][p], w.vr[e][p], 0x05040100u);
-            hi[e / 2] = __builtin_amdgcn_perm(w.vr[e + 1][p], w.vr[e][p], 0x07060302u);
-        }
-        uint16_t* d0 = vt + (dc * 8 + 2 * p) * SM::VS + kg * KPL;
-        uint16_t* d1 = d0 + SM::VS;
-        if constexpr (KPL == 8) {
-            *(u32x4*)d0 = u32x4{lo[0], lo[1], lo[2], lo[3]};
-            *(u32x4*)d1 = u32x4{hi[0], hi[1], hi[2], hi[3]};
-        } else {
-            *(u32x2*)d0 = u32x2{lo[0], lo[1]};
-            *(u32x2*)d1 = u32x2{hi[0], hi[1]};
-        }
-    }
+    for (int e = 0; e < WaveTile<D>::KPL; ++e)
+        *(u32x4*)(vt + (e * RPI + kg) * SM::VS + dc * 8) = w.vr[e];
 }
 
 __device__ __forceinline__ void wave_lds_fence() {
@@ -167,6 +163,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const uint16_t* kseq = k + (plan.key_off[sq] * H_kv + kv) * (int64_t)D;
     const uint16_t* vseq = v + (plan.key_off[sq] * H_kv + kv) * (int64_t)D;
     uint16_t* vt = (uint16_t*)smem + wave * SM::VT_ELEMS;
+    // transposed-read source address: lane L of group g4 points at key row
+    // g4 + 4 (L / 4) (+ 16 for the second read), dims 4 (L % 4) of each 16-dim block
+    const uint16_t* vrd = vt + (g4 + 4 * ((lane & 15) >> 2)) * SM::VS + 4 * (lane & 3);
 
     f32x4 oacc[DBLK];
 #pragma unroll
@@ -179,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     if (tt < n_tiles) load_wave_tile<D>(wt, kseq, vseq, row_stride, kbeg + tt * kTile, kend, lane);
     for (; tt < n_tiles; tt += kWaves) {
         const int key0 = kbeg + tt * kTile;
-        // S^T for two 16-key blocks; element i of s[blk] is key key0 + 8 g4 + 4 blk + i
+        // S^T for two 16-key blocks; element i of s[blk] is key key0 + g4 + 16 blk + 4 i
         f32x4 s[2];
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
@@ -189,8 +188,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
                 s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     __builtin_bit_cast(bf16x8, wt.kf[blk][ks]), qf[ks], s[blk], 0, 0, 0);
         }
-        wave_lds_fence();                    // previous tile's V^T reads are done
-        store_vt<D>(wt, vt, lane);
+        wave_lds_fence();                    // previous tile's V reads are done
+        store_v<D>(wt, vt, lane);
         const int nt = tt + kWaves;
         if (nt < n_tiles) load_wave_tile<D>(wt, kseq, vseq, row_stride, kbeg + nt * kTile, kend, lane);
         if (key0 + kTile > kend) {
@@ -198,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
             for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (key0 + 8 * g4 + 4 * blk + i >= kend) s[blk][i] = -INFINITY;
+                    if (key0 + g4 + 16 * blk + 4 * i >= kend) s[blk][i] = -INFINITY;
         }
         float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                          fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
@@ -217,12 +216,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
         u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                     pack_bf16x2(p[6], p[7])};
         const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-        wave_lds_fence();                    // V^T of this tile is visible to the wave
+        wave_lds_fence();                    // V of this tile is visible to the wave
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) {
             oacc[db] *= corr;
-            bf16x8 a = *(const bf16x8*)(vt + (db * 16 + col) * SM::VS + g4 * 8);
-            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, oacc[db], 0, 0, 0);
+            const s16x4 lo = lds_read_tr16(vrd + db * 16);
+            const s16x4 hi = lds_read_tr16(vrd + 16 * SM::VS + db * 16);
+            const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a8), pb,
+                                                               oacc[db], 0, 0, 0);
         }
     }
 
@@ -231,36 +233,34 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     l_run += __shfl_xor(l_run, 32);
     __syncthreads();                         // every wave is done with its V^T tile
     float* mrg = (float*)smem;
-    float* mw_o = mrg + wave * kCols * (D + 2);     // [16][D] then m[16], l[16]
-    float* mw_m = mw_o + kCols * D;
-    float* mw_l = mw_m + kCols;
+    constexpr int WSTRIDE = kCols * (D + 2);        // per wave: O [16][D], then m[16], l[16]
+    float* mw_o = mrg + wave * WSTRIDE;
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mw_o[col * D + db * 16 + g4 * 4 + i] = oacc[db][i];
+    for (int db = 0; db < DBLK; ++db) *(f32x4*)(mw_o + col * D + db * 16 + g4 * 4) = oacc[db];
     if (g4 == 0) {
-        mw_m[col] = m_run;
-        mw_l[col] = l_run;
+        mw_o[kCols * D + col] = m_run;
+        mw_o[kCols * D + kCols + col] = l_run;
     }
     __syncthreads();
     const int64_t pidx = (int64_t)plan.split_base + unit;
-    for (int e = tid; e < kCols * D; e += kThreads) {
-        const int cc = e / D, x = e % D;
+    for (int e = tid; e < kCols * (D / 4); e += kThreads) {
+        const int cc = e / (D / 4), x = (e % (D / 4)) * 4;
         if (hg * kCols + cc >= G) continue;
         float mx = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, mrg[w * kCols * (D + 2) + kCols * D + cc]);
-        float acc = 0.f, lsum = 0.f;
+        for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, mrg[w * WSTRIDE + kCols * D + cc]);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        float lsum = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const float* base = mrg + w * kCols * (D + 2);
+            const float* base = mrg + w * WSTRIDE;
             const float mwv = base[kCols * D + cc];
             const float sc = (mwv == -INFINITY) ? 0.f : fast_exp2((mwv - mx) * c);
-            acc += sc * base[cc * D + x];
+            acc += sc * *(const f32x4*)(base + cc * D + x);
             lsum += sc * base[kCols * D + kCols + cc];
         }
         const int64_t hrow = pidx * H_q + (int64_t)kv * G + hg * kCols + cc;
-        ws_o[hrow * D + x] = acc;
+        *(f32x4*)(ws_o + hrow * D + x) = acc;
         if (x == 0) {
             ws_m[hrow] = mx * c;             // base-2 units
             ws_l[hrow] = lsum;
@@ -268,50 +268,71 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     }
 }
 
+// One wave per (sequence, query head, 32-dim chunk of O).  Lane (sg, dq):
+// split group sg = lane / 8 takes splits sg, sg + 8, sg + 16, ...; dim quad
+// dq = lane % 8 owns dims 4 dq .. 4 dq + 3 of the chunk.  A lane issues all
+// loads of a batch of its splits before using any, the eight split groups
+// are then reduced with a fixed butterfly, so the result does not depend on
+// timing (bitwise reproducible for a given split plan).
+constexpr int kCombineBatch = 4;
+
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
     const float* __restrict__ ws_m, const float* __restrict__ ws_l,
     const float* __restrict__ ws_o, uint16_t* __restrict__ o, float* __restrict__ lse,
     const DecodePlanChunk plan, int H_q) {
-    constexpr int VPL = D / 64;              // values per lane
+    constexpr int CHUNKS = D / 32;
     const int lane = threadIdx.x & 63;
-    const int item = blockIdx.x * 4 + (threadIdx.x >> 6);     // (sequence, head) in this launch
-    if (item >= plan.nseq * H_q) return;
-    const int sq = item / H_q, h = item % H_q;
+    const int item = blockIdx.x * 4 + (threadIdx.x >> 6);   // (sequence, head, chunk)
+    if (item >= plan.nseq * H_q * CHUNKS) return;
+    const int chunk = item % CHUNKS;
+    const int sh = item / CHUNKS;
+    const int sq = sh / H_q, h = sh % H_q;
     const int n = plan.unit_base[sq + 1] - plan.unit_base[sq];
     const int64_t p0 = (int64_t)plan.split_base + plan.unit_base[sq];
 
+    // global max of the split maxima (base-2 units)
     float mx = -INFINITY;
     for (int s = lane; s < n; s += 64) mx = fmaxf(mx, ws_m[(p0 + s) * H_q + h]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
 
-    float acc[VPL];
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) acc[i] = 0.f;
+    const int sg = lane >> 3, dq = lane & 7;
+    const int dim = chunk * 32 + dq * 4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float lsum = 0.f;
-    for (int s = 0; s < n; ++s) {
-        const int64_t hrow = (p0 + s) * H_q + h;
-        const float w = fast_exp2(ws_m[hrow] - mx);
-        lsum += w * ws_l[hrow];
-        const float* src = ws_o + hrow * D + lane * VPL;
-        if constexpr (VPL == 2) {
-            float2 val = *(const float2*)src;
-            acc[0] += w * val.x;
-            acc[1] += w * val.y;
-        } else {
-            acc[0] += w * src[0];
+    for (int s0 = sg; s0 < n; s0 += 8 * kCombineBatch) {
+        float mv[kCombineBatch], lv[kCombineBatch];
+        f32x4 ov[kCombineBatch];
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u) {
+            const int s = s0 + 8 * u;
+            const int64_t hrow = (p0 + (s < n ? s : 0)) * H_q + h;
+            mv[u] = s < n ? ws_m[hrow] : -INFINITY;
+            lv[u] = ws_l[hrow];
+            ov[u] = *(const f32x4*)(ws_o + hrow * D + dim);
         }
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u) {
+            const float w = fast_exp2(mv[u] - mx);      // 0 for padding entries
+            lsum += w * lv[u];
+            acc += w * ov[u];
+        }
+    }
+#pragma unroll
+    for (int off = 8; off <= 32; off <<= 1) {
+        lsum += __shfl_xor(lsum, off);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], off);
     }
     const float inv = 1.f / lsum;
     const int b = plan.seq0 + sq;
-    uint16_t* dst = o + ((int64_t)b * H_q + h) * D + lane * VPL;
-    if constexpr (VPL == 2) {
-        *(uint32_t*)dst = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-    } else {
-        dst[0] = (uint16_t)(pack_bf16x2(acc[0] * inv, 0.f) & 0xffffu);
+    if (sg == 0) {
+        u32x2 w = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+        *(u32x2*)(o + ((int64_t)b * H_q + h) * D + dim) = w;
     }
-    if (lse != nullptr && lane == 0) lse[(int64_t)b * H_q + h] = (mx + fast_log2(lsum)) * kLn2;
+    if (lse != nullptr && chunk == 0 && lane == 0)
+        lse[(int64_t)b * H_q + h] = (mx + fast_log2(lsum)) * kLn2;
 }
 
 }  // namespace
@@ -337,7 +358,7 @@ hipError_t launch_decode_split_bf16(const void* q, const void* k, const void* v,
 
 hipError_t launch_decode_combine_bf16(const DecodeWorkspace& ws, const DecodePlanChunk& plan,
                                       void* o, float* lse, int H_q, int d, hipStream_t stream) {
-    const int64_t items = (int64_t)plan.nseq * H_q;
+    const int64_t items = (int64_t)plan.nseq * H_q * (d / 32);
     const int64_t grid = (items + 3) / 4;
     if (grid < 1 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     if (d == 128)

@@ -17,23 +17,28 @@
 //    key > q_offset + t  ->  -inf.
 //
 // MI355X mapping:
-//  * Work-group = 4 waves x 32 query rows (128 rows), key tiles of 64.
-//    blockIdx -> (kv head fastest, then batch, then row block); causal row
-//    blocks are issued longest-first.  With 8 KV heads and 8 XCDs the
-//    round-robin dispatch keeps each KV head's K/V in one XCD's L2.
+//  * Work-group = 8 waves x 32 query rows (256 rows), key tiles of 64; two
+//    waves per SIMD.  blockIdx -> (kv head fastest, then batch, then row
+//    block); causal row blocks are issued longest-first.  With 8 KV heads and
+//    8 XCDs the round-robin dispatch keeps each KV head's K/V in one XCD's L2.
 //  * The MFMA computes S^T = K Q^T: A = K tile rows from LDS, B = Q^T held in
 //    registers for the whole sweep.  In the 32x32 output layout each lane
 //    then owns one query column, so the running max / sum / rescale are
-//    lane-local (only lanes l and l^32 share a query), and the fp32 P values
-//    of a lane are exactly the B operand of O^T = V^T P^T after packing to
-//    bf16.  The K rows are loaded into the A operand in a permuted order
-//    (bits 2 and 3 of the row index swapped) so that the 8 keys a lane
-//    contributes to each P.V step are consecutive.
-//  * K tiles are stored row-major in LDS (row padded by 16 B, conflict-free
-//    b128 reads); V tiles are transposed on the way into LDS (V^T rows = head
-//    dims) so the P.V A operand is one b128 read per lane.  LDS is double
-//    buffered; the next tile's global loads are issued before the current
-//    tile's math.
+//    lane-local (only lanes l and l^32 share a query, joined with
+//    v_permlane32_swap), and the fp32 P values of a lane, packed to bf16, are
+//    exactly the B operand of O^T = V^T P^T.  K rows are loaded into the A
+//    operand in a permuted order (bits 2 and 3 of the row index swapped) so
+//    that the 8 keys a lane contributes to each P.V step are consecutive.
+//  * K and V tiles are both stored row-major in LDS with 16-byte writes.  The
+//    V^T operand is read with ds_read_b64_tr_b16 (each lane of a 16-lane group
+//    receives one head-dim column of four key rows), so V is never transposed
+//    in registers.  Row paddings make the b128 K reads and the transposed V
+//    reads bank-conflict free.  LDS is double buffered; the next tile's global
+//    loads are issued before the current tile's math.
+//  * Lazy rescaling: the running max used for the exponentials is only moved
+//    when some row's tile max exceeds it by more than 8 (log2 units), so most
+//    tiles skip the O rescale; exact, since O and l always share the same
+//    reference max and P stays below 2^8.
 #include "common.h"
 #include "launch.h"
 
@@ -41,19 +46,21 @@ namespace gqa {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kRowsPerWave = 32;
-constexpr int kBlockM = kWaves * kRowsPerWave;   // 128 query rows per work-group
+constexpr int kBlockM = kWaves * kRowsPerWave;   // 256 query rows per work-group
 constexpr int kBlockN = 64;                      // keys per tile
 constexpr int kThreads = kWaves * 64;
+constexpr float kRescaleThreshold = 8.f;         // log2 units
 
 template <int D>
 struct PrefillSmem {
-    static constexpr int KS = D + 8;             // K row stride (elements)
-    static constexpr int VS = kBlockN + 8;       // V^T row stride (elements)
+    static constexpr int KS = D + 8;             // K row stride (elements): b128 reads conflict-free
+    static constexpr int VS = D + 32;            // V row stride (elements): tr16 reads conflict-free
     static constexpr int K_ELEMS = kBlockN * KS;
-    static constexpr int V_ELEMS = D * VS;
+    static constexpr int V_ELEMS = kBlockN * VS;
     static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
+    static constexpr int CHUNKS = kBlockN * D / 8 / kThreads;   // 16-byte chunks per thread per tensor
 };
 
 // Row of the A operand that lane-row m loads: bits 2 and 3 swapped.
@@ -61,13 +68,17 @@ __device__ __forceinline__ int swap_bits23(int m) {
     return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(p));
+}
+
 template <int D>
 struct TileRegs {
-    static constexpr int K_CHUNKS = kBlockN * D / 8 / kThreads;    // 16-byte chunks per thread
-    static constexpr int V_TOTAL = (kBlockN / 4) * (D / 8);  // items of 4 keys x 8 dims
-    static constexpr int V_ITEMS = (V_TOTAL + kThreads - 1) / kThreads;
-    u32x4 kc[K_CHUNKS];
-    u32x4 vc[V_ITEMS][4];
+    u32x4 kc[PrefillSmem<D>::CHUNKS];
+    u32x4 vc[PrefillSmem<D>::CHUNKS];
 };
 
 template <int D>
@@ -76,25 +87,17 @@ __device__ __forceinline__ void load_tile(TileRegs<D>& r, const uint16_t* __rest
                                           int key0, int S_kv, int tid) {
     constexpr int CPR = D / 8;   // chunks per key row
 #pragma unroll
-    for (int i = 0; i < TileRegs<D>::K_CHUNKS; ++i) {
-        int c = tid + i * kThreads;
-        int key = c / CPR, dc = c % CPR;
-        int kk = key0 + key;
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (kk < S_kv) val = *(const u32x4*)(kbase + (int64_t)kk * row_stride + dc * 8);
-        r.kc[i] = val;
-    }
-#pragma unroll
-    for (int i = 0; i < TileRegs<D>::V_ITEMS; ++i) {
-        int it = tid + i * kThreads;
-        int dc = it % CPR, kq = it / CPR;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            int kk = key0 + kq * 4 + e;
-            u32x4 val = {0u, 0u, 0u, 0u};
-            if (it < TileRegs<D>::V_TOTAL && kk < S_kv) val = *(const u32x4*)(vbase + (int64_t)kk * row_stride + dc * 8);
-            r.vc[i][e] = val;
+    for (int i = 0; i < PrefillSmem<D>::CHUNKS; ++i) {
+        const int c = tid + i * kThreads;
+        const int kk = key0 + c / CPR;
+        const int64_t off = (int64_t)kk * row_stride + (c % CPR) * 8;
+        u32x4 kval = {0u, 0u, 0u, 0u}, vval = {0u, 0u, 0u, 0u};
+        if (kk < S_kv) {
+            kval = *(const u32x4*)(kbase + off);
+            vval = *(const u32x4*)(vbase + off);
         }
+        r.kc[i] = kval;
+        r.vc[i] = vval;
     }
 }
 
@@ -103,35 +106,17 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& r, uint16_t* __res
                                            int tid) {
     using SM = PrefillSmem<D>;
     constexpr int CPR = D / 8;
-    uint16_t* ks = buf;
-    uint16_t* vt = buf + SM::K_ELEMS;
 #pragma unroll
-    for (int i = 0; i < TileRegs<D>::K_CHUNKS; ++i) {
-        int c = tid + i * kThreads;
-        int key = c / CPR, dc = c % CPR;
-        *(u32x4*)(ks + key * SM::KS + dc * 8) = r.kc[i];
-    }
-#pragma unroll
-    for (int i = 0; i < TileRegs<D>::V_ITEMS; ++i) {
-        int it = tid + i * kThreads;
-        if (it >= TileRegs<D>::V_TOTAL) break;
-        int dc = it % CPR, kq = it / CPR;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {   // dim pair (2p, 2p+1) of this chunk
-            uint32_t w0 = r.vc[i][0][p], w1 = r.vc[i][1][p];
-            uint32_t w2 = r.vc[i][2][p], w3 = r.vc[i][3][p];
-            u32x2 lo = {__builtin_amdgcn_perm(w1, w0, 0x05040100u),
-                        __builtin_amdgcn_perm(w3, w2, 0x05040100u)};
-            u32x2 hi = {__builtin_amdgcn_perm(w1, w0, 0x07060302u),
-                        __builtin_amdgcn_perm(w3, w2, 0x07060302u)};
-            *(u32x2*)(vt + (dc * 8 + 2 * p) * SM::VS + kq * 4) = lo;
-            *(u32x2*)(vt + (dc * 8 + 2 * p + 1) * SM::VS + kq * 4) = hi;
-        }
+    for (int i = 0; i < SM::CHUNKS; ++i) {
+        const int c = tid + i * kThreads;
+        const int key = c / CPR, dc = c % CPR;
+        *(u32x4*)(buf + key * SM::KS + dc * 8) = r.kc[i];
+        *(u32x4*)(buf + SM::K_ELEMS + key * SM::VS + dc * 8) = r.vc[i];
     }
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int B,
     int T_q, int S_kv, int H_q, int H_kv, int G, float c, int q_offset, int n_mblk) {
@@ -172,7 +157,6 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
     }
 
     // Key range of the work-group and of this wave.
-    const int t_lo = r0 / G;
     const int t_hi = min(T_q - 1, (r0 + kBlockM - 1) / G);
     const int kend = CAUSAL ? min(S_kv, q_offset + t_hi + 1) : S_kv;
     const int n_tiles = (kend + kBlockN - 1) / kBlockN;
@@ -182,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
     const int wave_kend = CAUSAL ? min(S_kv, q_offset + wt_hi + 1) : S_kv;
     // keys [0, wave_full) are visible to every row of this wave
     const int wave_full = CAUSAL ? min(S_kv, q_offset + wt_lo + 1) : S_kv;
-    const int pos = CAUSAL ? (valid ? q_offset + t : S_kv) : S_kv;   // last visible key + 1 - 1
+    const int pos = CAUSAL ? (valid ? q_offset + t : S_kv) : S_kv;
 
     const int64_t row_stride = (int64_t)H_kv * D;
     const uint16_t* kbase = k + ((int64_t)b * S_kv * H_kv + kv) * D;
@@ -191,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
     f32x16 oacc[DBLK];
 #pragma unroll
     for (int i = 0; i < DBLK; ++i) oacc[i] = f32x16{};
-    float m_run = -INFINITY;
+    float m_run = -INFINITY;   // reference max (raw score units) used by P
     float l_run = 0.f;
 
     TileRegs<D> regs;
@@ -199,7 +183,13 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
     store_tile<D>(regs, smem, tid);
     __syncthreads();
 
-    const int arow0 = swap_bits23(lq);
+    // K operand rows and V^T transposed-read addresses (per lane, per buffer offset 0)
+    const int krow_off = swap_bits23(lq) * SM::KS + hh * 8;
+    // tr16 source lane L = lane % 16 of group (dh = (lane/16) % 2, hh): key row 8 hh + 4 t + L / 4,
+    // columns 16 dh + 4 (L % 4) of each 32-dim block
+    const int L16 = lane & 15;
+    const int dh = (lane >> 4) & 1;
+    const int vrow_off = (hh * 8 + (L16 >> 2)) * SM::VS + dh * 16 + (L16 & 3) * 4;
 
     for (int j = 0; j < n_tiles; ++j) {
         const bool has_next = j + 1 < n_tiles;
@@ -208,13 +198,13 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
         const int key0 = j * kBlockN;
         if (wave_live && key0 < wave_kend) {
             const uint16_t* ks = smem + (j & 1) * SM::BUF_ELEMS;
-            const uint16_t* vt = ks + SM::K_ELEMS;
+            const uint16_t* vs = ks + SM::K_ELEMS;
             // ---- S^T = K Q^T (two 32-key blocks) ----
             f32x16 s[2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 s[kb] = f32x16{};
-                const uint16_t* krow = ks + (kb * 32 + arow0) * SM::KS + hh * 8;
+                const uint16_t* krow = ks + kb * 32 * SM::KS + krow_off;
 #pragma unroll
                 for (int kst = 0; kst < KSTEPS; ++kst) {
                     bf16x8 a = *(const bf16x8*)(krow + kst * 16);
@@ -222,54 +212,65 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
                 }
             }
             // element i of s[kb] is key key0 + 32 kb + 16 (i / 8) + 8 hh + (i % 8)
-            const bool need_mask = (key0 + kBlockN > wave_full);
-            if (need_mask) {
+            if (key0 + kBlockN > wave_full) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        int key = key0 + kb * 32 + (i >> 3) * 16 + hh * 8 + (i & 7);
+                        const int key = key0 + kb * 32 + (i >> 3) * 16 + hh * 8 + (i & 7);
                         if (key > pos || key >= S_kv) s[kb][i] = -INFINITY;
                     }
             }
-            // ---- online softmax (base 2) ----
-            float mt = s[0][0];
+            // ---- online softmax (base 2), lazy rescale ----
+            float mt = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-            for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[0][i]);
+            for (int i = 1; i < 16; ++i) mt = fmaxf(mt, fmaxf(s[0][i], s[1][i]));
+            {
+                auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
+                                                           false, false);
+                mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            }
+            const bool grow = mt * c > m_run * c + kRescaleThreshold;
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                const float m_new = fmaxf(m_run, mt);
+                // 0 on the first tile; a row with no visible key so far keeps corr = 1
+                const float corr = (m_new == -INFINITY) ? 1.f : fast_exp2((m_run - m_new) * c);
+                l_run *= corr;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[1][i]);
-            mt = max_xor32(mt);
-            const float m_new = fmaxf(m_run, mt);
-            const float mc = (m_new == -INFINITY) ? 0.f : m_new * c;
-            const float corr = fast_exp2(m_run * c - mc);
+                for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) oacc[db][i] *= corr;
+                m_run = m_new;
+            }
+            const float mc = m_run * c;
             float psum = 0.f;
             uint32_t pk[2][8];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; i += 2) {
-                    float p0 = fast_exp2(__builtin_fmaf(s[kb][i], c, -mc));
-                    float p1 = fast_exp2(__builtin_fmaf(s[kb][i + 1], c, -mc));
+                    const float p0 = fast_exp2(__builtin_fmaf(s[kb][i], c, -mc));
+                    const float p1 = fast_exp2(__builtin_fmaf(s[kb][i + 1], c, -mc));
                     psum += p0 + p1;
                     pk[kb][i >> 1] = pack_bf16x2(p0, p1);
                 }
-            l_run = l_run * corr + psum;
-            m_run = m_new;
-#pragma unroll
-            for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) oacc[db][i] *= corr;
+            l_run += psum;
             // ---- O^T += V^T P^T, four 16-key steps ----
 #pragma unroll
             for (int kst = 0; kst < 4; ++kst) {
                 const int kb = kst >> 1, half = kst & 1;
                 u32x4 pw = {pk[kb][half * 4 + 0], pk[kb][half * 4 + 1], pk[kb][half * 4 + 2],
                             pk[kb][half * 4 + 3]};
-                bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+                const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+                const uint16_t* vp = vs + kst * 16 * SM::VS + vrow_off;
 #pragma unroll
                 for (int db = 0; db < DBLK; ++db) {
-                    bf16x8 a = *(const bf16x8*)(vt + (db * 32 + lq) * SM::VS + kst * 16 + hh * 8);
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
+                    s16x4 lo = lds_read_tr16(vp + db * 32);
+                    s16x4 hi = lds_read_tr16(vp + 4 * SM::VS + db * 32);
+                    typedef __attribute__((ext_vector_type(8))) short s16x8;
+                    s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, a8), pb, oacc[db], 0, 0, 0);
                 }
             }
         }
@@ -278,9 +279,13 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
     }
 
     // ---- epilogue: O / l, LSE ----
-    const float l_tot = sum_xor32(l_run);
+    {
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run),
+                                                   false, false);
+        l_run = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
     if (valid) {
-        const float inv = 1.f / l_tot;
+        const float inv = 1.f / l_run;
 #pragma unroll
         for (int db = 0; db < DBLK; ++db)
 #pragma unroll
@@ -290,7 +295,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
                 *(u32x2*)(o + qo_off + db * 32 + u * 8 + hh * 4) = w;
             }
         if (lse != nullptr && hh == 0)
-            lse[qo_off / D] = (m_run * c + fast_log2(l_tot)) * kLn2;
+            lse[qo_off / D] = (m_run * c + fast_log2(l_run)) * kLn2;
     }
 }
 
