@@ -207,6 +207,8 @@ def main():
     ap.add_argument("--decode-workload", default="decode_8k")
     ap.add_argument("--prefill-workload", default="prefill_8k_causal")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", choices=["decode", "prefill"], default=None,
+                    help="run one path only (profiling runs); prints a partial line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
@@ -220,11 +222,18 @@ def main():
     import gqa_attention_flashattention_amd as gq
     gq.load_library()
 
+    if args.only == "prefill":
+        pre = bench_prefill(args.prefill_workload, args.prefill_steps, 2)
+        log(f"[bench] prefill {pre['ms']:.3f} ms/call "
+            f"{pre['flops'] / (pre['ms'] * 1e-3) / 1e12:.1f} TFLOP/s")
+        return
     log(f"[bench] decode {args.decode_workload}: warmup {args.warmup}, steps {args.steps}")
     torch.cuda.synchronize()
     dec = bench_decode(args.decode_workload, args.steps, args.warmup)
     torch.cuda.synchronize()
     log(f"[bench] decode {dec['ms_call'] * 1e3:.2f} us/call, split {dec['ms_split'] * 1e3:.2f} us")
+    if args.only == "decode":
+        return
     log(f"[bench] prefill {args.prefill_workload}: steps {args.prefill_steps}")
     pre = bench_prefill(args.prefill_workload, args.prefill_steps, 2)
     log(f"[bench] prefill {pre['ms']:.3f} ms/call")

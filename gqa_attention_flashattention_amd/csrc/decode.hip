@@ -121,10 +121,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     using SM = DecodeSmem<D>;
     constexpr int KSTEPS = WaveTile<D>::KSTEPS;
     constexpr int DBLK = D / 16;             // 16-row blocks of O^T
-    constexpr int MERGE_FLOATS = kWaves * kCols * (D + 2);
-    constexpr int VT_BYTES = kWaves * SM::VT_ELEMS * 2;
-    constexpr int SMEM_BYTES = VT_BYTES > MERGE_FLOATS * 4 ? VT_BYTES : MERGE_FLOATS * 4;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM_BYTES];
+    constexpr int WSTRIDE = kCols * (D + 2);        // per wave: O [16][D], then m[16], l[16]
+    __shared__ __attribute__((aligned(16))) uint16_t vtiles[kWaves * SM::VT_ELEMS];
+    __shared__ __attribute__((aligned(16))) float mrg[kWaves * WSTRIDE];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -150,6 +149,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const bool col_valid = head < G;
     const int hq = kv * G + (col_valid ? head : 0);
 
+    const int64_t row_stride = (int64_t)H_kv * D;
+    const uint16_t* kseq = k + (plan.key_off[sq] * H_kv + kv) * (int64_t)D;
+    const uint16_t* vseq = v + (plan.key_off[sq] * H_kv + kv) * (int64_t)D;
+    const int n_tiles = (kend - kbeg + kTile - 1) / kTile;
+    // the first tile's K/V loads go out before anything else
+    WaveTile<D> wt;
+    int tt = wave;
+    if (tt < n_tiles) load_wave_tile<D>(wt, kseq, vseq, row_stride, kbeg + tt * kTile, kend, lane);
+
     // Q^T operand: column = query head, k-group g4 = 8 dims per k-step.
     bf16x8 qf[KSTEPS];
 #pragma unroll
@@ -158,11 +166,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
         if (col_valid) val = *(const u32x4*)(q + ((int64_t)b * H_q + hq) * D + s * 32 + g4 * 8);
         qf[s] = __builtin_bit_cast(bf16x8, val);
     }
-
-    const int64_t row_stride = (int64_t)H_kv * D;
-    const uint16_t* kseq = k + (plan.key_off[sq] * H_kv + kv) * (int64_t)D;
-    const uint16_t* vseq = v + (plan.key_off[sq] * H_kv + kv) * (int64_t)D;
-    uint16_t* vt = (uint16_t*)smem + wave * SM::VT_ELEMS;
+    uint16_t* vt = vtiles + wave * SM::VT_ELEMS;
     // transposed-read source address: lane L of group g4 points at key row
     // g4 + 4 (L / 4) (+ 16 for the second read), dims 4 (L % 4) of each 16-dim block
     const uint16_t* vrd = vt + (g4 + 4 * ((lane & 15) >> 2)) * SM::VS + 4 * (lane & 3);
@@ -172,10 +176,6 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     for (int i = 0; i < DBLK; ++i) oacc[i] = f32x4{};
     float m_run = -INFINITY, l_run = 0.f;
 
-    const int n_tiles = (kend - kbeg + kTile - 1) / kTile;
-    WaveTile<D> wt;
-    int tt = wave;
-    if (tt < n_tiles) load_wave_tile<D>(wt, kseq, vseq, row_stride, kbeg + tt * kTile, kend, lane);
     for (; tt < n_tiles; tt += kWaves) {
         const int key0 = kbeg + tt * kTile;
         // S^T for two 16-key blocks; element i of s[blk] is key key0 + g4 + 16 blk + 4 i
@@ -231,9 +231,6 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     // ---- merge the four wave partials through LDS ----
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
-    __syncthreads();                         // every wave is done with its V^T tile
-    float* mrg = (float*)smem;
-    constexpr int WSTRIDE = kCols * (D + 2);        // per wave: O [16][D], then m[16], l[16]
     float* mw_o = mrg + wave * WSTRIDE;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) *(f32x4*)(mw_o + col * D + db * 16 + g4 * 4) = oacc[db];
@@ -270,11 +267,22 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 
 // One wave per (sequence, query head, 32-dim chunk of O).  Lane (sg, dq):
 // split group sg = lane / 8 takes splits sg, sg + 8, sg + 16, ...; dim quad
-// dq = lane % 8 owns dims 4 dq .. 4 dq + 3 of the chunk.  A lane issues all
-// loads of a batch of its splits before using any, the eight split groups
-// are then reduced with a fixed butterfly, so the result does not depend on
-// timing (bitwise reproducible for a given split plan).
+// dq = lane % 8 owns dims 4 dq .. 4 dq + 3 of the chunk.  A lane loads a
+// batch of its splits at once and folds them into a running (m, l, O) with
+// the section 4 merge; the eight split groups are then merged with a fixed
+// butterfly, so the result does not depend on timing (bitwise reproducible
+// for a given split plan).  All in base 2.
 constexpr int kCombineBatch = 4;
+
+__device__ __forceinline__ void merge_lse(float& m, float& l, f32x4& o, float m2, float l2,
+                                          const f32x4& o2) {
+    const float mm = fmaxf(m, m2);
+    const float w1 = (m == -INFINITY) ? 0.f : fast_exp2(m - mm);
+    const float w2 = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - mm);
+    l = l * w1 + l2 * w2;
+    o = o * w1 + o2 * w2;
+    m = mm;
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
@@ -291,16 +299,10 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
     const int n = plan.unit_base[sq + 1] - plan.unit_base[sq];
     const int64_t p0 = (int64_t)plan.split_base + plan.unit_base[sq];
 
-    // global max of the split maxima (base-2 units)
-    float mx = -INFINITY;
-    for (int s = lane; s < n; s += 64) mx = fmaxf(mx, ws_m[(p0 + s) * H_q + h]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-
     const int sg = lane >> 3, dq = lane & 7;
     const int dim = chunk * 32 + dq * 4;
+    float m = -INFINITY, l = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float lsum = 0.f;
     for (int s0 = sg; s0 < n; s0 += 8 * kCombineBatch) {
         float mv[kCombineBatch], lv[kCombineBatch];
         f32x4 ov[kCombineBatch];
@@ -309,30 +311,30 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
             const int s = s0 + 8 * u;
             const int64_t hrow = (p0 + (s < n ? s : 0)) * H_q + h;
             mv[u] = s < n ? ws_m[hrow] : -INFINITY;
-            lv[u] = ws_l[hrow];
+            lv[u] = s < n ? ws_l[hrow] : 0.f;
             ov[u] = *(const f32x4*)(ws_o + hrow * D + dim);
+            if (s >= n) ov[u] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
-        for (int u = 0; u < kCombineBatch; ++u) {
-            const float w = fast_exp2(mv[u] - mx);      // 0 for padding entries
-            lsum += w * lv[u];
-            acc += w * ov[u];
-        }
+        for (int u = 0; u < kCombineBatch; ++u) merge_lse(m, l, acc, mv[u], lv[u], ov[u]);
     }
 #pragma unroll
     for (int off = 8; off <= 32; off <<= 1) {
-        lsum += __shfl_xor(lsum, off);
+        const float m2 = __shfl_xor(m, off);
+        const float l2 = __shfl_xor(l, off);
+        f32x4 o2;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], off);
+        for (int i = 0; i < 4; ++i) o2[i] = __shfl_xor(acc[i], off);
+        merge_lse(m, l, acc, m2, l2, o2);
     }
-    const float inv = 1.f / lsum;
+    const float inv = 1.f / l;
     const int b = plan.seq0 + sq;
     if (sg == 0) {
         u32x2 w = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
         *(u32x2*)(o + ((int64_t)b * H_q + h) * D + dim) = w;
     }
     if (lse != nullptr && chunk == 0 && lane == 0)
-        lse[(int64_t)b * H_q + h] = (mx + fast_log2(lsum)) * kLn2;
+        lse[(int64_t)b * H_q + h] = (m + fast_log2(l)) * kLn2;
 }
 
 }  // namespace

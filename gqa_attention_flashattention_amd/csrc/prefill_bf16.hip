@@ -29,12 +29,13 @@
 //    exactly the B operand of O^T = V^T P^T.  K rows are loaded into the A
 //    operand in a permuted order (bits 2 and 3 of the row index swapped) so
 //    that the 8 keys a lane contributes to each P.V step are consecutive.
-//  * K and V tiles are both stored row-major in LDS with 16-byte writes.  The
-//    V^T operand is read with ds_read_b64_tr_b16 (each lane of a 16-lane group
-//    receives one head-dim column of four key rows), so V is never transposed
-//    in registers.  Row paddings make the b128 K reads and the transposed V
-//    reads bank-conflict free.  LDS is double buffered; the next tile's global
-//    loads are issued before the current tile's math.
+//  * K and V tiles go from HBM/L2 straight into LDS with global_load_lds_dwordx4
+//    (no staging registers), three tiles in flight in a ring of LDS stages:
+//    while tile j is computed, tiles j+1 and j+2 are loading.  Rows are not
+//    padded; instead the 16-byte chunks of each row are XOR-swizzled (chunk c
+//    of row r sits at c ^ f(r)), which makes the b128 K reads and the
+//    ds_read_b64_tr_b16 V^T reads (each lane of a 16-lane group receives one
+//    head-dim column of four key rows) bank-conflict free.
 //  * Lazy rescaling: the running max used for the exponentials is only moved
 //    when some row's tile max exceeds it by more than 8 (log2 units), so most
 //    tiles skip the O rescale; exact, since O and l always share the same
@@ -51,82 +52,104 @@ constexpr int kRowsPerWave = 32;
 constexpr int kBlockM = kWaves * kRowsPerWave;   // 256 query rows per work-group
 constexpr int kBlockN = 64;                      // keys per tile
 constexpr int kThreads = kWaves * 64;
+constexpr int kStages = 3;                       // LDS ring depth (tiles in flight)
 constexpr float kRescaleThreshold = 8.f;         // log2 units
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void global_void_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(8))) short s16x8;
+
 template <int D>
-struct PrefillSmem {
-    static constexpr int KS = D + 8;             // K row stride (elements): b128 reads conflict-free
-    static constexpr int VS = D + 32;            // V row stride (elements): tr16 reads conflict-free
-    static constexpr int K_ELEMS = kBlockN * KS;
-    static constexpr int V_ELEMS = kBlockN * VS;
-    static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
-    static constexpr int CHUNKS = kBlockN * D / 8 / kThreads;   // 16-byte chunks per thread per tensor
+struct Tile {
+    static constexpr int ELEMS = kBlockN * D;            // one K or V tile, unpadded
+    static constexpr int CPR = D / 8;                    // 16-byte chunks per row
+    static constexpr int ROWS_PER_LOAD = 64 / CPR;       // rows per wave load instruction
+    static constexpr int LOADS = kBlockN / ROWS_PER_LOAD / kWaves;   // per wave per tensor
 };
+
+// Physical 16-byte chunk of logical chunk c in row r is c ^ swz(r).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
 
 // Row of the A operand that lane-row m loads: bits 2 and 3 swapped.
 __device__ __forceinline__ int swap_bits23(int m) {
     return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
-typedef __attribute__((ext_vector_type(4))) short s16x4;
-
 __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)(p));
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+
+// Issue this wave's direct global->LDS loads of K and V tile `tile` (keys
+// tile*64 ..) into the given stage buffers.  Keys past S_kv are clamped to the
+// last key: their scores are masked to -inf and their P is exactly 0.
+template <int D>
+__device__ __forceinline__ void issue_tile(uint16_t* kst, uint16_t* vst,
+                                           const uint16_t* __restrict__ kbase,
+                                           const uint16_t* __restrict__ vbase,
+                                           int64_t row_stride, int tile, int S_kv, int wave,
+                                           int lane) {
+    using T = Tile<D>;
+#pragma unroll
+    for (int i = 0; i < T::LOADS; ++i) {
+        const int row0 = (wave * T::LOADS + i) * T::ROWS_PER_LOAD;
+        const int r = row0 + lane / T::CPR;
+        const int cc = (lane % T::CPR) ^ swz<D>(r);
+        const int key = min(tile * kBlockN + r, S_kv - 1);
+        const int64_t off = (int64_t)key * row_stride + cc * 8;
+        __builtin_amdgcn_global_load_lds((const global_void_t*)(kbase + off),
+                                         (lds_void_t*)(kst + row0 * D), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const global_void_t*)(vbase + off),
+                                         (lds_void_t*)(vst + row0 * D), 16, 0, 0);
+    }
+}
+
+// Work-group barrier for LDS traffic only: this wave's LDS operations have
+// completed, then all waves meet.  Unlike __syncthreads() it does not wait for
+// outstanding global->LDS loads of later tiles (those are waited for
+// explicitly with wait_vmcnt); the memory clobber keeps the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wait until at most N of this wave's vector-memory operations are pending.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
 }
 
 template <int D>
-struct TileRegs {
-    u32x4 kc[PrefillSmem<D>::CHUNKS];
-    u32x4 vc[PrefillSmem<D>::CHUNKS];
+struct LaneOffsets {
+    int k[D / 16];            // K operand read offset (elements) per k-step, key block 0
+    int v[2][D / 32];         // V^T tr16 read offset per (half t, 32-dim block), key step 0
 };
-
-template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& r, const uint16_t* __restrict__ kbase,
-                                          const uint16_t* __restrict__ vbase, int64_t row_stride,
-                                          int key0, int S_kv, int tid) {
-    constexpr int CPR = D / 8;   // chunks per key row
-#pragma unroll
-    for (int i = 0; i < PrefillSmem<D>::CHUNKS; ++i) {
-        const int c = tid + i * kThreads;
-        const int kk = key0 + c / CPR;
-        const int64_t off = (int64_t)kk * row_stride + (c % CPR) * 8;
-        u32x4 kval = {0u, 0u, 0u, 0u}, vval = {0u, 0u, 0u, 0u};
-        if (kk < S_kv) {
-            kval = *(const u32x4*)(kbase + off);
-            vval = *(const u32x4*)(vbase + off);
-        }
-        r.kc[i] = kval;
-        r.vc[i] = vval;
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D>& r, uint16_t* __restrict__ buf,
-                                           int tid) {
-    using SM = PrefillSmem<D>;
-    constexpr int CPR = D / 8;
-#pragma unroll
-    for (int i = 0; i < SM::CHUNKS; ++i) {
-        const int c = tid + i * kThreads;
-        const int key = c / CPR, dc = c % CPR;
-        *(u32x4*)(buf + key * SM::KS + dc * 8) = r.kc[i];
-        *(u32x4*)(buf + SM::K_ELEMS + key * SM::VS + dc * 8) = r.vc[i];
-    }
-}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int B,
     int T_q, int S_kv, int H_q, int H_kv, int G, float c, int q_offset, int n_mblk) {
-    using SM = PrefillSmem<D>;
+    using T = Tile<D>;
     constexpr int KSTEPS = D / 16;   // MFMA k-steps over the head dim
     constexpr int DBLK = D / 32;     // 32-row blocks of O^T
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SM::BUF_ELEMS];
+    constexpr int LOADS_PER_TILE = 2 * T::LOADS;   // vmem ops per wave per tile
+    static_assert(LOADS_PER_TILE == 2 || LOADS_PER_TILE == 4, "wait_vmcnt covers 2 and 4");
+    __shared__ __attribute__((aligned(1024))) uint16_t ks0[T::ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t ks1[T::ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t ks2[T::ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t vs0[T::ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t vs1[T::ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t vs2[T::ELEMS];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int lane = tid & 63;
     const int lq = lane & 31;
     const int hh = lane >> 5;
@@ -147,6 +170,31 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const int g = valid ? row % G : 0;
     const int64_t qo_off = (((int64_t)b * T_q + t) * H_q + (int64_t)kv * G + g) * D;
 
+    // Key range of the work-group and of this wave.
+    // (wave- and block-uniform values are pinned to scalar registers so the
+    // branches on them are scalar branches)
+    const int t_hi = min(T_q - 1, (r0 + kBlockM - 1) / G);
+    const int kend = CAUSAL ? min(S_kv, q_offset + t_hi + 1) : S_kv;
+    const int n_tiles = __builtin_amdgcn_readfirstlane((kend + kBlockN - 1) / kBlockN);
+    const bool wave_live = rw0 < rows_total;
+    const int wt_lo = rw0 / G;
+    const int wt_hi = min(T_q - 1, (rw0 + kRowsPerWave - 1) / G);
+    const int wave_kend = __builtin_amdgcn_readfirstlane(
+        wave_live ? (CAUSAL ? min(S_kv, q_offset + wt_hi + 1) : S_kv) : 0);
+    // keys [0, wave_full) are visible to every row of this wave
+    const int wave_full = __builtin_amdgcn_readfirstlane(
+        CAUSAL ? min(S_kv, q_offset + wt_lo + 1) : S_kv);
+    // last key this row may see (rows past the end see everything: their output is dropped)
+    const int last_key = CAUSAL ? (valid ? min(q_offset + t, S_kv - 1) : S_kv - 1) : S_kv - 1;
+
+    const int64_t row_stride = (int64_t)H_kv * D;
+    const uint16_t* kbase = k + ((int64_t)b * S_kv * H_kv + kv) * D;
+    const uint16_t* vbase = v + ((int64_t)b * S_kv * H_kv + kv) * D;
+
+    // tiles 0 and 1 start loading before anything else
+    issue_tile<D>(ks0, vs0, kbase, vbase, row_stride, 0, S_kv, wave, lane);
+    if (n_tiles > 1) issue_tile<D>(ks1, vs1, kbase, vbase, row_stride, 1, S_kv, wave, lane);
+
     // Q^T operand, resident for the whole key sweep.
     bf16x8 qf[KSTEPS];
 #pragma unroll
@@ -156,21 +204,26 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         qf[ks] = __builtin_bit_cast(bf16x8, val);
     }
 
-    // Key range of the work-group and of this wave.
-    const int t_hi = min(T_q - 1, (r0 + kBlockM - 1) / G);
-    const int kend = CAUSAL ? min(S_kv, q_offset + t_hi + 1) : S_kv;
-    const int n_tiles = (kend + kBlockN - 1) / kBlockN;
-    const bool wave_live = rw0 < rows_total;
-    const int wt_lo = rw0 / G;
-    const int wt_hi = min(T_q - 1, (rw0 + kRowsPerWave - 1) / G);
-    const int wave_kend = CAUSAL ? min(S_kv, q_offset + wt_hi + 1) : S_kv;
-    // keys [0, wave_full) are visible to every row of this wave
-    const int wave_full = CAUSAL ? min(S_kv, q_offset + wt_lo + 1) : S_kv;
-    const int pos = CAUSAL ? (valid ? q_offset + t : S_kv) : S_kv;
-
-    const int64_t row_stride = (int64_t)H_kv * D;
-    const uint16_t* kbase = k + ((int64_t)b * S_kv * H_kv + kv) * D;
-    const uint16_t* vbase = v + ((int64_t)b * S_kv * H_kv + kv) * D;
+    // Per-lane LDS read offsets (elements), fixed for the whole sweep.
+    LaneOffsets<D> off;
+    {
+        const int kr = swap_bits23(lq);               // + 32 rows for the second key block
+        const int kf = swz<D>(kr);
+#pragma unroll
+        for (int kst = 0; kst < KSTEPS; ++kst) off.k[kst] = kr * D + (((2 * kst + hh) ^ kf) << 3);
+        const int L16 = lane & 15;
+        const int dh = (lane >> 4) & 1;
+#pragma unroll
+        for (int th = 0; th < 2; ++th) {
+            const int vr = 8 * hh + 4 * th + (L16 >> 2);   // + 16 rows per key step
+            const int vf = swz<D>(vr);
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db) {
+                const int col = 32 * db + 16 * dh + 4 * (L16 & 3);
+                off.v[th][db] = vr * D + (((col >> 3) ^ vf) << 3) + (col & 7);
+            }
+        }
+    }
 
     f32x16 oacc[DBLK];
 #pragma unroll
@@ -178,36 +231,21 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     float m_run = -INFINITY;   // reference max (raw score units) used by P
     float l_run = 0.f;
 
-    TileRegs<D> regs;
-    load_tile<D>(regs, kbase, vbase, row_stride, 0, S_kv, tid);
-    store_tile<D>(regs, smem, tid);
-    __syncthreads();
-
-    // K operand rows and V^T transposed-read addresses (per lane, per buffer offset 0)
-    const int krow_off = swap_bits23(lq) * SM::KS + hh * 8;
-    // tr16 source lane L = lane % 16 of group (dh = (lane/16) % 2, hh): key row 8 hh + 4 t + L / 4,
-    // columns 16 dh + 4 (L % 4) of each 32-dim block
-    const int L16 = lane & 15;
-    const int dh = (lane >> 4) & 1;
-    const int vrow_off = (hh * 8 + (L16 >> 2)) * SM::VS + dh * 16 + (L16 & 3) * 4;
-
-    for (int j = 0; j < n_tiles; ++j) {
-        const bool has_next = j + 1 < n_tiles;
-        if (has_next) load_tile<D>(regs, kbase, vbase, row_stride, (j + 1) * kBlockN, S_kv, tid);
-
+    // One key tile: tile j sits in stage buffers (kt, vt); first tile j + 2 is
+    // issued into (kn, vn), the stage that tile j - 1 used.
+    auto step = [&](int j, const uint16_t* kt, const uint16_t* vt, uint16_t* kn, uint16_t* vn) {
+        const bool issue = j + 2 < n_tiles;
+        if (issue) issue_tile<D>(kn, vn, kbase, vbase, row_stride, j + 2, S_kv, wave, lane);
         const int key0 = j * kBlockN;
-        if (wave_live && key0 < wave_kend) {
-            const uint16_t* ks = smem + (j & 1) * SM::BUF_ELEMS;
-            const uint16_t* vs = ks + SM::K_ELEMS;
+        if (key0 < wave_kend) {
             // ---- S^T = K Q^T (two 32-key blocks) ----
             f32x16 s[2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 s[kb] = f32x16{};
-                const uint16_t* krow = ks + kb * 32 * SM::KS + krow_off;
 #pragma unroll
                 for (int kst = 0; kst < KSTEPS; ++kst) {
-                    bf16x8 a = *(const bf16x8*)(krow + kst * 16);
+                    const bf16x8 a = *(const bf16x8*)(kt + kb * 32 * D + off.k[kst]);
                     s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kst], s[kb], 0, 0, 0);
                 }
             }
@@ -218,7 +256,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int key = key0 + kb * 32 + (i >> 3) * 16 + hh * 8 + (i & 7);
-                        if (key > pos || key >= S_kv) s[kb][i] = -INFINITY;
+                        if (key > last_key) s[kb][i] = -INFINITY;
                     }
             }
             // ---- online softmax (base 2), lazy rescale ----
@@ -259,23 +297,32 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 #pragma unroll
             for (int kst = 0; kst < 4; ++kst) {
                 const int kb = kst >> 1, half = kst & 1;
-                u32x4 pw = {pk[kb][half * 4 + 0], pk[kb][half * 4 + 1], pk[kb][half * 4 + 2],
-                            pk[kb][half * 4 + 3]};
+                const u32x4 pw = {pk[kb][half * 4 + 0], pk[kb][half * 4 + 1],
+                                  pk[kb][half * 4 + 2], pk[kb][half * 4 + 3]};
                 const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-                const uint16_t* vp = vs + kst * 16 * SM::VS + vrow_off;
 #pragma unroll
                 for (int db = 0; db < DBLK; ++db) {
-                    s16x4 lo = lds_read_tr16(vp + db * 32);
-                    s16x4 hi = lds_read_tr16(vp + 4 * SM::VS + db * 32);
-                    typedef __attribute__((ext_vector_type(8))) short s16x8;
-                    s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    const s16x4 lo = lds_read_tr16(vt + kst * 16 * D + off.v[0][db]);
+                    const s16x4 hi = lds_read_tr16(vt + kst * 16 * D + off.v[1][db]);
+                    const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                     oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         __builtin_bit_cast(bf16x8, a8), pb, oacc[db], 0, 0, 0);
                 }
             }
         }
-        if (has_next) store_tile<D>(regs, smem + ((j + 1) & 1) * SM::BUF_ELEMS, tid);
-        __syncthreads();
+        // tile j + 1 (issued one step earlier) must be in LDS for every wave
+        if (issue) wait_vmcnt<LOADS_PER_TILE>();
+        else wait_vmcnt<0>();
+        lds_barrier();
+    };
+
+    if (n_tiles > 1) wait_vmcnt<LOADS_PER_TILE>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    for (int j = 0; j < n_tiles; j += kStages) {
+        step(j, ks0, vs0, ks2, vs2);
+        if (j + 1 < n_tiles) step(j + 1, ks1, vs1, ks0, vs0);
+        if (j + 2 < n_tiles) step(j + 2, ks2, vs2, ks1, vs1);
     }
 
     // ---- epilogue: O / l, LSE ----
