@@ -156,6 +156,32 @@ def bench_prefill(name, steps, warmup):
     return dict(inp=inp, ms=ms, flops=flops, rows=rows, o_rows=o_rows, lse_rows=lse_rows)
 
 
+def copy_calibration(mib: int):
+    """A plain device-to-device copy of `mib` MiB, three times (rocprofv3
+    counter runs scale FETCH_SIZE / WRITE_SIZE by what this copy reads)."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def traffic_record(kernel: str):
+    """HBM bytes per dispatch of `kernel` from profiles/traffic.json, or None
+    when absent or measured on a different kernel source."""
+    from gqa_attention_flashattention_amd import profile_summary as ps
+    path = ps.TRAFFIC_JSON
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel)
+    if not rec or rec.get("source_sha256") != ps.source_sha(kernel):
+        return None
+    return rec["bytes_per_dispatch"]
+
+
 def cpu_threads():
     try:
         return len(os.sched_getaffinity(0))
@@ -209,6 +235,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None,
                     help="run one path only (profiling runs); prints a partial line")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
@@ -221,6 +249,8 @@ def main():
         sys.exit(1)
     import gqa_attention_flashattention_amd as gq
     gq.load_library()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
 
     if args.only == "prefill":
         pre = bench_prefill(args.prefill_workload, args.prefill_steps, 2)
@@ -265,7 +295,8 @@ def main():
         "hot_cache_GBps": round(dec["kv_bytes"] / (dec["ms_hot"] * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "kernel": "decode_split_kernel<128>",
                      "achieved": round(gbs_split, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs_split / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gbs_split / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_record("decode_split_kernel<128>"),
                      "algorithmic_bytes_per_launch": dec["kv_bytes"],
                      "avg_launch_us": round(dec["ms_split"] * 1e3, 3)},
         "prefill": {
@@ -275,7 +306,7 @@ def main():
             "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel<128,true>",
                          "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "traffic": None, "algorithmic_flops_per_launch": pre["flops"],
+                         "traffic": traffic_record("prefill_bf16_kernel<128,true>"), "algorithmic_flops_per_launch": pre["flops"],
                          "avg_launch_us": round(pre["ms"] * 1e3, 3)},
         },
     }
