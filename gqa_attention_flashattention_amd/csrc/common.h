@@ -28,8 +28,22 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Max of x over lanes l and l ^ 32 of a wave64.
-__device__ __forceinline__ float max_xor32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ __forceinline__ float sum_xor32(float x) { return x + __shfl_xor(x, 32); }
+// Value of x held by lane l ^ 32 (v_permlane32_swap: lanes 0-31 <-> 32-63).
+__device__ __forceinline__ float xor32(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((__lane_id() & 32) ? r[0] : r[1]);
+}
+
+// Value of x held by lane l ^ 16 (v_permlane16_swap: 16-lane rows 0 <-> 1, 2 <-> 3).
+__device__ __forceinline__ float xor16(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((__lane_id() & 16) ? r[0] : r[1]);
+}
+
+// Value of x held by lane l ^ 8 (DPP row_ror:8 rotates each 16-lane row by 8).
+__device__ __forceinline__ float xor8(float x) {
+    return __uint_as_float(
+        __builtin_amdgcn_update_dpp(0u, __float_as_uint(x), 0x128, 0xf, 0xf, false));
+}
 
 }  // namespace gqa

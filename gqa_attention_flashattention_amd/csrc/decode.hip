@@ -66,6 +66,10 @@ struct WaveTile {
     u32x4 vr[KPL];                            // V chunks: KPL rows x 8 dims
 };
 
+// Loads are never predicated (a predicated load forces the compiler to wait
+// for it on the spot): keys past the split end are clamped to its last key.
+// Their scores are masked to -inf, so their P is exactly 0 and the clamped
+// (finite) K/V values do not contribute.
 template <int D>
 __device__ __forceinline__ void load_wave_tile(WaveTile<D>& w, const uint16_t* __restrict__ kseq,
                                                const uint16_t* __restrict__ vseq,
@@ -74,23 +78,18 @@ __device__ __forceinline__ void load_wave_tile(WaveTile<D>& w, const uint16_t* _
     const int m = lane & 15, g4 = lane >> 4;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-        const int kk = key0 + tile_key(m, blk);
+        const int kk = min(key0 + tile_key(m, blk), key_end - 1);
 #pragma unroll
-        for (int s = 0; s < WaveTile<D>::KSTEPS; ++s) {
-            u32x4 val = {0u, 0u, 0u, 0u};
-            if (kk < key_end) val = *(const u32x4*)(kseq + (int64_t)kk * row_stride + s * 32 + g4 * 8);
-            w.kf[blk][s] = val;
-        }
+        for (int s = 0; s < WaveTile<D>::KSTEPS; ++s)
+            w.kf[blk][s] = *(const u32x4*)(kseq + (int64_t)kk * row_stride + s * 32 + g4 * 8);
     }
     constexpr int CPR = D / 8;                // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;             // rows per wave instruction
     const int dc = lane % CPR, kg = lane / CPR;
 #pragma unroll
     for (int e = 0; e < WaveTile<D>::KPL; ++e) {
-        const int kk = key0 + e * RPI + kg;
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (kk < key_end) val = *(const u32x4*)(vseq + (int64_t)kk * row_stride + dc * 8);
-        w.vr[e] = val;
+        const int kk = min(key0 + e * RPI + kg, key_end - 1);
+        w.vr[e] = *(const u32x4*)(vseq + (int64_t)kk * row_stride + dc * 8);
     }
 }
 
@@ -147,7 +146,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 
     const int head = hg * kCols + col;       // head within the KV group
     const bool col_valid = head < G;
-    const int hq = kv * G + (col_valid ? head : 0);
+    // columns past the group read a valid head's Q; their outputs are never written
+    const int hq = kv * G + (col_valid ? head : G - 1);
 
     const int64_t row_stride = (int64_t)H_kv * D;
     const uint16_t* kseq = k + (plan.key_off[sq] * H_kv + kv) * (int64_t)D;
@@ -161,11 +161,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     // Q^T operand: column = query head, k-group g4 = 8 dims per k-step.
     bf16x8 qf[KSTEPS];
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (col_valid) val = *(const u32x4*)(q + ((int64_t)b * H_q + hq) * D + s * 32 + g4 * 8);
-        qf[s] = __builtin_bit_cast(bf16x8, val);
-    }
+    for (int s = 0; s < KSTEPS; ++s)
+        qf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q + ((int64_t)b * H_q + hq) * D +
+                                                            s * 32 + g4 * 8));
     uint16_t* vt = vtiles + wave * SM::VT_ELEMS;
     // transposed-read source address: lane L of group g4 points at key row
     // g4 + 4 (L / 4) (+ 16 for the second read), dims 4 (L % 4) of each 16-dim block
@@ -201,8 +199,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
         }
         float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                          fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        mt = fmaxf(mt, xor16(mt));
+        mt = fmaxf(mt, xor32(mt));
         const float m_new = fmaxf(m_run, mt);
         const float mc = (m_new == -INFINITY) ? 0.f : m_new * c;
         const float corr = fast_exp2(m_run * c - mc);
@@ -229,8 +227,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     }
 
     // ---- merge the four wave partials through LDS ----
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    l_run += xor16(l_run);
+    l_run += xor32(l_run);
     float* mw_o = mrg + wave * WSTRIDE;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) *(f32x4*)(mw_o + col * D + db * 16 + g4 * 4) = oacc[db];
@@ -272,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 // the section 4 merge; the eight split groups are then merged with a fixed
 // butterfly, so the result does not depend on timing (bitwise reproducible
 // for a given split plan).  All in base 2.
-constexpr int kCombineBatch = 4;
+constexpr int kCombineBatch = 8;
 
 __device__ __forceinline__ void merge_lse(float& m, float& l, f32x4& o, float m2, float l2,
                                           const f32x4& o2) {
@@ -285,13 +283,13 @@ __device__ __forceinline__ void merge_lse(float& m, float& l, f32x4& o, float m2
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void decode_combine_kernel(
+__global__ __launch_bounds__(64) void decode_combine_kernel(
     const float* __restrict__ ws_m, const float* __restrict__ ws_l,
     const float* __restrict__ ws_o, uint16_t* __restrict__ o, float* __restrict__ lse,
     const DecodePlanChunk plan, int H_q) {
     constexpr int CHUNKS = D / 32;
-    const int lane = threadIdx.x & 63;
-    const int item = blockIdx.x * 4 + (threadIdx.x >> 6);   // (sequence, head, chunk)
+    const int lane = threadIdx.x;
+    const int item = blockIdx.x;   // (sequence, head, chunk)
     if (item >= plan.nseq * H_q * CHUNKS) return;
     const int chunk = item % CHUNKS;
     const int sh = item / CHUNKS;
@@ -319,12 +317,13 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
         for (int u = 0; u < kCombineBatch; ++u) merge_lse(m, l, acc, mv[u], lv[u], ov[u]);
     }
 #pragma unroll
-    for (int off = 8; off <= 32; off <<= 1) {
-        const float m2 = __shfl_xor(m, off);
-        const float l2 = __shfl_xor(l, off);
+    for (int step = 0; step < 3; ++step) {   // partner lanes l ^ 8, l ^ 16, l ^ 32
+        auto other = [step](float x) { return step == 0 ? xor8(x) : step == 1 ? xor16(x) : xor32(x); };
+        const float m2 = other(m);
+        const float l2 = other(l);
         f32x4 o2;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o2[i] = __shfl_xor(acc[i], off);
+        for (int i = 0; i < 4; ++i) o2[i] = other(acc[i]);
         merge_lse(m, l, acc, m2, l2, o2);
     }
     const float inv = 1.f / l;
@@ -360,14 +359,13 @@ hipError_t launch_decode_split_bf16(const void* q, const void* k, const void* v,
 
 hipError_t launch_decode_combine_bf16(const DecodeWorkspace& ws, const DecodePlanChunk& plan,
                                       void* o, float* lse, int H_q, int d, hipStream_t stream) {
-    const int64_t items = (int64_t)plan.nseq * H_q * (d / 32);
-    const int64_t grid = (items + 3) / 4;
+    const int64_t grid = (int64_t)plan.nseq * H_q * (d / 32);   // one wave per item
     if (grid < 1 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     if (d == 128)
-        hipLaunchKernelGGL((decode_combine_kernel<128>), dim3((unsigned)grid), dim3(256), 0, stream,
+        hipLaunchKernelGGL((decode_combine_kernel<128>), dim3((unsigned)grid), dim3(64), 0, stream,
                            ws.m, ws.l, ws.o, (uint16_t*)o, lse, plan, H_q);
     else
-        hipLaunchKernelGGL((decode_combine_kernel<64>), dim3((unsigned)grid), dim3(256), 0, stream,
+        hipLaunchKernelGGL((decode_combine_kernel<64>), dim3((unsigned)grid), dim3(64), 0, stream,
                            ws.m, ws.l, ws.o, (uint16_t*)o, lse, plan, H_q);
     return hipGetLastError();
 }

@@ -166,8 +166,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const int rw0 = r0 + wave * kRowsPerWave;          // first row of this wave
     const int row = rw0 + lq;
     const bool valid = row < rows_total;
-    const int t = valid ? row / G : 0;
-    const int g = valid ? row % G : 0;
+    // rows past the end read the last row's Q (loads are never predicated);
+    // their outputs are not written
+    const int row_c = valid ? row : rows_total - 1;
+    const int t = row_c / G;
+    const int g = row_c % G;
     const int64_t qo_off = (((int64_t)b * T_q + t) * H_q + (int64_t)kv * G + g) * D;
 
     // Key range of the work-group and of this wave.
@@ -198,11 +201,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     // Q^T operand, resident for the whole key sweep.
     bf16x8 qf[KSTEPS];
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (valid) val = *(const u32x4*)(q + qo_off + ks * 16 + hh * 8);
-        qf[ks] = __builtin_bit_cast(bf16x8, val);
-    }
+    for (int ks = 0; ks < KSTEPS; ++ks)
+        qf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q + qo_off + ks * 16 + hh * 8));
 
     // Per-lane LDS read offsets (elements), fixed for the whole sweep.
     LaneOffsets<D> off;
