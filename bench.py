@@ -127,6 +127,37 @@ def bench_decode(name, steps, warmup):
                 n_copies=n_copies, plan=plan, o_gpu=o_gpu, lse_gpu=lse_gpu)
 
 
+def bench_decode_multi(name, steps, warmup):
+    """Multi-token decode (T_q new tokens per sequence) through the one-call
+    entry point, timed by graph replay over rotated K/V copies."""
+    import torch
+    import gqa_attention_flashattention_amd as gq
+    from gqa_attention_flashattention_amd import inputs as gin
+    inp = gin.make(name)
+    w = inp.workload
+    kv_bytes = decode_algorithmic_bytes(w, inp.kv_len)
+    q = dev_tensor(inp.q_store)
+    k0 = dev_tensor(inp.k_store)
+    v0 = dev_tensor(inp.v_store)
+    n_copies = max(1, min(64, math.ceil(ROTATE_BYTES / kv_bytes)))
+    ks = [k0] + [k0.clone() for _ in range(n_copies - 1)]
+    vs = [v0] + [v0.clone() for _ in range(n_copies - 1)]
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+
+    def call(i):
+        return lambda: gq.decode_multi(q, ks[i % n_copies], vs[i % n_copies], inp.kv_len,
+                                       out=out, lse=lse)
+
+    for i in range(max(warmup, 1)):       # also sizes the library workspace before capture
+        call(i)()
+    torch.cuda.synchronize()
+    ms = time_graph([call(i) for i in range(steps)])
+    return dict(inp=inp, kv_bytes=kv_bytes, ms=ms, n_copies=n_copies,
+                o_gpu=out.float().cpu().numpy().astype(np.float64),
+                lse_gpu=lse.cpu().numpy().astype(np.float64))
+
+
 def bench_prefill(name, steps, warmup):
     import torch
     import gqa_attention_flashattention_amd as gq
@@ -224,6 +255,24 @@ def cpu_baseline_prefill(inp, rows, min_seconds=5.0):
                        f"{el:.1f} s"), o, lse
 
 
+def parity_decode_multi(mul, n_seq=2):
+    """Oracle check of the first n_seq sequences of the multi-token decode
+    result (every row of those sequences)."""
+    import oracle
+    inp = mul["inp"]
+    w = inp.workload
+    errs_o, errs_l = [], []
+    off = 0
+    for b, n in enumerate(np.asarray(inp.kv_len).tolist()[:n_seq]):
+        o, l = oracle.prefill(inp.q[b:b + 1], inp.k[None, off:off + n], inp.v[None, off:off + n],
+                              causal=True, q_offset=n - w.T_q)
+        errs_o.append(np.abs(mul["o_gpu"][b] - o[0]).max())
+        errs_l.append(np.abs(mul["lse_gpu"][b] - l[0]).max())
+        off += n
+    return {"decode_multi_sample_max_abs_dO": float(max(errs_o)),
+            "decode_multi_sample_max_abs_dLSE": float(max(errs_l))}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -232,8 +281,10 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--decode-workload", default="decode_8k")
     ap.add_argument("--prefill-workload", default="prefill_8k_causal")
+    ap.add_argument("--multi-workload", default="decode_t4_varlen_b16",
+                    help="multi-token decode workload (reported under decode_multi)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["decode", "prefill"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "decode_multi"], default=None,
                     help="run one path only (profiling runs); prints a partial line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (counter calibration)")
@@ -252,6 +303,11 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
 
+    if args.only == "decode_multi":
+        mul = bench_decode_multi(args.multi_workload, min(args.steps, 200), args.warmup)
+        log(f"[bench] decode_multi {mul['ms'] * 1e3:.2f} us/call "
+            f"{mul['kv_bytes'] / (mul['ms'] * 1e-3) / 1e9:.1f} GB/s")
+        return
     if args.only == "prefill":
         pre = bench_prefill(args.prefill_workload, args.prefill_steps, 2)
         log(f"[bench] prefill {pre['ms']:.3f} ms/call "
@@ -267,6 +323,10 @@ def main():
     log(f"[bench] prefill {args.prefill_workload}: steps {args.prefill_steps}")
     pre = bench_prefill(args.prefill_workload, args.prefill_steps, 2)
     log(f"[bench] prefill {pre['ms']:.3f} ms/call")
+
+    log(f"[bench] decode_multi {args.multi_workload}")
+    mul = bench_decode_multi(args.multi_workload, min(args.steps, 200), args.warmup)
+    log(f"[bench] decode_multi {mul['ms'] * 1e3:.2f} us/call")
 
     dw = dec["inp"].workload
     gbs = dec["kv_bytes"] / (dec["ms_call"] * 1e-3) / 1e9
@@ -310,6 +370,17 @@ def main():
                          "avg_launch_us": round(pre["ms"] * 1e3, 3)},
         },
     }
+    mw = mul["inp"].workload
+    gbs_multi = mul["kv_bytes"] / (mul["ms"] * 1e-3) / 1e9
+    result["decode_multi"] = {
+        "workload": mw.name, "B": mw.B, "T_q": mw.T_q, "H_q": mw.H_q, "H_kv": mw.H_kv, "d": mw.d,
+        "kv_len_range": list(mw.kv_len_range) if mw.kv_len_range else None,
+        "ms_per_call": mul["ms"], "value": round(gbs_multi, 2), "unit": "GB/s",
+        "roofline": {"bound": "hbm", "achieved": round(gbs_multi, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs_multi / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes_per_call": mul["kv_bytes"],
+                     "note": "whole call (split + combine kernels)"},
+    }
     if not args.no_cpu:
         log("[bench] cpu oracle baseline (decode)")
         cb, o_ref, lse_ref = cpu_baseline_decode(dec["inp"], dec["kv_bytes"])
@@ -321,6 +392,8 @@ def main():
         result["prefill"]["cpu_baseline"] = cbp
         result["parity"]["prefill_sample_max_abs_dO"] = float(np.abs(pre["o_rows"] - op).max())
         result["parity"]["prefill_sample_max_abs_dLSE"] = float(np.abs(pre["lse_rows"] - lp).max())
+        log("[bench] oracle check (decode_multi sample)")
+        result["parity"].update(parity_decode_multi(mul))
     print(json.dumps(result), flush=True)
 
 

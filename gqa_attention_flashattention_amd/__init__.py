@@ -5,8 +5,10 @@ C ABI, declared in include/gqa_attn.h).  ``binding`` is the thin ctypes layer
 over it; importing this package does not load the library, the first call
 does, and it raises if the library is missing -- there is no fallback path.
 """
-from .binding import (GQAError, decode, decode_combine, decode_plan, decode_split,  # noqa: F401
+from .binding import (GQAError, decode, decode_combine, decode_multi, decode_plan,  # noqa: F401
+                      decode_split,
                       decode_workspace_bytes, library_path, load_library, prefill)
 
-__all__ = ["GQAError", "prefill", "decode", "decode_split", "decode_combine", "decode_plan",
+__all__ = ["GQAError", "prefill", "decode", "decode_multi", "decode_split", "decode_combine",
+           "decode_plan",
            "decode_workspace_bytes", "load_library", "library_path"]

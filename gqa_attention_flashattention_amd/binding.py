@@ -57,6 +57,8 @@ def load_library():
     lib.gqa_attn_decode_plan.argtypes = [i, i, i, i, vp, i, vp, vp, vp, vp, vp]
     lib.gqa_attn_decode_split.restype = i
     lib.gqa_attn_decode_split.argtypes = [vp, vp, vp, vp, sz, i, i, i, i, vp, f, i, i, vp]
+    lib.gqa_attn_decode_multi.restype = i
+    lib.gqa_attn_decode_multi.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, f, i, i, vp]
     lib.gqa_attn_decode_combine.restype = i
     lib.gqa_attn_decode_combine.argtypes = [vp, sz, vp, vp, i, i, i, i, vp, i, i, vp]
     _lib = lib
@@ -189,6 +191,35 @@ def decode(q, k, v, kv_len, *, scale: float | None = None, num_splits: int = 0, 
                                         _dtype_code(q), _stream(q.device))
     _check(rc, "gqa_attn_decode")
     return out
+
+
+def decode_multi(q, k, v, kv_len, *, scale: float | None = None, num_splits: int = 0,
+                 out=None, lse=None, return_lse: bool = True):
+    """Multi-token decode.  q [B,T_q,H_q,d] bf16 (T_q new tokens per sequence,
+    already appended to the cache), k/v packed [sum(kv_len),H_kv,d].
+    Returns (o [B,T_q,H_q,d], lse [B,T_q,H_q] fp32 or None)."""
+    import torch
+    _require(q, "q", 4)
+    _require(k, "k", 3)
+    _require(v, "v", 3)
+    B, T_q, H_q, d = q.shape
+    if k.shape != v.shape or k.shape[2] != d:
+        raise GQAError("k and v must be [sum(kv_len), H_kv, d] matching q", 2)
+    a = _kv_len_array(kv_len, B)
+    if int(a.astype(np.int64).sum()) != k.shape[0]:
+        raise GQAError("k/v rows must equal sum(kv_len)", 2)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, T_q, H_q), dtype=torch.float32, device=q.device)
+    rc = load_library().gqa_attn_decode_multi(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                              B, T_q, H_q, k.shape[1], d, a.ctypes.data,
+                                              float(scale), int(num_splits), _dtype_code(q),
+                                              _stream(q.device))
+    _check(rc, "gqa_attn_decode_multi")
+    return out, lse
 
 
 def decode_split(q, k, v, kv_len, workspace, *, scale: float | None = None, num_splits: int = 0):

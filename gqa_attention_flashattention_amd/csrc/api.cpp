@@ -22,6 +22,7 @@ constexpr int kTargetSplitWorkgroups = 1024;   // about four per compute unit on
 constexpr int kMinSplitLen = 128;
 constexpr int kMaxSplitLen = 8192;
 constexpr int kSplitAlign = 64;
+constexpr int kMaxDecodeTokens = 256;   // new tokens per sequence in gqa_attn_decode_multi
 
 bool finite_positive(float x) { return isfinite(x) && x > 0.f; }
 
@@ -48,8 +49,8 @@ int env_split_len() {
     return cached;
 }
 
-int make_plan(int B, int H_q, int H_kv, const int32_t* kv_len, int num_splits, int32_t* splits,
-              int32_t* lens, Plan* out) {
+int make_plan(int B, int T_q, int H_q, int H_kv, const int32_t* kv_len, int num_splits,
+              int32_t* splits, int32_t* lens, Plan* out) {
     if (kv_len == nullptr) return GQA_ERR_NULL;
     if (B < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv) return GQA_ERR_SHAPE;
     int64_t total_keys = 0;
@@ -58,7 +59,7 @@ int make_plan(int B, int H_q, int H_kv, const int32_t* kv_len, int num_splits, i
         total_keys += kv_len[b];
     }
     const int G = H_q / H_kv;
-    const int n_hg = (G + 15) / 16;
+    const int n_hg = (T_q * G + 15) / 16;
     int64_t auto_len = 0;
     if (num_splits <= 0) {
         int forced = env_split_len();
@@ -95,16 +96,17 @@ int make_plan(int B, int H_q, int H_kv, const int32_t* kv_len, int num_splits, i
     return GQA_OK;
 }
 
-size_t workspace_bytes_for(int64_t total, int H_q, int d) {
-    return (size_t)total * (size_t)H_q * (size_t)(d + 2) * sizeof(float);
+// rows = partial rows per split: T_q * H_q
+size_t workspace_bytes_for(int64_t total, int rows, int d) {
+    return (size_t)total * (size_t)rows * (size_t)(d + 2) * sizeof(float);
 }
 
-DecodeWorkspace carve(void* base, int64_t total, int H_q) {
+DecodeWorkspace carve(void* base, int64_t total, int rows) {
     float* f = (float*)base;
     DecodeWorkspace ws;
     ws.m = f;
-    ws.l = f + total * H_q;
-    ws.o = f + 2 * total * H_q;
+    ws.l = f + total * rows;
+    ws.o = f + 2 * total * rows;
     return ws;
 }
 
@@ -158,11 +160,11 @@ struct HostPlan {
         free(splits);
         free(lens);
     }
-    int build(int B, int H_q, int H_kv, const int32_t* kv_len, int num_splits) {
+    int build(int B, int H_q, int H_kv, const int32_t* kv_len, int num_splits, int T_q = 1) {
         splits = (int32_t*)malloc(sizeof(int32_t) * (size_t)B);
         lens = (int32_t*)malloc(sizeof(int32_t) * (size_t)B);
         if (!splits || !lens) return GQA_ERR_SHAPE;
-        return make_plan(B, H_q, H_kv, kv_len, num_splits, splits, lens, &p);
+        return make_plan(B, T_q, H_q, H_kv, kv_len, num_splits, splits, lens, &p);
     }
 };
 
@@ -268,7 +270,7 @@ int gqa_attn_decode_split(const void* q, const void* k, const void* v, void* wor
     DecodeWorkspace ws = carve(workspace, hp.p.total, H_q);
     (void)hipGetLastError();
     return for_each_chunk(B, kv_len, hp.splits, hp.lens, [&](const DecodePlanChunk& c) {
-        return gqa::launch_decode_split_bf16(q, k, v, ws, c, H_q, H_kv, d, scale,
+        return gqa::launch_decode_split_bf16(q, k, v, ws, c, 1, H_q, H_kv, d, scale,
                                              (hipStream_t)stream);
     });
 }
@@ -288,7 +290,7 @@ int gqa_attn_decode_combine(const void* workspace, size_t workspace_bytes, void*
     DecodeWorkspace ws = carve((void*)workspace, hp.p.total, H_q);
     (void)hipGetLastError();
     return for_each_chunk(B, kv_len, hp.splits, hp.lens, [&](const DecodePlanChunk& c) {
-        return gqa::launch_decode_combine_bf16(ws, c, o, lse, H_q, d, (hipStream_t)stream);
+        return gqa::launch_decode_combine_bf16(ws, c, o, lse, 1, H_q, d, (hipStream_t)stream);
     });
 }
 
@@ -308,12 +310,41 @@ int gqa_attn_decode(const void* q, const void* k, const void* v, void* o, int B,
     DecodeWorkspace ws = carve(base, hp.p.total, H_q);
     (void)hipGetLastError();
     rc = for_each_chunk(B, kv_len, hp.splits, hp.lens, [&](const DecodePlanChunk& c) {
-        return gqa::launch_decode_split_bf16(q, k, v, ws, c, H_q, H_kv, d, scale,
+        return gqa::launch_decode_split_bf16(q, k, v, ws, c, 1, H_q, H_kv, d, scale,
                                              (hipStream_t)stream);
     });
     if (rc) return rc;
     return for_each_chunk(B, kv_len, hp.splits, hp.lens, [&](const DecodePlanChunk& c) {
-        return gqa::launch_decode_combine_bf16(ws, c, o, nullptr, H_q, d, (hipStream_t)stream);
+        return gqa::launch_decode_combine_bf16(ws, c, o, nullptr, 1, H_q, d, (hipStream_t)stream);
+    });
+}
+
+int gqa_attn_decode_multi(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int T_q, int H_q, int H_kv, int d, const int32_t* kv_len,
+                          float scale, int num_splits, int dtype, void* stream) {
+    int rc = check_decode_args(q, k, v, B, H_q, H_kv, d, kv_len, scale, dtype);
+    if (rc) return rc;
+    if (!o) return GQA_ERR_NULL;
+    if (T_q < 1 || T_q > kMaxDecodeTokens) return GQA_ERR_SHAPE;
+    for (int b = 0; b < B; ++b)
+        if (kv_len[b] < T_q) return GQA_ERR_SHAPE;   // the new tokens are in the cache
+    HostPlan hp;
+    rc = hp.build(B, H_q, H_kv, kv_len, num_splits, T_q);
+    if (rc) return rc;
+    const int rows = T_q * H_q;
+    const size_t need = workspace_bytes_for(hp.p.total, rows, d);
+    void* base = nullptr;
+    rc = get_workspace(need, &base);
+    if (rc) return rc;
+    DecodeWorkspace ws = carve(base, hp.p.total, rows);
+    (void)hipGetLastError();
+    rc = for_each_chunk(B, kv_len, hp.splits, hp.lens, [&](const DecodePlanChunk& c) {
+        return gqa::launch_decode_split_bf16(q, k, v, ws, c, T_q, H_q, H_kv, d, scale,
+                                             (hipStream_t)stream);
+    });
+    if (rc) return rc;
+    return for_each_chunk(B, kv_len, hp.splits, hp.lens, [&](const DecodePlanChunk& c) {
+        return gqa::launch_decode_combine_bf16(ws, c, o, lse, T_q, H_q, d, (hipStream_t)stream);
     });
 }
 

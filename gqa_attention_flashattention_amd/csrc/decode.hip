@@ -2,10 +2,12 @@
 // kernel writing unnormalised partials and a log-sum-exp combine kernel.
 //
 // Method (ADR-0060 page, "AHBM GQA Fused Attention kernel (Llama3-70B)"):
-//  * Decode has one query token per sequence; the G query heads of a KV head
-//    are folded into the matmul M dimension so each K/V tile is read once for
-//    all of them (section 5.2).  There is no causal mask, only a bounds mask
-//    on the ragged last tile of a split.
+//  * Decode has one (or, for multi-token decode, T_q <= 16-ish) query token
+//    per sequence; the G query heads of a KV head (times the T_q tokens) are
+//    folded into the matmul M dimension so each K/V tile is read once for all
+//    of them (section 5.2, "G * T_q" rows).  With one token there is no causal
+//    mask, only a bounds mask on the ragged last tile of a split; with T_q new
+//    tokens, token t at position len - T_q + t sees keys up to itself.
 //  * The keys of a sequence are sharded; every shard produces the
 //    unnormalised triplet (m_i, l_i, O_i) of the online softmax (sections 3
 //    and 5.3), and the shards are reduced once, at the owner, with the
@@ -115,8 +117,8 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ ws_m, float* __restrict__ ws_l,
-    float* __restrict__ ws_o, const DecodePlanChunk plan, int H_q, int H_kv, int G, int n_hg,
-    float c) {
+    float* __restrict__ ws_o, const DecodePlanChunk plan, int T_q, int H_q, int H_kv, int G,
+    int n_hg, float c) {
     using SM = DecodeSmem<D>;
     constexpr int KSTEPS = WaveTile<D>::KSTEPS;
     constexpr int DBLK = D / 16;             // 16-row blocks of O^T
@@ -144,10 +146,17 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const int kend = min(len, kbeg + L);
     const int b = plan.seq0 + sq;
 
-    const int head = hg * kCols + col;       // head within the KV group
-    const bool col_valid = head < G;
-    // columns past the group read a valid head's Q; their outputs are never written
-    const int hq = kv * G + (col_valid ? head : G - 1);
+    // MFMA column -> (new token t, query head g of this KV group); the G * T_q
+    // query rows of a KV head are the M dimension, split into blocks of 16.
+    const int f = hg * kCols + col;
+    const bool col_valid = f < T_q * G;
+    // columns past the end read a valid row's Q; their outputs are never written
+    const int fc = col_valid ? f : T_q * G - 1;
+    const int tq = fc / G;
+    const int hq = kv * G + fc % G;
+    // new token tq sits at position len - T_q + tq and sees keys up to it
+    const int vis_end = min(kend, len - T_q + tq + 1);
+    const int mask_from = min(kend, len - T_q + 1);   // keys before this are visible to all
 
     const int64_t row_stride = (int64_t)H_kv * D;
     const uint16_t* kseq = k + (plan.key_off[sq] * H_kv + kv) * (int64_t)D;
@@ -162,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     bf16x8 qf[KSTEPS];
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s)
-        qf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q + ((int64_t)b * H_q + hq) * D +
+        qf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q + (((int64_t)b * T_q + tq) * H_q + hq) * D +
                                                             s * 32 + g4 * 8));
     uint16_t* vt = vtiles + wave * SM::VT_ELEMS;
     // transposed-read source address: lane L of group g4 points at key row
@@ -190,12 +199,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
         store_v<D>(wt, vt, lane);
         const int nt = tt + kWaves;
         if (nt < n_tiles) load_wave_tile<D>(wt, kseq, vseq, row_stride, kbeg + nt * kTile, kend, lane);
-        if (key0 + kTile > kend) {
+        if (key0 + kTile > mask_from) {
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (key0 + g4 + 16 * blk + 4 * i >= kend) s[blk][i] = -INFINITY;
+                    if (key0 + g4 + 16 * blk + 4 * i >= vis_end) s[blk][i] = -INFINITY;
         }
         float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                          fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
@@ -240,7 +249,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const int64_t pidx = (int64_t)plan.split_base + unit;
     for (int e = tid; e < kCols * (D / 4); e += kThreads) {
         const int cc = e / (D / 4), x = (e % (D / 4)) * 4;
-        if (hg * kCols + cc >= G) continue;
+        const int fo = hg * kCols + cc;
+        if (fo >= T_q * G) continue;
         float mx = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, mrg[w * WSTRIDE + kCols * D + cc]);
@@ -254,7 +264,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
             acc += sc * *(const f32x4*)(base + cc * D + x);
             lsum += sc * base[kCols * D + kCols + cc];
         }
-        const int64_t hrow = pidx * H_q + (int64_t)kv * G + hg * kCols + cc;
+        // partial row: (split, new token, query head)
+        const int64_t hrow = (pidx * T_q + fo / G) * H_q + (int64_t)kv * G + fo % G;
         *(f32x4*)(ws_o + hrow * D + x) = acc;
         if (x == 0) {
             ws_m[hrow] = mx * c;             // base-2 units
@@ -286,14 +297,15 @@ template <int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(
     const float* __restrict__ ws_m, const float* __restrict__ ws_l,
     const float* __restrict__ ws_o, uint16_t* __restrict__ o, float* __restrict__ lse,
-    const DecodePlanChunk plan, int H_q) {
+    const DecodePlanChunk plan, int T_q, int H_q) {
     constexpr int CHUNKS = D / 32;
+    const int R = T_q * H_q;                                   // rows per sequence
     const int lane = threadIdx.x;
     const int item = blockIdx.x;   // (sequence, head, chunk)
-    if (item >= plan.nseq * H_q * CHUNKS) return;
+    if (item >= plan.nseq * R * CHUNKS) return;
     const int chunk = item % CHUNKS;
     const int sh = item / CHUNKS;
-    const int sq = sh / H_q, h = sh % H_q;
+    const int sq = sh / R, r = sh % R;                         // r = t * H_q + h
     const int n = plan.unit_base[sq + 1] - plan.unit_base[sq];
     const int64_t p0 = (int64_t)plan.split_base + plan.unit_base[sq];
 
@@ -307,7 +319,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
 #pragma unroll
         for (int u = 0; u < kCombineBatch; ++u) {
             const int s = s0 + 8 * u;
-            const int64_t hrow = (p0 + (s < n ? s : 0)) * H_q + h;
+            const int64_t hrow = (p0 + (s < n ? s : 0)) * R + r;
             mv[u] = s < n ? ws_m[hrow] : -INFINITY;
             lv[u] = s < n ? ws_l[hrow] : 0.f;
             ov[u] = *(const f32x4*)(ws_o + hrow * D + dim);
@@ -330,43 +342,45 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
     const int b = plan.seq0 + sq;
     if (sg == 0) {
         u32x2 w = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
-        *(u32x2*)(o + ((int64_t)b * H_q + h) * D + dim) = w;
+        *(u32x2*)(o + ((int64_t)b * R + r) * D + dim) = w;
     }
     if (lse != nullptr && chunk == 0 && lane == 0)
-        lse[(int64_t)b * H_q + h] = (m + fast_log2(l)) * kLn2;
+        lse[(int64_t)b * R + r] = (m + fast_log2(l)) * kLn2;
 }
 
 }  // namespace
 
 hipError_t launch_decode_split_bf16(const void* q, const void* k, const void* v,
                                     const DecodeWorkspace& ws, const DecodePlanChunk& plan,
-                                    int H_q, int H_kv, int d, float scale, hipStream_t stream) {
+                                    int T_q, int H_q, int H_kv, int d, float scale,
+                                    hipStream_t stream) {
     const int G = H_q / H_kv;
-    const int n_hg = (G + kCols - 1) / kCols;
+    const int n_hg = (T_q * G + kCols - 1) / kCols;
     const int64_t grid = (int64_t)plan.units * n_hg * H_kv;
     if (grid < 1 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     const float c = scale * kLog2e;
     if (d == 128)
         hipLaunchKernelGGL((decode_split_kernel<128>), dim3((unsigned)grid), dim3(kThreads), 0,
                            stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                           ws.m, ws.l, ws.o, plan, H_q, H_kv, G, n_hg, c);
+                           ws.m, ws.l, ws.o, plan, T_q, H_q, H_kv, G, n_hg, c);
     else
         hipLaunchKernelGGL((decode_split_kernel<64>), dim3((unsigned)grid), dim3(kThreads), 0,
                            stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                           ws.m, ws.l, ws.o, plan, H_q, H_kv, G, n_hg, c);
+                           ws.m, ws.l, ws.o, plan, T_q, H_q, H_kv, G, n_hg, c);
     return hipGetLastError();
 }
 
 hipError_t launch_decode_combine_bf16(const DecodeWorkspace& ws, const DecodePlanChunk& plan,
-                                      void* o, float* lse, int H_q, int d, hipStream_t stream) {
-    const int64_t grid = (int64_t)plan.nseq * H_q * (d / 32);   // one wave per item
+                                      void* o, float* lse, int T_q, int H_q, int d,
+                                      hipStream_t stream) {
+    const int64_t grid = (int64_t)plan.nseq * T_q * H_q * (d / 32);   // one wave per item
     if (grid < 1 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     if (d == 128)
         hipLaunchKernelGGL((decode_combine_kernel<128>), dim3((unsigned)grid), dim3(64), 0, stream,
-                           ws.m, ws.l, ws.o, (uint16_t*)o, lse, plan, H_q);
+                           ws.m, ws.l, ws.o, (uint16_t*)o, lse, plan, T_q, H_q);
     else
         hipLaunchKernelGGL((decode_combine_kernel<64>), dim3((unsigned)grid), dim3(64), 0, stream,
-                           ws.m, ws.l, ws.o, (uint16_t*)o, lse, plan, H_q);
+                           ws.m, ws.l, ws.o, (uint16_t*)o, lse, plan, T_q, H_q);
     return hipGetLastError();
 }
 

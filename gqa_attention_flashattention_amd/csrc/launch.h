@@ -42,10 +42,14 @@ struct DecodeWorkspace {
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 
+// T_q new tokens per sequence (1 for plain decode); partial and output rows are
+// (sequence, token, query head).
 hipError_t launch_decode_split_bf16(const void* q, const void* k, const void* v,
                                     const DecodeWorkspace& ws, const DecodePlanChunk& plan,
-                                    int H_q, int H_kv, int d, float scale, hipStream_t stream);
+                                    int T_q, int H_q, int H_kv, int d, float scale,
+                                    hipStream_t stream);
 hipError_t launch_decode_combine_bf16(const DecodeWorkspace& ws, const DecodePlanChunk& plan,
-                                      void* o, float* lse, int H_q, int d, hipStream_t stream);
+                                      void* o, float* lse, int T_q, int H_q, int d,
+                                      hipStream_t stream);
 
 }  // namespace gqa

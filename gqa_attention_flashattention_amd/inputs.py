@@ -29,7 +29,7 @@ class Workload:
     H_q: int
     H_kv: int
     d: int
-    T_q: int = 1            # prefill only
+    T_q: int = 1            # prefill query rows, or new tokens per sequence in decode
     S_kv: int = 0           # prefill keys, or fixed decode length
     causal: bool = False
     q_offset: int = 0
@@ -56,6 +56,8 @@ WORKLOADS = {
         Workload("decode_128k", "decode", "bf16", B=1, H_q=64, H_kv=8, d=128, S_kv=131072),
         Workload("prefill_chunk_64k", "prefill", "bf16", B=1, H_q=64, H_kv=8, d=128,
                  T_q=2048, S_kv=67584, causal=True, q_offset=65536),
+        Workload("decode_t4_varlen_b16", "decode", "bf16", B=16, H_q=64, H_kv=8, d=128,
+                 T_q=4, kv_len_range=(1024, 32768)),
     ]
 }
 
@@ -101,6 +103,8 @@ def shapes(w: Workload, kv_len: np.ndarray | None):
     if w.kind == "prefill":
         return ((w.B, w.T_q, w.H_q, w.d), (w.B, w.S_kv, w.H_kv, w.d))
     total = int(np.asarray(kv_len, np.int64).sum())
+    if w.T_q > 1:   # multi-token decode: T_q new tokens per sequence
+        return ((w.B, w.T_q, w.H_q, w.d), (total, w.H_kv, w.d))
     return ((w.B, w.H_q, w.d), (total, w.H_kv, w.d))
 
 

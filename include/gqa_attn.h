@@ -152,6 +152,27 @@ int gqa_attn_decode_combine(const void *workspace, size_t workspace_bytes, void 
                             float *lse, int B, int H_q, int H_kv, int d,
                             const int32_t *kv_len, int num_splits, int dtype, void *stream);
 
+/*
+ * Multi-token decode (speculative verification, batched new tokens): T_q new
+ * tokens per sequence whose K/V rows are already the last T_q rows of the
+ * sequence in the cache.  The G query heads times the T_q tokens of a KV head
+ * are folded into the matmul M dimension (ADR-0060 section 5.2: G * T_q rows
+ * per KV tile), keys are split across work-groups and merged as in
+ * gqa_attn_decode.  New token t of sequence b sits at position
+ * kv_len[b] - T_q + t and attends to keys 0 .. kv_len[b] - T_q + t (causal
+ * among the new tokens, bottom-right aligned, as in gqa_attn_prefill with
+ * q_offset = kv_len[b] - T_q).
+ *   q, o [B, T_q, H_q, d] (dtype)        lse [B, T_q, H_q] fp32, may be NULL
+ *   k, v packed [sum_b kv_len[b], H_kv, d], kv_len HOST array [B]
+ * Requires 1 <= T_q <= 256 and kv_len[b] >= T_q.  Uses the library-owned
+ * workspace like gqa_attn_decode (same concurrency rule).
+ * Errors: GQA_ERR_NULL, GQA_ERR_SHAPE, GQA_ERR_UNSUPPORTED, GQA_ERR_RANGE,
+ * GQA_ERR_HIP.
+ */
+int gqa_attn_decode_multi(const void *q, const void *k, const void *v, void *o, float *lse,
+                          int B, int T_q, int H_q, int H_kv, int d, const int32_t *kv_len,
+                          float scale, int num_splits, int dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,8 +23,8 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ["gqa_attn_prefill", "gqa_attn_decode", "gqa_attn_decode_split",
-              "gqa_attn_decode_combine", "gqa_attn_decode_plan", "gqa_attn_status_string",
-              "gqa_attn_version"]:
+              "gqa_attn_decode_combine", "gqa_attn_decode_plan", "gqa_attn_decode_multi",
+              "gqa_attn_status_string", "gqa_attn_version"]:
         assert n in names
 
 
@@ -80,6 +80,25 @@ def _decode(kv_len, **kw):
 ])
 def test_decode_rejects(kv_len, kw, code):
     assert _decode(kv_len, **kw) == code
+
+
+def _decode_multi(kv_len, **kw):
+    a = dict(q=P, k=P, v=P, o=P, B=len(kv_len), T=2, Hq=8, Hkv=2, d=128, scale=0.1, ns=0, dtype=0)
+    a.update(kw)
+    arr = np.asarray(kv_len, np.int32)
+    return gq.load_library().gqa_attn_decode_multi(
+        a["q"], a["k"], a["v"], a["o"], None, a["B"], a["T"], a["Hq"], a["Hkv"], a["d"],
+        arr.ctypes.data if kv_len else None, a["scale"], a["ns"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kv_len,kw,code", [
+    ([4], dict(q=None), 1), ([4], dict(o=None), 1), ([], dict(B=1), 1),
+    ([4, 1], {}, 2),                     # fewer keys than new tokens
+    ([4], dict(T=0), 2), ([400], dict(T=257), 2), ([4], dict(Hq=9), 2),
+    ([4], dict(d=32), 3), ([4], dict(dtype=1), 3), ([4], dict(scale=0.0), 4),
+])
+def test_decode_multi_rejects(kv_len, kw, code):
+    assert _decode_multi(kv_len, **kw) == code
 
 
 def test_split_and_combine_reject_small_workspace():

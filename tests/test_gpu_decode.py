@@ -117,3 +117,90 @@ def test_full_size_workloads(name):
     assert_close(og, oref, lg, lref, name=name)
     og2 = _decode(inp)
     assert np.array_equal(og2, og)
+
+
+# ---- multi-token decode: T_q new tokens per sequence, causal among them ----
+
+def _as_multi(inp):
+    """Decode inputs with one token per sequence get an explicit T_q = 1 axis."""
+    if inp.q.ndim == 3:
+        inp.q = inp.q[:, None]
+        inp.q_store = inp.q_store[:, None]
+    return inp
+
+
+def _oracle_multi(inp):
+    """Per sequence: the oracle prefill of its T_q new tokens against its
+    cache, causal with the new tokens at the end (q_offset = len - T_q)."""
+    B, T_q, Hq, d = inp.q.shape
+    o = np.empty((B, T_q, Hq, d))
+    lse = np.empty((B, T_q, Hq))
+    off = 0
+    for b, n in enumerate(np.asarray(inp.kv_len).tolist()):
+        ob, lb = oracle.prefill(inp.q[b:b + 1], inp.k[None, off:off + n], inp.v[None, off:off + n],
+                                causal=True, q_offset=n - T_q)
+        o[b], lse[b] = ob[0], lb[0]
+        off += n
+    return o, lse
+
+
+def _decode_multi(inp, num_splits=0):
+    import gqa_attention_flashattention_amd as gq
+    import torch
+    q, k, v = _dev(inp)
+    o, lse = gq.decode_multi(q, k, v, inp.kv_len, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return to_f64(o), to_f64(lse)
+
+
+@pytest.mark.parametrize("T_q,kv_len,Hq,Hkv,d", [
+    (1, [1, 33, 700], 64, 8, 128),
+    (2, [2, 3, 64, 65, 1000], 64, 8, 128),
+    (3, [3, 31, 130], 64, 8, 64),        # G * T_q = 24: partial second column block
+    (4, [4, 5, 4097], 64, 8, 128),
+    (8, [8, 9, 40, 513], 64, 8, 128),
+    (16, [16, 17, 333], 64, 8, 128),      # G * T_q = 128: eight column blocks
+    (5, [77, 300, 5], 12, 4, 128),        # G = 3, odd T_q
+    (2, [250, 40], 20, 1, 64),            # G = 20
+    (7, [129, 7], 8, 8, 128),             # G = 1
+])
+def test_decode_multi_parity(T_q, kv_len, Hq, Hkv, d):
+    inp = _as_multi(gin.random_case("decode", "bf16", B=len(kv_len), H_q=Hq, H_kv=Hkv, d=d,
+                                    T_q=T_q, kv_len=kv_len, seed=T_q * 1000 + sum(kv_len)))
+    og, lg = _decode_multi(inp)
+    oref, lref = _oracle_multi(inp)
+    assert_close(og, oref, lg, lref, name=f"decode_multi T_q={T_q} {kv_len} {Hq}/{Hkv} d={d}")
+
+
+@pytest.mark.parametrize("num_splits", [1, 3, 1000])
+def test_decode_multi_split_counts(num_splits):
+    """Splits that end inside the new tokens' causal band (some splits are
+    wholly in the future for the earlier new tokens)."""
+    kv_len = [1000, 9, 257]
+    inp = gin.random_case("decode", "bf16", B=3, H_q=64, H_kv=8, d=128, T_q=8, kv_len=kv_len,
+                          seed=21)
+    og, lg = _decode_multi(inp, num_splits)
+    oref, lref = _oracle_multi(inp)
+    assert_close(og, oref, lg, lref, name=f"decode_multi splits={num_splits}")
+
+
+def test_decode_multi_one_token_matches_decode():
+    """T_q = 1 is plain decode: same kernels, bitwise equal outputs."""
+    import gqa_attention_flashattention_amd as gq
+    import torch
+    kv_len = [300, 4000, 1]
+    inp = gin.random_case("decode", "bf16", B=3, H_q=64, H_kv=8, d=128, kv_len=kv_len, seed=22)
+    q, k, v = _dev(inp)
+    o1 = gq.decode(q, k, v, inp.kv_len)
+    om, _ = gq.decode_multi(q[:, None], k, v, inp.kv_len)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, om[:, 0])
+
+
+def test_decode_multi_full_size():
+    """The multi-token decode workload (16 ragged sequences, 4 new tokens),
+    every output element against the oracle."""
+    inp = gin.make("decode_t4_varlen_b16")
+    og, lg = _decode_multi(inp)
+    oref, lref = _oracle_multi(inp)
+    assert_close(og, oref, lg, lref, name="decode_t4_varlen_b16")
