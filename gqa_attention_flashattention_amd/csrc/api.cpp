@@ -59,7 +59,7 @@ int make_plan(int B, int T_q, int H_q, int H_kv, const int32_t* kv_len, int num_
         total_keys += kv_len[b];
     }
     const int G = H_q / H_kv;
-    const int n_hg = (T_q * G + 15) / 16;
+    const int n_hg = gqa::decode_column_groups(T_q, G);
     int64_t auto_len = 0;
     if (num_splits <= 0) {
         int forced = env_split_len();

@@ -113,8 +113,8 @@ __device__ __forceinline__ void wave_lds_fence() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(
+template <int D, int NH>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ ws_m, float* __restrict__ ws_l,
     float* __restrict__ ws_o, const DecodePlanChunk plan, int T_q, int H_q, int H_kv, int G,
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    const int col = lane & 15;               // query head within the 16-head block
+    const int col = lane & 15;               // MFMA column within a 16-column block
     const int g4 = lane >> 4;
 
     int bid = blockIdx.x;
@@ -145,19 +145,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const int kbeg = split * L;
     const int kend = min(len, kbeg + L);
     const int b = plan.seq0 + sq;
+    const int ncols = T_q * G;
 
-    // MFMA column -> (new token t, query head g of this KV group); the G * T_q
-    // query rows of a KV head are the M dimension, split into blocks of 16.
-    const int f = hg * kCols + col;
-    const bool col_valid = f < T_q * G;
-    // columns past the end read a valid row's Q; their outputs are never written
-    const int fc = col_valid ? f : T_q * G - 1;
-    const int tq = fc / G;
-    const int hq = kv * G + fc % G;
-    // new token tq sits at position len - T_q + tq and sees keys up to it
-    const int vis_end = min(kend, len - T_q + tq + 1);
-    const int mask_from = min(kend, len - T_q + 1);   // keys before this are visible to all
-
+    // MFMA columns: the G * T_q query rows (new token t, query head g) of a KV
+    // head, in blocks of 16; this work-group takes blocks hg*NH .. hg*NH+NH-1,
+    // so every K/V tile it loads serves up to 16*NH rows.
+    // vis_end[h]: new token t sits at position len - T_q + t and sees keys up to it.
+    int vis_end[NH];
+    bf16x8 qf[NH][KSTEPS];
     const int64_t row_stride = (int64_t)H_kv * D;
     const uint16_t* kseq = k + (plan.key_off[sq] * H_kv + kv) * (int64_t)D;
     const uint16_t* vseq = v + (plan.key_off[sq] * H_kv + kv) * (int64_t)D;
@@ -167,109 +162,144 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     int tt = wave;
     if (tt < n_tiles) load_wave_tile<D>(wt, kseq, vseq, row_stride, kbeg + tt * kTile, kend, lane);
 
-    // Q^T operand: column = query head, k-group g4 = 8 dims per k-step.
-    bf16x8 qf[KSTEPS];
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s)
-        qf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q + (((int64_t)b * T_q + tq) * H_q + hq) * D +
-                                                            s * 32 + g4 * 8));
+    for (int h = 0; h < NH; ++h) {
+        const int f = (hg * NH + h) * kCols + col;
+        // columns past the end read a valid row's Q; their outputs are never written
+        const int fc = min(f, ncols - 1);
+        const int tq = fc / G;
+        const int hq = kv * G + fc % G;
+        vis_end[h] = min(kend, len - T_q + tq + 1);
+        // Q^T operand: column = query row, k-group g4 = 8 dims per k-step.
+        const uint16_t* qrow = q + (((int64_t)b * T_q + tq) * H_q + hq) * D + g4 * 8;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s)
+            qf[h][s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + s * 32));
+    }
+    const int mask_from = min(kend, len - T_q + 1);   // keys before this are visible to all
     uint16_t* vt = vtiles + wave * SM::VT_ELEMS;
     // transposed-read source address: lane L of group g4 points at key row
     // g4 + 4 (L / 4) (+ 16 for the second read), dims 4 (L % 4) of each 16-dim block
     const uint16_t* vrd = vt + (g4 + 4 * ((lane & 15) >> 2)) * SM::VS + 4 * (lane & 3);
 
-    f32x4 oacc[DBLK];
+    f32x4 oacc[NH][DBLK];
+    float m_run[NH], l_run[NH];
 #pragma unroll
-    for (int i = 0; i < DBLK; ++i) oacc[i] = f32x4{};
-    float m_run = -INFINITY, l_run = 0.f;
+    for (int h = 0; h < NH; ++h) {
+#pragma unroll
+        for (int i = 0; i < DBLK; ++i) oacc[h][i] = f32x4{};
+        m_run[h] = -INFINITY;
+        l_run[h] = 0.f;
+    }
 
     for (; tt < n_tiles; tt += kWaves) {
         const int key0 = kbeg + tt * kTile;
-        // S^T for two 16-key blocks; element i of s[blk] is key key0 + g4 + 16 blk + 4 i
-        f32x4 s[2];
+        // S^T for two 16-key blocks; element i of s[h][blk] is key key0 + g4 + 16 blk + 4 i
+        f32x4 s[NH][2];
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            s[blk] = f32x4{};
+        for (int h = 0; h < NH; ++h)
 #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks)
-                s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, wt.kf[blk][ks]), qf[ks], s[blk], 0, 0, 0);
-        }
+            for (int blk = 0; blk < 2; ++blk) {
+                s[h][blk] = f32x4{};
+#pragma unroll
+                for (int ks = 0; ks < KSTEPS; ++ks)
+                    s[h][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, wt.kf[blk][ks]), qf[h][ks], s[h][blk], 0, 0, 0);
+            }
         wave_lds_fence();                    // previous tile's V reads are done
         store_v<D>(wt, vt, lane);
         const int nt = tt + kWaves;
         if (nt < n_tiles) load_wave_tile<D>(wt, kseq, vseq, row_stride, kbeg + nt * kTile, kend, lane);
         if (key0 + kTile > mask_from) {
 #pragma unroll
+            for (int h = 0; h < NH; ++h)
+#pragma unroll
+                for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (key0 + g4 + 16 * blk + 4 * i >= vis_end[h]) s[h][blk][i] = -INFINITY;
+        }
+        float corr[NH];
+        bf16x8 pb[NH];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            float mt = fmaxf(fmaxf(fmaxf(s[h][0][0], s[h][0][1]), fmaxf(s[h][0][2], s[h][0][3])),
+                             fmaxf(fmaxf(s[h][1][0], s[h][1][1]), fmaxf(s[h][1][2], s[h][1][3])));
+            mt = fmaxf(mt, xor16(mt));
+            mt = fmaxf(mt, xor32(mt));
+            const float m_new = fmaxf(m_run[h], mt);
+            const float mc = (m_new == -INFINITY) ? 0.f : m_new * c;
+            corr[h] = fast_exp2(m_run[h] * c - mc);
+            float p[8];
+#pragma unroll
             for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (key0 + g4 + 16 * blk + 4 * i >= vis_end) s[blk][i] = -INFINITY;
+                    p[blk * 4 + i] = fast_exp2(__builtin_fmaf(s[h][blk][i], c, -mc));
+            l_run[h] = l_run[h] * corr[h] +
+                       (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+            m_run[h] = m_new;
+            u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                        pack_bf16x2(p[6], p[7])};
+            pb[h] = __builtin_bit_cast(bf16x8, pw);
         }
-        float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-        mt = fmaxf(mt, xor16(mt));
-        mt = fmaxf(mt, xor32(mt));
-        const float m_new = fmaxf(m_run, mt);
-        const float mc = (m_new == -INFINITY) ? 0.f : m_new * c;
-        const float corr = fast_exp2(m_run * c - mc);
-        float p[8];
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) p[blk * 4 + i] = fast_exp2(__builtin_fmaf(s[blk][i], c, -mc));
-        l_run = l_run * corr + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
-        m_run = m_new;
-        u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                    pack_bf16x2(p[6], p[7])};
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
         wave_lds_fence();                    // V of this tile is visible to the wave
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) {
-            oacc[db] *= corr;
             const s16x4 lo = lds_read_tr16(vrd + db * 16);
             const s16x4 hi = lds_read_tr16(vrd + 16 * SM::VS + db * 16);
             const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a8), pb,
-                                                               oacc[db], 0, 0, 0);
+#pragma unroll
+            for (int h = 0; h < NH; ++h) {
+                oacc[h][db] *= corr[h];
+                oacc[h][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, a8), pb[h], oacc[h][db], 0, 0, 0);
+            }
         }
     }
 
-    // ---- merge the four wave partials through LDS ----
-    l_run += xor16(l_run);
-    l_run += xor32(l_run);
-    float* mw_o = mrg + wave * WSTRIDE;
-#pragma unroll
-    for (int db = 0; db < DBLK; ++db) *(f32x4*)(mw_o + col * D + db * 16 + g4 * 4) = oacc[db];
-    if (g4 == 0) {
-        mw_o[kCols * D + col] = m_run;
-        mw_o[kCols * D + kCols + col] = l_run;
-    }
-    __syncthreads();
+    // ---- merge the four wave partials through LDS, one column block at a time ----
     const int64_t pidx = (int64_t)plan.split_base + unit;
-    for (int e = tid; e < kCols * (D / 4); e += kThreads) {
-        const int cc = e / (D / 4), x = (e % (D / 4)) * 4;
-        const int fo = hg * kCols + cc;
-        if (fo >= T_q * G) continue;
-        float mx = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, mrg[w * WSTRIDE + kCols * D + cc]);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        float lsum = 0.f;
+    for (int h = 0; h < NH; ++h) {
+        const int fbase = (hg * NH + h) * kCols;
+        if (fbase >= ncols) break;           // work-group uniform
+        if (h > 0) __syncthreads();          // the previous block's merge reads are done
+        float lr = l_run[h];
+        lr += xor16(lr);
+        lr += xor32(lr);
+        float* mw_o = mrg + wave * WSTRIDE;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float* base = mrg + w * WSTRIDE;
-            const float mwv = base[kCols * D + cc];
-            const float sc = (mwv == -INFINITY) ? 0.f : fast_exp2((mwv - mx) * c);
-            acc += sc * *(const f32x4*)(base + cc * D + x);
-            lsum += sc * base[kCols * D + kCols + cc];
+        for (int db = 0; db < DBLK; ++db) *(f32x4*)(mw_o + col * D + db * 16 + g4 * 4) = oacc[h][db];
+        if (g4 == 0) {
+            mw_o[kCols * D + col] = m_run[h];
+            mw_o[kCols * D + kCols + col] = lr;
         }
-        // partial row: (split, new token, query head)
-        const int64_t hrow = (pidx * T_q + fo / G) * H_q + (int64_t)kv * G + fo % G;
-        *(f32x4*)(ws_o + hrow * D + x) = acc;
-        if (x == 0) {
-            ws_m[hrow] = mx * c;             // base-2 units
-            ws_l[hrow] = lsum;
+        __syncthreads();
+        for (int e = tid; e < kCols * (D / 4); e += kThreads) {
+            const int cc = e / (D / 4), x = (e % (D / 4)) * 4;
+            const int fo = fbase + cc;
+            if (fo >= ncols) continue;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, mrg[w * WSTRIDE + kCols * D + cc]);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            float lsum = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float* base = mrg + w * WSTRIDE;
+                const float mwv = base[kCols * D + cc];
+                const float sc = (mwv == -INFINITY) ? 0.f : fast_exp2((mwv - mx) * c);
+                acc += sc * *(const f32x4*)(base + cc * D + x);
+                lsum += sc * base[kCols * D + kCols + cc];
+            }
+            // partial row: (split, new token, query head)
+            const int64_t hrow = (pidx * T_q + fo / G) * H_q + (int64_t)kv * G + fo % G;
+            *(f32x4*)(ws_o + hrow * D + x) = acc;
+            if (x == 0) {
+                ws_m[hrow] = mx * c;             // base-2 units
+                ws_l[hrow] = lsum;
+            }
         }
     }
 }
@@ -350,23 +380,38 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
 
 }  // namespace
 
+int decode_column_blocks_per_group(int T_q, int G) { return T_q * G > kCols ? 2 : 1; }
+
+int decode_column_groups(int T_q, int G) {
+    const int blocks = (T_q * G + kCols - 1) / kCols;
+    const int nh = decode_column_blocks_per_group(T_q, G);
+    return (blocks + nh - 1) / nh;
+}
+
+template <int D, int NH>
+static void launch_split(dim3 grid, const void* q, const void* k, const void* v,
+                         const DecodeWorkspace& ws, const DecodePlanChunk& plan, int T_q, int H_q,
+                         int H_kv, int G, int n_hg, float c, hipStream_t stream) {
+    hipLaunchKernelGGL((decode_split_kernel<D, NH>), grid, dim3(kThreads), 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, ws.m, ws.l,
+                       ws.o, plan, T_q, H_q, H_kv, G, n_hg, c);
+}
+
 hipError_t launch_decode_split_bf16(const void* q, const void* k, const void* v,
                                     const DecodeWorkspace& ws, const DecodePlanChunk& plan,
                                     int T_q, int H_q, int H_kv, int d, float scale,
                                     hipStream_t stream) {
     const int G = H_q / H_kv;
-    const int n_hg = (T_q * G + kCols - 1) / kCols;
+    const int n_hg = decode_column_groups(T_q, G);
+    const int nh = decode_column_blocks_per_group(T_q, G);
     const int64_t grid = (int64_t)plan.units * n_hg * H_kv;
     if (grid < 1 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     const float c = scale * kLog2e;
-    if (d == 128)
-        hipLaunchKernelGGL((decode_split_kernel<128>), dim3((unsigned)grid), dim3(kThreads), 0,
-                           stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                           ws.m, ws.l, ws.o, plan, T_q, H_q, H_kv, G, n_hg, c);
-    else
-        hipLaunchKernelGGL((decode_split_kernel<64>), dim3((unsigned)grid), dim3(kThreads), 0,
-                           stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                           ws.m, ws.l, ws.o, plan, T_q, H_q, H_kv, G, n_hg, c);
+    const dim3 g((unsigned)grid);
+    if (d == 128 && nh == 1) launch_split<128, 1>(g, q, k, v, ws, plan, T_q, H_q, H_kv, G, n_hg, c, stream);
+    else if (d == 128) launch_split<128, 2>(g, q, k, v, ws, plan, T_q, H_q, H_kv, G, n_hg, c, stream);
+    else if (nh == 1) launch_split<64, 1>(g, q, k, v, ws, plan, T_q, H_q, H_kv, G, n_hg, c, stream);
+    else launch_split<64, 2>(g, q, k, v, ws, plan, T_q, H_q, H_kv, G, n_hg, c, stream);
     return hipGetLastError();
 }
 

@@ -42,6 +42,10 @@ struct DecodeWorkspace {
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 
+// Work-groups per (split, KV head) that the split kernel uses for T_q * G
+// query rows (each covers up to 32 rows).
+int decode_column_groups(int T_q, int G);
+
 // T_q new tokens per sequence (1 for plain decode); partial and output rows are
 // (sequence, token, query head).
 hipError_t launch_decode_split_bf16(const void* q, const void* k, const void* v,
