@@ -187,6 +187,34 @@ def bench_prefill(name, steps, warmup):
     return dict(inp=inp, ms=ms, flops=flops, rows=rows, o_rows=o_rows, lse_rows=lse_rows)
 
 
+def bench_prefill_kvsplit(name, steps):
+    """KV-parallel prefill (key ranges on separate work-groups + combine)
+    beside the plain prefill kernel on the same chunk."""
+    import torch
+    import gqa_attention_flashattention_amd as gq
+    from gqa_attention_flashattention_amd import inputs as gin
+    inp = gin.make(name)
+    w = inp.workload
+    q, k, v = (dev_tensor(x) for x in (inp.q_store, inp.k_store, inp.v_store))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    split = lambda: gq.prefill_kvsplit(q, k, v, causal=w.causal, q_offset=w.q_offset, out=o,
+                                       lse=lse)
+    plain = lambda: gq.prefill(q, k, v, causal=w.causal, q_offset=w.q_offset, out=o, lse=lse)
+    res = {}
+    for tag, fn in (("plain", plain), ("kvsplit", split)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        res[tag] = time_graph([fn] * steps)
+    o_split = o.float().cpu().numpy()    # the kvsplit result (timed last)
+    ns = gq.prefill_kvsplit_count(w.B, w.T_q, w.S_kv, w.H_q, w.H_kv, w.d, causal=w.causal,
+                                  q_offset=w.q_offset)
+    return dict(inp=inp, ms=res["kvsplit"], ms_plain=res["plain"], n_split=ns,
+                flops=prefill_algorithmic_flops(w), o_gpu=o_split,
+                lse_gpu=lse.cpu().numpy())
+
+
 def copy_calibration(mib: int):
     """A plain device-to-device copy of `mib` MiB, three times (rocprofv3
     counter runs scale FETCH_SIZE / WRITE_SIZE by what this copy reads)."""
@@ -273,6 +301,20 @@ def parity_decode_multi(mul, n_seq=2):
             "decode_multi_sample_max_abs_dLSE": float(max(errs_l))}
 
 
+def parity_prefill_kvsplit(kvs, n_rows=64):
+    import oracle
+    inp = kvs["inp"]
+    w = inp.workload
+    rng = np.random.default_rng(0)
+    total = w.B * w.T_q * w.H_q
+    rows = np.unique(np.concatenate([[0, total - 1], rng.integers(0, total, n_rows - 2)]))
+    o, l = oracle.prefill(inp.q, inp.k, inp.v, causal=w.causal, q_offset=w.q_offset, rows=rows)
+    og = kvs["o_gpu"].reshape(-1, w.d)[rows].astype(np.float64)
+    lg = kvs["lse_gpu"].reshape(-1)[rows].astype(np.float64)
+    return {"prefill_kvsplit_sample_max_abs_dO": float(np.abs(og - o).max()),
+            "prefill_kvsplit_sample_max_abs_dLSE": float(np.abs(lg - l).max())}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -281,10 +323,13 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--decode-workload", default="decode_8k")
     ap.add_argument("--prefill-workload", default="prefill_8k_causal")
+    ap.add_argument("--kvsplit-workload", default="prefill_chunk_256_64k",
+                    help="KV-parallel prefill workload (reported under prefill_kvsplit)")
     ap.add_argument("--multi-workload", default="decode_t4_varlen_b16",
                     help="multi-token decode workload (reported under decode_multi)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["decode", "prefill", "decode_multi"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "decode_multi", "prefill_kvsplit"],
+                    default=None,
                     help="run one path only (profiling runs); prints a partial line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (counter calibration)")
@@ -308,6 +353,11 @@ def main():
         log(f"[bench] decode_multi {mul['ms'] * 1e3:.2f} us/call "
             f"{mul['kv_bytes'] / (mul['ms'] * 1e-3) / 1e9:.1f} GB/s")
         return
+    if args.only == "prefill_kvsplit":
+        kvs = bench_prefill_kvsplit(args.kvsplit_workload, args.prefill_steps)
+        log(f"[bench] prefill_kvsplit {kvs['ms'] * 1e3:.1f} us/call (plain "
+            f"{kvs['ms_plain'] * 1e3:.1f} us), {kvs['n_split']} ranges")
+        return
     if args.only == "prefill":
         pre = bench_prefill(args.prefill_workload, args.prefill_steps, 2)
         log(f"[bench] prefill {pre['ms']:.3f} ms/call "
@@ -327,6 +377,10 @@ def main():
     log(f"[bench] decode_multi {args.multi_workload}")
     mul = bench_decode_multi(args.multi_workload, min(args.steps, 200), args.warmup)
     log(f"[bench] decode_multi {mul['ms'] * 1e3:.2f} us/call")
+
+    log(f"[bench] prefill_kvsplit {args.kvsplit_workload}")
+    kvs = bench_prefill_kvsplit(args.kvsplit_workload, args.prefill_steps)
+    log(f"[bench] prefill_kvsplit {kvs['ms'] * 1e3:.1f} us/call (plain {kvs['ms_plain'] * 1e3:.1f} us)")
 
     dw = dec["inp"].workload
     gbs = dec["kv_bytes"] / (dec["ms_call"] * 1e-3) / 1e9
@@ -381,6 +435,20 @@ def main():
                      "algorithmic_bytes_per_call": mul["kv_bytes"],
                      "note": "whole call (split + combine kernels)"},
     }
+    kw = kvs["inp"].workload
+    tf_split = kvs["flops"] / (kvs["ms"] * 1e-3) / 1e12
+    result["prefill_kvsplit"] = {
+        "workload": kw.name, "T_q": kw.T_q, "S_kv": kw.S_kv, "q_offset": kw.q_offset,
+        "causal": kw.causal, "key_ranges": kvs["n_split"], "ms_per_call": kvs["ms"],
+        "value": round(tf_split, 2), "unit": "TFLOP/s",
+        "plain_prefill_ms_per_call": kvs["ms_plain"],
+        "plain_prefill_TFLOPs": round(kvs["flops"] / (kvs["ms_plain"] * 1e-3) / 1e12, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tf_split, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf_split / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "algorithmic_flops_per_call": kvs["flops"],
+                     "note": "whole call (split prefill + combine kernels)"},
+    }
     if not args.no_cpu:
         log("[bench] cpu oracle baseline (decode)")
         cb, o_ref, lse_ref = cpu_baseline_decode(dec["inp"], dec["kv_bytes"])
@@ -392,6 +460,8 @@ def main():
         result["prefill"]["cpu_baseline"] = cbp
         result["parity"]["prefill_sample_max_abs_dO"] = float(np.abs(pre["o_rows"] - op).max())
         result["parity"]["prefill_sample_max_abs_dLSE"] = float(np.abs(pre["lse_rows"] - lp).max())
+        log("[bench] oracle check (prefill_kvsplit sample)")
+        result["parity"].update(parity_prefill_kvsplit(kvs))
         log("[bench] oracle check (decode_multi sample)")
         result["parity"].update(parity_decode_multi(mul))
     print(json.dumps(result), flush=True)

@@ -57,6 +57,11 @@ def load_library():
     lib.gqa_attn_decode_plan.argtypes = [i, i, i, i, vp, i, vp, vp, vp, vp, vp]
     lib.gqa_attn_decode_split.restype = i
     lib.gqa_attn_decode_split.argtypes = [vp, vp, vp, vp, sz, i, i, i, i, vp, f, i, i, vp]
+    lib.gqa_attn_prefill_kvsplit.restype = i
+    lib.gqa_attn_prefill_kvsplit.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, i,
+                                             vp]
+    lib.gqa_attn_prefill_kvsplit_count.restype = i
+    lib.gqa_attn_prefill_kvsplit_count.argtypes = [i] * 9
     lib.gqa_attn_decode_multi.restype = i
     lib.gqa_attn_decode_multi.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, f, i, i, vp]
     lib.gqa_attn_decode_combine.restype = i
@@ -142,6 +147,49 @@ def prefill(q, k, v, *, causal: bool, q_offset: int = 0, scale: float | None = N
                                          int(q_offset), _dtype_code(q), _stream(q.device))
     _check(rc, "gqa_attn_prefill")
     return out, lse
+
+
+def prefill_kvsplit(q, k, v, *, causal: bool, q_offset: int = 0, scale: float | None = None,
+                    num_splits: int = 0, out=None, lse=None, return_lse: bool = True):
+    """KV-parallel prefill: as prefill (bf16), with each row block's key tiles
+    cut into ranges on separate work-groups and merged by log-sum-exp."""
+    import torch
+    _require(q, "q", 4)
+    _require(k, "k", 4)
+    _require(v, "v", 4)
+    B, T_q, H_q, d = q.shape
+    S_kv, H_kv = k.shape[1], k.shape[2]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        raise GQAError("k and v must be [B, S_kv, H_kv, d] matching q", 2)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise GQAError("q, k, v must share one dtype", 3)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require(out, "out", 4)
+    if lse is None and return_lse:
+        lse = torch.empty((B, T_q, H_q), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _require(lse, "lse", 3)
+    rc = load_library().gqa_attn_prefill_kvsplit(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, T_q, S_kv, H_q, H_kv, d,
+        float(scale), int(bool(causal)), int(q_offset), int(num_splits), _dtype_code(q),
+        _stream(q.device))
+    _check(rc, "gqa_attn_prefill_kvsplit")
+    return out, lse
+
+
+def prefill_kvsplit_count(B: int, T_q: int, S_kv: int, H_q: int, H_kv: int, d: int, *,
+                          causal: bool, q_offset: int = 0, num_splits: int = 0) -> int:
+    """Host-only: the key-range count prefill_kvsplit uses."""
+    n = load_library().gqa_attn_prefill_kvsplit_count(B, T_q, S_kv, H_q, H_kv, d,
+                                                      int(bool(causal)), int(q_offset),
+                                                      int(num_splits))
+    if n < 1:
+        _check(-n, "gqa_attn_prefill_kvsplit_count")
+    return n
 
 
 def decode_plan(B: int, H_q: int, H_kv: int, d: int, kv_len, num_splits: int = 0) -> dict:

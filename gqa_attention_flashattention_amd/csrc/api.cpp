@@ -23,6 +23,9 @@ constexpr int kMinSplitLen = 128;
 constexpr int kMaxSplitLen = 8192;
 constexpr int kSplitAlign = 64;
 constexpr int kMaxDecodeTokens = 256;   // new tokens per sequence in gqa_attn_decode_multi
+constexpr int kMaxPrefillSplits = 64;
+constexpr int kMinPrefillSplitTiles = 4;          // 64-key tiles per split, at least
+constexpr size_t kMaxPrefillWorkspace = (size_t)4 << 30;
 
 bool finite_positive(float x) { return isfinite(x) && x > 0.f; }
 
@@ -201,6 +204,50 @@ int get_workspace(size_t bytes, void** out) {
     return GQA_OK;
 }
 
+int device_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+        return 256;
+    return n;
+}
+
+int check_prefill_args(const void* q, const void* k, const void* v, const void* o, int B,
+                       int T_q, int S_kv, int H_q, int H_kv, int d, float scale, int causal,
+                       int q_offset) {
+    if (!q || !k || !v || !o) return GQA_ERR_NULL;
+    if (B < 1 || T_q < 1 || S_kv < 1) return GQA_ERR_SHAPE;
+    int rc = check_heads(H_q, H_kv, d);
+    if (rc) return rc;
+    if (!finite_positive(scale)) return GQA_ERR_RANGE;
+    if (causal && (q_offset < 0 || (int64_t)q_offset + T_q > S_kv)) return GQA_ERR_RANGE;
+    if ((int64_t)T_q * (H_q / H_kv) > 0x7fffffff - 256) return GQA_ERR_SHAPE;
+    return GQA_OK;
+}
+
+// Key splits per row block for the KV-parallel prefill (see gqa_attn_prefill_kvsplit).
+int prefill_splits(int B, int T_q, int S_kv, int H_q, int H_kv, int d, int causal, int q_offset,
+                   int num_splits) {
+    const int64_t blocks = gqa::prefill_row_blocks(T_q, H_q / H_kv) * B * H_kv;
+    // the longest row block sees keys up to its last query
+    const int64_t keys = causal ? (int64_t)q_offset + T_q : S_kv;
+    const int64_t tiles = (keys + 63) / 64;
+    int64_t ns;
+    if (num_splits > 0) {
+        ns = num_splits;
+    } else {
+        const int64_t target = 2 * (int64_t)device_cus();
+        ns = blocks >= target ? 1 : (target + blocks - 1) / blocks;
+        const int64_t by_len = tiles / kMinPrefillSplitTiles;
+        if (ns > by_len) ns = by_len;
+    }
+    if (ns > tiles) ns = tiles;
+    if (ns > kMaxPrefillSplits) ns = kMaxPrefillSplits;
+    const size_t row_bytes = (size_t)B * T_q * H_q * (size_t)(d + 2) * sizeof(float);
+    while (ns > 1 && row_bytes * (size_t)ns > kMaxPrefillWorkspace) --ns;
+    return ns < 1 ? 1 : (int)ns;
+}
+
 }  // namespace
 
 extern "C" {
@@ -222,14 +269,9 @@ int gqa_attn_version(void) { return 100; }
 int gqa_attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                      int T_q, int S_kv, int H_q, int H_kv, int d, float scale, int causal,
                      int q_offset, int dtype, void* stream) {
-    if (!q || !k || !v || !o) return GQA_ERR_NULL;
-    if (B < 1 || T_q < 1 || S_kv < 1) return GQA_ERR_SHAPE;
-    int rc = check_heads(H_q, H_kv, d);
+    int rc = check_prefill_args(q, k, v, o, B, T_q, S_kv, H_q, H_kv, d, scale, causal, q_offset);
     if (rc) return rc;
     if (dtype != GQA_BF16 && dtype != GQA_F32) return GQA_ERR_UNSUPPORTED;
-    if (!finite_positive(scale)) return GQA_ERR_RANGE;
-    if (causal && (q_offset < 0 || (int64_t)q_offset + T_q > S_kv)) return GQA_ERR_RANGE;
-    if ((int64_t)T_q * (H_q / H_kv) > 0x7fffffff - 256) return GQA_ERR_SHAPE;
     gqa::PrefillArgs a{q, k, v, o, lse, B, T_q, S_kv, H_q, H_kv, d, scale, causal ? 1 : 0,
                        causal ? q_offset : 0};
     (void)hipGetLastError();
@@ -317,6 +359,49 @@ int gqa_attn_decode(const void* q, const void* k, const void* v, void* o, int B,
     return for_each_chunk(B, kv_len, hp.splits, hp.lens, [&](const DecodePlanChunk& c) {
         return gqa::launch_decode_combine_bf16(ws, c, o, nullptr, 1, H_q, d, (hipStream_t)stream);
     });
+}
+
+int gqa_attn_prefill_kvsplit(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int T_q, int S_kv, int H_q, int H_kv, int d, float scale,
+                             int causal, int q_offset, int num_splits, int dtype, void* stream) {
+    int rc = check_prefill_args(q, k, v, o, B, T_q, S_kv, H_q, H_kv, d, scale, causal, q_offset);
+    if (rc) return rc;
+    if (dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+    if (!causal) q_offset = 0;
+    gqa::PrefillArgs a{q, k, v, o, lse, B, T_q, S_kv, H_q, H_kv, d, scale, causal ? 1 : 0,
+                       q_offset};
+    const int ns = prefill_splits(B, T_q, S_kv, H_q, H_kv, d, causal, q_offset, num_splits);
+    (void)hipGetLastError();
+    if (ns == 1)
+        return gqa::launch_prefill_bf16(a, (hipStream_t)stream) == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+    const int64_t total = (int64_t)B * ns;               // partials per (t, h)
+    const int rows = T_q * H_q;
+    void* base = nullptr;
+    rc = get_workspace(workspace_bytes_for(total, rows, d), &base);
+    if (rc) return rc;
+    DecodeWorkspace ws = carve(base, total, rows);
+    if (gqa::launch_prefill_split_bf16(a, ns, ws, (hipStream_t)stream) != hipSuccess)
+        return GQA_ERR_HIP;
+    for (int b0 = 0; b0 < B; b0 += gqa::kDecodeSeqPerLaunch) {
+        DecodePlanChunk c;
+        memset(&c, 0, sizeof(c));
+        c.nseq = B - b0 < gqa::kDecodeSeqPerLaunch ? B - b0 : gqa::kDecodeSeqPerLaunch;
+        c.seq0 = b0;
+        c.split_base = b0 * ns;
+        for (int i = 0; i <= c.nseq; ++i) c.unit_base[i] = i * ns;
+        c.units = c.nseq * ns;
+        if (gqa::launch_decode_combine_bf16(ws, c, o, lse, T_q, H_q, d, (hipStream_t)stream) !=
+            hipSuccess)
+            return GQA_ERR_HIP;
+    }
+    return GQA_OK;
+}
+
+int gqa_attn_prefill_kvsplit_count(int B, int T_q, int S_kv, int H_q, int H_kv, int d, int causal,
+                                   int q_offset, int num_splits) {
+    if (B < 1 || T_q < 1 || S_kv < 1 || check_heads(H_q, H_kv, d)) return -GQA_ERR_SHAPE;
+    if (causal && (q_offset < 0 || (int64_t)q_offset + T_q > S_kv)) return -GQA_ERR_RANGE;
+    return prefill_splits(B, T_q, S_kv, H_q, H_kv, d, causal, causal ? q_offset : 0, num_splits);
 }
 
 int gqa_attn_decode_multi(const void* q, const void* k, const void* v, void* o, float* lse,

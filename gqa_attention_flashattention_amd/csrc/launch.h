@@ -39,8 +39,20 @@ struct DecodeWorkspace {
     float* o;   // [total_splits][H_q][d]
 };
 
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
+
+// Row blocks (work-groups per batch entry and KV head) of the bf16 prefill
+// kernel for T_q * G query rows.
+int64_t prefill_row_blocks(int T_q, int G);
+
+// KV-split prefill, step 1: partials of n_split key ranges per row block into
+// ws (partial row ((b * n_split + split) * T_q + t) * H_q + h); step 2 is
+// launch_decode_combine_bf16 with a chunk whose sequence sq owns splits
+// sq * n_split .. sq * n_split + n_split - 1.
+hipError_t launch_prefill_split_bf16(const PrefillArgs& a, int n_split, const DecodeWorkspace& ws,
+                                     hipStream_t stream);
 
 // Work-groups per (split, KV head) that the split kernel uses for T_q * G
 // query rows (each covers up to 32 rows).

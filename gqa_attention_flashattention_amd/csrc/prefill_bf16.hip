@@ -131,11 +131,17 @@ struct LaneOffsets {
     int v[2][D / 32];         // V^T tr16 read offset per (half t, 32-dim block), key step 0
 };
 
-template <int D, bool CAUSAL>
+// SPLIT: the key tiles a row block sees are cut into n_split contiguous
+// ranges, one work-group each, and every work-group writes the unnormalised
+// partial (m in base-2 units, l, O) of its rows to the workspace instead of
+// O and LSE (partial row ((b * n_split + split) * T_q + t) * H_q + h); the
+// decode combine kernel merges them.
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int B,
-    int T_q, int S_kv, int H_q, int H_kv, int G, float c, int q_offset, int n_mblk) {
+    int T_q, int S_kv, int H_q, int H_kv, int G, float c, int q_offset, int n_mblk,
+    int n_split, float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o) {
     using T = Tile<D>;
     constexpr int KSTEPS = D / 16;   // MFMA k-steps over the head dim
     constexpr int DBLK = D / 32;     // 32-row blocks of O^T
@@ -157,6 +163,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     int bid = blockIdx.x;
     const int kv = bid % H_kv;
     bid /= H_kv;
+    int split = 0;
+    if (SPLIT) {
+        split = bid % n_split;
+        bid /= n_split;
+    }
     const int b = bid % B;
     int mb = bid / B;
     if (CAUSAL) mb = n_mblk - 1 - mb;
@@ -178,7 +189,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     // branches on them are scalar branches)
     const int t_hi = min(T_q - 1, (r0 + kBlockM - 1) / G);
     const int kend = CAUSAL ? min(S_kv, q_offset + t_hi + 1) : S_kv;
-    const int n_tiles = __builtin_amdgcn_readfirstlane((kend + kBlockN - 1) / kBlockN);
+    const int wg_tiles = (kend + kBlockN - 1) / kBlockN;
+    // this work-group's tiles: [j_lo, j_lo + n_tiles)
+    int j_lo = 0, n_tiles = wg_tiles;
+    if (SPLIT) {
+        const int per = (wg_tiles + n_split - 1) / n_split;
+        j_lo = min(wg_tiles, split * per);
+        n_tiles = min(wg_tiles - j_lo, per);
+    }
+    j_lo = __builtin_amdgcn_readfirstlane(j_lo);
+    n_tiles = __builtin_amdgcn_readfirstlane(n_tiles);
     const bool wave_live = rw0 < rows_total;
     const int wt_lo = rw0 / G;
     const int wt_hi = min(T_q - 1, (rw0 + kRowsPerWave - 1) / G);
@@ -194,9 +214,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const uint16_t* kbase = k + ((int64_t)b * S_kv * H_kv + kv) * D;
     const uint16_t* vbase = v + ((int64_t)b * S_kv * H_kv + kv) * D;
 
-    // tiles 0 and 1 start loading before anything else
-    issue_tile<D>(ks0, vs0, kbase, vbase, row_stride, 0, S_kv, wave, lane);
-    if (n_tiles > 1) issue_tile<D>(ks1, vs1, kbase, vbase, row_stride, 1, S_kv, wave, lane);
+    // the first two tiles start loading before anything else
+    if (n_tiles > 0) issue_tile<D>(ks0, vs0, kbase, vbase, row_stride, j_lo, S_kv, wave, lane);
+    if (n_tiles > 1) issue_tile<D>(ks1, vs1, kbase, vbase, row_stride, j_lo + 1, S_kv, wave, lane);
 
     // Q^T operand, resident for the whole key sweep.
     bf16x8 qf[KSTEPS];
@@ -231,12 +251,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     float m_run = -INFINITY;   // reference max (raw score units) used by P
     float l_run = 0.f;
 
-    // One key tile: tile j sits in stage buffers (kt, vt); first tile j + 2 is
-    // issued into (kn, vn), the stage that tile j - 1 used.
+    // One key tile: the work-group's tile j (global tile j_lo + j) sits in
+    // stage buffers (kt, vt); first tile j + 2 is issued into (kn, vn), the
+    // stage that tile j - 1 used.
     auto step = [&](int j, const uint16_t* kt, const uint16_t* vt, uint16_t* kn, uint16_t* vn) {
         const bool issue = j + 2 < n_tiles;
-        if (issue) issue_tile<D>(kn, vn, kbase, vbase, row_stride, j + 2, S_kv, wave, lane);
-        const int key0 = j * kBlockN;
+        if (issue) issue_tile<D>(kn, vn, kbase, vbase, row_stride, j_lo + j + 2, S_kv, wave, lane);
+        const int key0 = (j_lo + j) * kBlockN;
         if (key0 < wave_kend) {
             // ---- S^T = K Q^T (two 32-key blocks) ----
             f32x16 s[2];
@@ -280,7 +301,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
                     for (int i = 0; i < 16; ++i) oacc[db][i] *= corr;
                 m_run = m_new;
             }
-            const float mc = m_run * c;
+            // a split can start past a row's last key: its m stays -inf, P = 0
+            const float mc = (SPLIT && m_run == -INFINITY) ? 0.f : m_run * c;
             float psum = 0.f;
             uint32_t pk[2][8];
 #pragma unroll
@@ -319,6 +341,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     if (n_tiles > 1) wait_vmcnt<LOADS_PER_TILE>();
     else wait_vmcnt<0>();
     lds_barrier();
+    // (n_tiles == 0 only for an empty split: the loop below does nothing)
     for (int j = 0; j < n_tiles; j += kStages) {
         step(j, ks0, vs0, ks2, vs2);
         if (j + 1 < n_tiles) step(j + 1, ks1, vs1, ks0, vs0);
@@ -330,6 +353,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run),
                                                    false, false);
         l_run = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    if (SPLIT) {
+        if (valid) {
+            const int64_t hrow = (((int64_t)b * n_split + split) * T_q + t) * H_q +
+                                 (int64_t)kv * G + g;
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    *(f32x4*)(ws_o + hrow * D + db * 32 + u * 8 + hh * 4) =
+                        f32x4{oacc[db][4 * u], oacc[db][4 * u + 1], oacc[db][4 * u + 2],
+                              oacc[db][4 * u + 3]};
+            if (hh == 0) {
+                ws_m[hrow] = m_run * c;      // base-2 units (-inf: no visible key here)
+                ws_l[hrow] = l_run;
+            }
+        }
+        return;
     }
     if (valid) {
         const float inv = 1.f / l_run;
@@ -348,23 +389,38 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 
 }  // namespace
 
-template <int D, bool CAUSAL>
-static hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
-    const int rows_total = a.T_q * (a.H_q / a.H_kv);
-    const int n_mblk = (rows_total + kBlockM - 1) / kBlockM;
-    const int64_t grid = (int64_t)n_mblk * a.B * a.H_kv;
-    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+template <int D, bool CAUSAL, bool SPLIT>
+static hipError_t launch_one(const PrefillArgs& a, int n_split, const DecodeWorkspace* ws,
+                             hipStream_t stream) {
+    const int64_t n_mblk = prefill_row_blocks(a.T_q, a.H_q / a.H_kv);
+    const int64_t grid = n_mblk * a.B * a.H_kv * (SPLIT ? n_split : 1);
+    if (grid < 1 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     const float c = a.scale * kLog2e;
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,
-                       stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (uint16_t*)a.o, a.lse, a.B, a.T_q, a.S_kv, a.H_q, a.H_kv, a.H_q / a.H_kv, c,
-                       a.q_offset, n_mblk);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, SPLIT>), dim3((unsigned)grid),
+                       dim3(kThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.T_q, a.S_kv, a.H_q,
+                       a.H_kv, a.H_q / a.H_kv, c, a.q_offset, (int)n_mblk, n_split,
+                       SPLIT ? ws->m : nullptr, SPLIT ? ws->l : nullptr, SPLIT ? ws->o : nullptr);
     return hipGetLastError();
 }
 
+int64_t prefill_row_blocks(int T_q, int G) { return ((int64_t)T_q * G + kBlockM - 1) / kBlockM; }
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
-    if (a.d == 128) return a.causal ? launch_one<128, true>(a, stream) : launch_one<128, false>(a, stream);
-    return a.causal ? launch_one<64, true>(a, stream) : launch_one<64, false>(a, stream);
+    if (a.d == 128)
+        return a.causal ? launch_one<128, true, false>(a, 1, nullptr, stream)
+                        : launch_one<128, false, false>(a, 1, nullptr, stream);
+    return a.causal ? launch_one<64, true, false>(a, 1, nullptr, stream)
+                    : launch_one<64, false, false>(a, 1, nullptr, stream);
+}
+
+hipError_t launch_prefill_split_bf16(const PrefillArgs& a, int n_split, const DecodeWorkspace& ws,
+                                     hipStream_t stream) {
+    if (a.d == 128)
+        return a.causal ? launch_one<128, true, true>(a, n_split, &ws, stream)
+                        : launch_one<128, false, true>(a, n_split, &ws, stream);
+    return a.causal ? launch_one<64, true, true>(a, n_split, &ws, stream)
+                    : launch_one<64, false, true>(a, n_split, &ws, stream);
 }
 
 }  // namespace gqa

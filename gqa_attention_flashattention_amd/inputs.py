@@ -56,6 +56,8 @@ WORKLOADS = {
         Workload("decode_128k", "decode", "bf16", B=1, H_q=64, H_kv=8, d=128, S_kv=131072),
         Workload("prefill_chunk_64k", "prefill", "bf16", B=1, H_q=64, H_kv=8, d=128,
                  T_q=2048, S_kv=67584, causal=True, q_offset=65536),
+        Workload("prefill_chunk_256_64k", "prefill", "bf16", B=1, H_q=64, H_kv=8, d=128,
+                 T_q=256, S_kv=65792, causal=True, q_offset=65536),
         Workload("decode_t4_varlen_b16", "decode", "bf16", B=16, H_q=64, H_kv=8, d=128,
                  T_q=4, kv_len_range=(1024, 32768)),
     ]

@@ -81,6 +81,33 @@ int gqa_attn_prefill(const void *q, const void *k, const void *v, void *o, float
                      int causal, int q_offset, int dtype, void *stream);
 
 /*
+ * KV-parallel prefill (ADR-0060 section 5.5, sequence-parallel prefill, on one
+ * GPU): same operation, arguments and layouts as gqa_attn_prefill (bf16 only),
+ * but the key tiles that each block of query rows sees are cut into
+ * `n` contiguous ranges processed by separate work-groups; each writes the
+ * unnormalised partial (m, l, O) of its rows and the log-sum-exp merge of
+ * section 4 (the decode combine kernel) produces O and LSE.  This raises the
+ * number of work-groups when B * H_kv * row blocks is small (short chunks over
+ * long caches).  num_splits > 0 asks for that many ranges, num_splits <= 0 lets
+ * the library choose (about two work-groups per compute unit, at least 256
+ * keys per range); n is then clamped to [1, 64], to the number of 64-key tiles
+ * and so that the partials fit in 4 GiB.  n == 1 runs gqa_attn_prefill's kernel.
+ * Uses the library-owned workspace of gqa_attn_decode (same concurrency rule),
+ * n * B * T_q * H_q * (d + 2) * 4 bytes.
+ * Errors: as gqa_attn_prefill; GQA_ERR_UNSUPPORTED for dtype != GQA_BF16.
+ */
+int gqa_attn_prefill_kvsplit(const void *q, const void *k, const void *v, void *o, float *lse,
+                             int B, int T_q, int S_kv, int H_q, int H_kv, int d, float scale,
+                             int causal, int q_offset, int num_splits, int dtype, void *stream);
+
+/*
+ * Host only: the number of key ranges n that gqa_attn_prefill_kvsplit uses for
+ * these arguments (>= 1), or minus a gqa_status code for invalid sizes.
+ */
+int gqa_attn_prefill_kvsplit_count(int B, int T_q, int S_kv, int H_q, int H_kv, int d,
+                                   int causal, int q_offset, int num_splits);
+
+/*
  * Decode, one new token per sequence (ADR-0060 sections 4, 5.2, 5.3).
  *   q   [B, H_q, d]            o [B, H_q, d]            (dtype)
  *   k,v [sum_b kv_len[b], H_kv, d], sequences packed back to back: sequence b

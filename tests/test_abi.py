@@ -24,6 +24,7 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ["gqa_attn_prefill", "gqa_attn_decode", "gqa_attn_decode_split",
               "gqa_attn_decode_combine", "gqa_attn_decode_plan", "gqa_attn_decode_multi",
+              "gqa_attn_prefill_kvsplit", "gqa_attn_prefill_kvsplit_count",
               "gqa_attn_status_string", "gqa_attn_version"]:
         assert n in names
 
@@ -99,6 +100,25 @@ def _decode_multi(kv_len, **kw):
 ])
 def test_decode_multi_rejects(kv_len, kw, code):
     assert _decode_multi(kv_len, **kw) == code
+
+
+def test_kvsplit_rejects_and_counts():
+    lib = gq.load_library()
+    # f32 is not built for the KV-parallel path; bad offset; NULL output
+    assert lib.gqa_attn_prefill_kvsplit(P, P, P, P, None, 1, 4, 8, 8, 2, 128, 0.1, 1, 4, 0, 1,
+                                        None) == 3
+    assert lib.gqa_attn_prefill_kvsplit(P, P, P, P, None, 1, 4, 8, 8, 2, 128, 0.1, 1, 5, 0, 0,
+                                        None) == 4
+    assert lib.gqa_attn_prefill_kvsplit(P, P, P, None, None, 1, 4, 8, 8, 2, 128, 0.1, 1, 4, 0, 0,
+                                        None) == 1
+    with pytest.raises(binding.GQAError):
+        gq.prefill_kvsplit_count(1, 4, 8, 8, 2, 100, causal=False)
+    # explicit counts are clamped to the key tiles and to 64
+    assert gq.prefill_kvsplit_count(1, 64, 200, 8, 2, 128, causal=False, num_splits=16) == 4
+    assert gq.prefill_kvsplit_count(1, 64, 100000, 8, 2, 128, causal=False, num_splits=500) == 64
+    # a large grid needs no split; a short chunk over a long cache gets several
+    assert gq.prefill_kvsplit_count(1, 8192, 8192, 64, 8, 128, causal=True) == 1
+    assert gq.prefill_kvsplit_count(1, 256, 65792, 64, 8, 128, causal=True, q_offset=65536) > 1
 
 
 def test_split_and_combine_reject_small_workspace():
