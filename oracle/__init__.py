@@ -44,6 +44,12 @@ class OracleLib:
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, _i64, ctypes.c_int]
+        lib.gqa_oracle_prefill_window.restype = ctypes.c_int
+        lib.gqa_oracle_prefill_window.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, _i64,
+            ctypes.c_int]
         lib.gqa_oracle_decode.restype = ctypes.c_int
         lib.gqa_oracle_decode.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -87,6 +93,35 @@ class OracleLib:
                                          int(q_offset), rp, nr, int(threads))
         if rc != 0:
             raise ValueError(f"gqa_oracle_prefill failed with code {rc}")
+        return o, lse
+
+    def prefill_window(self, q, k, v, *, q_offset: int, window: int, sink: int = 0,
+                       scale: float | None = None, rows=None, threads: int = 0):
+        """Oracle sink + local-window prefill (always causal): query t at
+        position p = q_offset + t sees key j iff j <= p and (j < sink or
+        j > p - window).  Shapes and return values as ``prefill``."""
+        q, k, v = _f32(q), _f32(k), _f32(v)
+        B, T_q, H_q, d = q.shape
+        Bk, S_kv, H_kv, dk = k.shape
+        if Bk != B or dk != d or v.shape != k.shape:
+            raise ValueError("shape mismatch")
+        if scale is None:
+            scale = 1.0 / np.sqrt(d)
+        if rows is None:
+            o = np.empty((B, T_q, H_q, d), np.float64)
+            lse = np.empty((B, T_q, H_q), np.float64)
+            rp, nr = None, 0
+        else:
+            rows = np.ascontiguousarray(rows, dtype=np.int64)
+            o = np.empty((rows.size, d), np.float64)
+            lse = np.empty((rows.size,), np.float64)
+            rp, nr = rows.ctypes.data, rows.size
+        rc = self.lib.gqa_oracle_prefill_window(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                                o.ctypes.data, lse.ctypes.data, B, T_q, S_kv,
+                                                H_q, H_kv, d, float(scale), int(q_offset),
+                                                int(window), int(sink), rp, nr, int(threads))
+        if rc != 0:
+            raise ValueError(f"gqa_oracle_prefill_window failed with code {rc}")
         return o, lse
 
     def decode(self, q, k, v, kv_len, *, scale: float | None = None, num_splits: int = 0,
@@ -164,3 +199,8 @@ def prefill(q, k, v, **kw):
 def decode(q, k, v, kv_len, **kw):
     """See OracleLib.decode."""
     return _lib().decode(q, k, v, kv_len, **kw)
+
+
+def prefill_window(q, k, v, **kw):
+    """See OracleLib.prefill_window."""
+    return _lib().prefill_window(q, k, v, **kw)

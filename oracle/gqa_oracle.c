@@ -35,6 +35,17 @@
  *   l = l_a s_a + l_b s_b, O = O_a s_a + O_b s_b, and O / l is taken once at
  *   the end.
  *
+ *   Sink + local-window mask (pccx page, "Gemma 3N E4B on pccx v002 --
+ *   Execution / Scheduling", section 4, KV cache management, hard-cap ring
+ *   buffer: once the ring wraps, the oldest entries are overwritten under an
+ *   attention-sink + local-window policy).  Reading used here: a query at
+ *   absolute position p sees key j iff j <= p and (j < sink or
+ *   j > p - window), i.e. the first `sink` positions of the sequence plus
+ *   the `window` most recent positions up to and including its own.
+ *   gqa_oracle_prefill_window computes exactly that over the logical
+ *   (unwrapped) key sequence; where a ring buffer stores the keys is the
+ *   kernel's business, not the oracle's.
+ *
  * Layouts (all row-major, contiguous):
  *   prefill  Q, O [B, T_q, H_q, d]   K, V [B, S_kv, H_kv, d]   LSE [B, T_q, H_q]
  *   decode   Q, O [B, H_q, d]        K, V packed [sum_b kv_len[b], H_kv, d],
@@ -144,6 +155,79 @@ int gqa_oracle_prefill(const float *q, const float *k, const float *v, double *o
                 const float *vb = v + ((int64_t)b * S_kv * H_kv + kv) * d;
                 double m, l;
                 partial_row(qrow, kb, vb, kstride, 0, nvis, d, scale, s, &m, &l, acc);
+                for (int x = 0; x < d; ++x) o[i * d + x] = acc[x] / l;
+                if (lse) lse[i] = m + log(l);
+            }
+        }
+        free(s);
+        free(acc);
+    }
+    return bad ? ORACLE_EARG : ORACLE_OK;
+}
+
+/* Sink + local-window prefill: like gqa_oracle_prefill with causal = 1, but
+ * query t (position p = q_offset + t) sees key j iff j <= p and
+ * (j < sink or j > p - window); window >= 1, sink >= 0.  Two-pass softmax over
+ * the visible keys, taken one by one in key order. */
+int gqa_oracle_prefill_window(const float *q, const float *k, const float *v, double *o,
+                              double *lse, int B, int T_q, int S_kv, int H_q, int H_kv, int d,
+                              double scale, int q_offset, int window, int sink,
+                              const int64_t *rows, int64_t n_rows, int nthreads) {
+    if (!q || !k || !v || !o || B < 1 || T_q < 1 || S_kv < 1 || check_heads(H_q, H_kv, d))
+        return ORACLE_EARG;
+    if (q_offset < 0 || (int64_t)q_offset + T_q > S_kv || window < 1 || sink < 0)
+        return ORACLE_EARG;
+    const int G = H_q / H_kv;
+    const int64_t total = (int64_t)B * T_q * H_q;
+    const int64_t n = rows ? n_rows : total;
+    const int64_t kstride = (int64_t)H_kv * d;
+    int bad = 0;
+    set_threads(nthreads);
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)S_kv);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!s || !acc) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t i = 0; i < n; ++i) {
+                int64_t r = rows ? rows[i] : i;
+                if (r < 0 || r >= total) {
+#pragma omp atomic write
+                    bad = 1;
+                    continue;
+                }
+                int h = (int)(r % H_q);
+                int64_t bt = r / H_q;
+                int t = (int)(bt % T_q);
+                int b = (int)(bt / T_q);
+                int kv = h / G;
+                int64_t p = (int64_t)q_offset + t;
+                const float *qrow = q + r * d;
+                const float *kb = k + ((int64_t)b * S_kv * H_kv + kv) * d;
+                const float *vb = v + ((int64_t)b * S_kv * H_kv + kv) * d;
+                /* pass 1: scores of the visible keys and their max */
+                double m = -INFINITY;
+                for (int64_t j = 0; j <= p; ++j) {
+                    if (!(j < sink || j > p - window)) continue;
+                    const float *krow = kb + j * kstride;
+                    double dot = 0.0;
+                    for (int x = 0; x < d; ++x) dot += (double)qrow[x] * (double)krow[x];
+                    s[j] = scale * dot;
+                    if (s[j] > m) m = s[j];
+                }
+                /* pass 2: exponentials, their sum and the weighted sum of V */
+                double l = 0.0;
+                for (int x = 0; x < d; ++x) acc[x] = 0.0;
+                for (int64_t j = 0; j <= p; ++j) {
+                    if (!(j < sink || j > p - window)) continue;
+                    double pj = exp(s[j] - m);
+                    l += pj;
+                    const float *vrow = vb + j * kstride;
+                    for (int x = 0; x < d; ++x) acc[x] += pj * (double)vrow[x];
+                }
                 for (int x = 0; x < d; ++x) o[i * d + x] = acc[x] / l;
                 if (lse) lse[i] = m + log(l);
             }

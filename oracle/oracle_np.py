@@ -29,7 +29,10 @@ def _attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
 
 
 def prefill(q, k, v, *, causal: bool, q_offset: int = 0, scale: float | None = None,
-            return_probs: bool = False):
+            return_probs: bool = False, window: int | None = None, sink: int = 0):
+    """``window`` (causal only): additionally hide key j from the query at
+    position p unless j < sink or j > p - window (the sink + local-window
+    policy of the pccx page, section 4, hard-cap ring buffer)."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -41,7 +44,10 @@ def prefill(q, k, v, *, causal: bool, q_offset: int = 0, scale: float | None = N
     vis = None
     if causal:
         pos = q_offset + np.arange(T)[:, None]
-        vis = np.arange(S)[None, :] <= pos
+        key = np.arange(S)[None, :]
+        vis = key <= pos
+        if window is not None:
+            vis = vis & ((key < sink) | (key > pos - window))
     o = np.empty((B, T, Hq, d))
     lse = np.empty((B, T, Hq))
     probs = np.empty((B, Hq, T, S)) if return_probs else None

@@ -17,7 +17,10 @@ AssertionError when the oracle disagrees with the pinned fact.  The facts:
 * torch's scaled_dot_product_attention in float64 (a library routine), for
   multi-head attention and for GQA with its own enable_gqa head grouping;
 * split invariance: the FlashDecoding form (per-split partials merged with the
-  section 4 formula) equals the unsplit result for any split count.
+  section 4 formula) equals the unsplit result for any split count;
+* the sink + local-window mask: uniform weights over an explicitly built
+  visible set, Decimal brute force, and its two limits (the causal mask, the
+  diagonal alone).
 Scores s_j are formed here with math.fsum over exactly representable products
 (float32 x float32 fits in float64), i.e. correctly rounded dot products.
 """
@@ -373,6 +376,89 @@ def pin_split_invariance(lib):
         _close(lse, l0, what=f"split LSE ns={ns}")
 
 
+# ---------------------------------------------------------------------------
+# sink + local-window mask (pccx page, section 4, hard-cap ring buffer policy)
+#
+# The visible set of a query at position p is built here as an explicit union
+# of two integer ranges -- the first `sink` positions and the `window` newest
+# positions up to p -- not through the oracle's per-key predicate.
+
+
+def _window_set(p, window, sink):
+    return sorted(set(range(min(sink, p + 1))) | set(range(max(0, p - window + 1), p + 1)))
+
+
+def pin_window_uniform(lib):
+    """Q = 0: uniform weights over the visible set, so O is the mean of V over
+    exactly those positions and LSE = ln(count)."""
+    rng = _rng(20)
+    Hq, Hkv, d = 4, 2, 8
+    G = Hq // Hkv
+    S = 40
+    k = _randf32(rng, (1, S, Hkv, d))
+    v = _randf32(rng, (1, S, Hkv, d))
+    for T, q_offset, window, sink in ((8, 32, 5, 3), (12, 0, 4, 2), (6, 30, 1, 0), (6, 30, 1, 4),
+                                      (10, 20, 64, 0), (7, 10, 3, 30), (9, 31, 8, 8)):
+        q = np.zeros((1, T, Hq, d), np.float32)
+        o, lse = lib.prefill_window(q, k[:, :q_offset + T], v[:, :q_offset + T],
+                                    q_offset=q_offset, window=window, sink=sink)
+        for t in range(T):
+            vis = _window_set(q_offset + t, window, sink)
+            for h in range(Hq):
+                mean = np.array([math.fsum(float(v[0, j, h // G, x]) for j in vis) / len(vis)
+                                 for x in range(d)])
+                _close(o[0, t, h], mean, what=f"window mean w={window} s={sink}")
+                _close(lse[0, t, h], math.log(len(vis)), what=f"window LSE w={window} s={sink}")
+
+
+def pin_window_decimal(lib):
+    """Random queries on tiny shapes: 50-digit textbook softmax over the
+    explicit visible set."""
+    rng = _rng(21)
+    B, T, S, Hq, Hkv, d = 2, 5, 9, 4, 2, 3
+    G = Hq // Hkv
+    q = _randf32(rng, (B, T, Hq, d), 1.5)
+    k = _randf32(rng, (B, S, Hkv, d))
+    v = _randf32(rng, (B, S, Hkv, d))
+    with decimal.localcontext() as ctx:
+        ctx.prec = 50
+        for window, sink in ((2, 1), (3, 0), (1, 2), (4, 3)):
+            o, lse = lib.prefill_window(q, k, v, q_offset=S - T, window=window, sink=sink,
+                                        scale=0.7)
+            for b in range(B):
+                for t in range(T):
+                    vis = _window_set(S - T + t, window, sink)
+                    for h in range(Hq):
+                        eo, el = _dec_attend(q[b, t, h], k[b, vis, h // G], v[b, vis, h // G],
+                                             0.7)
+                        _close(o[b, t, h], eo, what="window decimal O")
+                        _close(lse[b, t, h], el, what="window decimal LSE")
+
+
+def pin_window_limits(lib):
+    """A window covering every earlier key is the causal mask; a window of one
+    with no sink sees only the diagonal: O = v_p, LSE = s_pp."""
+    rng = _rng(22)
+    Hq, Hkv, d = 6, 3, 8
+    G = Hq // Hkv
+    q = _randf32(rng, (2, 7, Hq, d))
+    k = _randf32(rng, (2, 19, Hkv, d))
+    v = _randf32(rng, (2, 19, Hkv, d))
+    oc, lc = lib.prefill(q, k, v, causal=True, q_offset=12)
+    for window, sink in ((19, 0), (1000, 5), (19, 19)):
+        o, lse = lib.prefill_window(q, k, v, q_offset=12, window=window, sink=sink)
+        _close(o, oc, what="window = causal O")
+        _close(lse, lc, what="window = causal LSE")
+    o, lse = lib.prefill_window(q, k, v, q_offset=12, window=1, sink=0, scale=0.3)
+    for b in range(2):
+        for t in range(7):
+            for h in range(Hq):
+                _close(o[b, t, h], v[b, 12 + t, h // G], what="diagonal-only O")
+                _close(lse[b, t, h], 0.3 * _dot(q[b, t, h], k[b, 12 + t, h // G]),
+                       what="diagonal-only LSE")
+
+
 ALL_PINS = [pin_uniform_scores, pin_equal_keys, pin_constant_v, pin_one_and_two_keys,
             pin_decimal_bruteforce, pin_torch_sdpa, pin_identity_v, pin_moving_max,
-            pin_large_scores, pin_split_invariance]
+            pin_large_scores, pin_split_invariance, pin_window_uniform, pin_window_decimal,
+            pin_window_limits]

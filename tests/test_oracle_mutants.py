@@ -35,6 +35,10 @@ MUTANTS = [
      "int64_t j0 = sp * len / ns, j1 = (sp + 1) * len / ns - (sp + 1 < ns);"),
     ("seq_offset_shift", "off[b] = acc;", "off[b] = b ? acc - 1 : 0;"),
     ("max_not_updated", "if (sj > m) m = sj;", "if (sj > m && j == j0) m = sj;"),
+    ("window_off_by_one", "j > p - window", "j >= p - window"),
+    ("sink_inclusive", "(j < sink ||", "(j <= sink ||"),
+    ("window_ignores_sink", "(j < sink || j > p - window)", "(j > p - window)"),
+    ("window_from_row_index", "int64_t p = (int64_t)q_offset + t;", "int64_t p = (int64_t)t + (t > 0) * q_offset;"),
 ]
 
 CHILD = textwrap.dedent("""

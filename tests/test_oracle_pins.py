@@ -21,6 +21,11 @@ class _NumpyOracle:
         return oracle_np.prefill(q, k, v, causal=causal, q_offset=q_offset, scale=scale)
 
     @staticmethod
+    def prefill_window(q, k, v, *, q_offset, window, sink=0, scale=None):
+        return oracle_np.prefill(q, k, v, causal=True, q_offset=q_offset, scale=scale,
+                                 window=window, sink=sink)
+
+    @staticmethod
     def decode(q, k, v, kv_len, *, scale=None, num_splits=0):
         # the NumPy form has no split path; it answers the unsplit definition
         return oracle_np.decode(q, k, v, kv_len, scale=scale)
@@ -40,6 +45,20 @@ def test_c_matches_numpy(causal, q_offset, T, S):
     v = rng.standard_normal((2, S, 2, 32)).astype(np.float32)
     o, lse = oracle.prefill(q, k, v, causal=causal, q_offset=q_offset)
     o2, lse2 = oracle_np.prefill(q, k, v, causal=causal, q_offset=q_offset)
+    assert np.max(np.abs(o - o2)) <= 1e-12
+    assert np.max(np.abs(lse - lse2)) <= 1e-12
+
+
+@pytest.mark.parametrize("q_offset,T,S,window,sink", [(0, 33, 33, 7, 2), (17, 16, 40, 5, 0),
+                                                       (30, 10, 40, 1, 3), (5, 20, 25, 100, 4)])
+def test_c_matches_numpy_window(q_offset, T, S, window, sink):
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((2, T, 8, 32)).astype(np.float32)
+    k = rng.standard_normal((2, S, 2, 32)).astype(np.float32)
+    v = rng.standard_normal((2, S, 2, 32)).astype(np.float32)
+    o, lse = oracle.prefill_window(q, k, v, q_offset=q_offset, window=window, sink=sink)
+    o2, lse2 = oracle_np.prefill(q, k, v, causal=True, q_offset=q_offset, window=window,
+                                 sink=sink)
     assert np.max(np.abs(o - o2)) <= 1e-12
     assert np.max(np.abs(lse - lse2)) <= 1e-12
 
