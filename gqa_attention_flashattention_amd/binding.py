@@ -60,6 +60,8 @@ def load_library():
     lib.gqa_attn_prefill_kvsplit.restype = i
     lib.gqa_attn_prefill_kvsplit.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, i,
                                              vp]
+    lib.gqa_attn_prefill_window.restype = i
+    lib.gqa_attn_prefill_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, i, vp]
     lib.gqa_attn_prefill_kvsplit_count.restype = i
     lib.gqa_attn_prefill_kvsplit_count.argtypes = [i] * 9
     lib.gqa_attn_decode_multi.restype = i
@@ -178,6 +180,38 @@ def prefill_kvsplit(q, k, v, *, causal: bool, q_offset: int = 0, scale: float | 
         float(scale), int(bool(causal)), int(q_offset), int(num_splits), _dtype_code(q),
         _stream(q.device))
     _check(rc, "gqa_attn_prefill_kvsplit")
+    return out, lse
+
+
+def prefill_window(q, k, v, *, window: int, sink: int = 0, q_offset: int = 0,
+                   scale: float | None = None, out=None, lse=None, return_lse: bool = True):
+    """Causal prefill with `sink` attention-sink keys and a local window of
+    `window` keys (bf16): the query at position p sees key j iff j <= p and
+    (j < sink or j > p - window)."""
+    import torch
+    _require(q, "q", 4)
+    _require(k, "k", 4)
+    _require(v, "v", 4)
+    B, T_q, H_q, d = q.shape
+    S_kv, H_kv = k.shape[1], k.shape[2]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        raise GQAError("k and v must be [B, S_kv, H_kv, d] matching q", 2)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise GQAError("q, k, v must share one dtype", 3)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require(out, "out", 4)
+    if lse is None and return_lse:
+        lse = torch.empty((B, T_q, H_q), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _require(lse, "lse", 3)
+    rc = load_library().gqa_attn_prefill_window(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, T_q, S_kv, H_q, H_kv, d,
+        float(scale), int(q_offset), int(window), int(sink), _dtype_code(q), _stream(q.device))
+    _check(rc, "gqa_attn_prefill_window")
     return out, lse
 
 

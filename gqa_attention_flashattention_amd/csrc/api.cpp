@@ -397,6 +397,20 @@ int gqa_attn_prefill_kvsplit(const void* q, const void* k, const void* v, void* 
     return GQA_OK;
 }
 
+int gqa_attn_prefill_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int T_q, int S_kv, int H_q, int H_kv, int d, float scale,
+                            int q_offset, int window, int sink, int dtype, void* stream) {
+    int rc = check_prefill_args(q, k, v, o, B, T_q, S_kv, H_q, H_kv, d, scale, 1, q_offset);
+    if (rc) return rc;
+    if (dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+    if (window < 1 || sink < 0) return GQA_ERR_RANGE;
+    gqa::PrefillArgs a{q, k, v, o, lse, B, T_q, S_kv, H_q, H_kv, d, scale, 1, q_offset};
+    a.window = window;
+    a.sink = sink < S_kv ? sink : S_kv;
+    (void)hipGetLastError();
+    return gqa::launch_prefill_bf16(a, (hipStream_t)stream) == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
 int gqa_attn_prefill_kvsplit_count(int B, int T_q, int S_kv, int H_q, int H_kv, int d, int causal,
                                    int q_offset, int num_splits) {
     if (B < 1 || T_q < 1 || S_kv < 1 || check_heads(H_q, H_kv, d)) return -GQA_ERR_SHAPE;

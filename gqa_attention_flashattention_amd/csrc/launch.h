@@ -17,6 +17,8 @@ struct PrefillArgs {
     float scale;
     int causal;
     int q_offset;
+    int window = 0;   // > 0: causal with attention sinks + local window (bf16 kernel only)
+    int sink = 0;
 };
 
 // Sequences described per decode launch (kernel-argument plan).

@@ -136,12 +136,23 @@ struct LaneOffsets {
 // partial (m in base-2 units, l, O) of its rows to the workspace instead of
 // O and LSE (partial row ((b * n_split + split) * T_q + t) * H_q + h); the
 // decode combine kernel merges them.
-template <int D, bool CAUSAL, bool SPLIT>
+//
+// MASK: kMaskNone (every key), kMaskCausal (key j visible to position p iff
+// j <= p), kMaskWindow (causal, and j < sink or j > p - window: attention
+// sinks plus a local window).  With the window, a row block's key tiles are
+// the sink tiles followed by the window tiles; the tiles in between are
+// never loaded.
+constexpr int kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2;
+
+template <int D, int MASK, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int B,
     int T_q, int S_kv, int H_q, int H_kv, int G, float c, int q_offset, int n_mblk,
-    int n_split, float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o) {
+    int n_split, float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
+    int window, int sink) {
+    constexpr bool CAUSAL = MASK != kMaskNone;
+    constexpr bool WINDOW = MASK == kMaskWindow;
     using T = Tile<D>;
     constexpr int KSTEPS = D / 16;   // MFMA k-steps over the head dim
     constexpr int DBLK = D / 32;     // 32-row blocks of O^T
@@ -189,7 +200,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     // branches on them are scalar branches)
     const int t_hi = min(T_q - 1, (r0 + kBlockM - 1) / G);
     const int kend = CAUSAL ? min(S_kv, q_offset + t_hi + 1) : S_kv;
-    const int wg_tiles = (kend + kBlockN - 1) / kBlockN;
+    int wg_tiles = (kend + kBlockN - 1) / kBlockN;
+    // window: tiles [0, sink_tiles) then [sink_tiles + gap, ...); the work-group
+    // counts tiles in that compacted order (tile index = j + (j >= sink_tiles) * gap)
+    int sink_tiles = 0, gap = 0;
+    if (WINDOW) {
+        const int t_lo = min(T_q - 1, r0 / G);
+        const int p_lo = q_offset + t_lo;
+        sink_tiles = (min(sink, kend) + kBlockN - 1) / kBlockN;
+        const int w_tile0 = max(0, p_lo - window + 1) / kBlockN;
+        gap = max(0, w_tile0 - sink_tiles);
+        wg_tiles -= gap;
+        sink_tiles = __builtin_amdgcn_readfirstlane(sink_tiles);
+        gap = __builtin_amdgcn_readfirstlane(gap);
+    }
     // this work-group's tiles: [j_lo, j_lo + n_tiles)
     int j_lo = 0, n_tiles = wg_tiles;
     if (SPLIT) {
@@ -209,14 +233,22 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         CAUSAL ? min(S_kv, q_offset + wt_lo + 1) : S_kv);
     // last key this row may see (rows past the end see everything: their output is dropped)
     const int last_key = CAUSAL ? (valid ? min(q_offset + t, S_kv - 1) : S_kv - 1) : S_kv - 1;
+    // window: keys in [sink, win_lo) are hidden from this row; the wave's rows
+    // all see [0, sink) and [wave_win_all, wave_full); a tile is needed by some
+    // row of the wave if it reaches wave_win_any
+    const int win_lo = (WINDOW && valid) ? q_offset + t - window + 1 : -1;
+    const int wave_win_any = __builtin_amdgcn_readfirstlane(WINDOW ? q_offset + wt_lo - window + 1 : 0);
+    const int wave_win_all = __builtin_amdgcn_readfirstlane(WINDOW ? q_offset + wt_hi - window + 1 : 0);
 
     const int64_t row_stride = (int64_t)H_kv * D;
     const uint16_t* kbase = k + ((int64_t)b * S_kv * H_kv + kv) * D;
     const uint16_t* vbase = v + ((int64_t)b * S_kv * H_kv + kv) * D;
 
     // the first two tiles start loading before anything else
-    if (n_tiles > 0) issue_tile<D>(ks0, vs0, kbase, vbase, row_stride, j_lo, S_kv, wave, lane);
-    if (n_tiles > 1) issue_tile<D>(ks1, vs1, kbase, vbase, row_stride, j_lo + 1, S_kv, wave, lane);
+    // global tile of the work-group's compacted tile index j
+    auto tile_of = [&](int j) { return WINDOW ? j + (j >= sink_tiles ? gap : 0) : j; };
+    if (n_tiles > 0) issue_tile<D>(ks0, vs0, kbase, vbase, row_stride, tile_of(j_lo), S_kv, wave, lane);
+    if (n_tiles > 1) issue_tile<D>(ks1, vs1, kbase, vbase, row_stride, tile_of(j_lo + 1), S_kv, wave, lane);
 
     // Q^T operand, resident for the whole key sweep.
     bf16x8 qf[KSTEPS];
@@ -256,9 +288,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     // stage that tile j - 1 used.
     auto step = [&](int j, const uint16_t* kt, const uint16_t* vt, uint16_t* kn, uint16_t* vn) {
         const bool issue = j + 2 < n_tiles;
-        if (issue) issue_tile<D>(kn, vn, kbase, vbase, row_stride, j_lo + j + 2, S_kv, wave, lane);
-        const int key0 = (j_lo + j) * kBlockN;
-        if (key0 < wave_kend) {
+        if (issue) issue_tile<D>(kn, vn, kbase, vbase, row_stride, tile_of(j_lo + j + 2), S_kv, wave, lane);
+        const int key0 = tile_of(j_lo + j) * kBlockN;
+        bool wave_needs = key0 < wave_kend;
+        if (WINDOW) wave_needs = wave_needs && (key0 < sink || key0 + kBlockN > wave_win_any);
+        if (wave_needs) {
             // ---- S^T = K Q^T (two 32-key blocks) ----
             f32x16 s[2];
 #pragma unroll
@@ -271,13 +305,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
                 }
             }
             // element i of s[kb] is key key0 + 32 kb + 16 (i / 8) + 8 hh + (i % 8)
-            if (key0 + kBlockN > wave_full) {
+            bool need_mask = key0 + kBlockN > wave_full;
+            if (WINDOW)
+                need_mask = need_mask || (key0 + kBlockN > sink && key0 < wave_win_all);
+            if (need_mask) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int key = key0 + kb * 32 + (i >> 3) * 16 + hh * 8 + (i & 7);
-                        if (key > last_key) s[kb][i] = -INFINITY;
+                        bool hide = key > last_key;
+                        if (WINDOW) hide = hide || (key >= sink && key < win_lo);
+                        if (hide) s[kb][i] = -INFINITY;
                     }
             }
             // ---- online softmax (base 2), lazy rescale ----
@@ -302,7 +341,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
                 m_run = m_new;
             }
             // a split can start past a row's last key: its m stays -inf, P = 0
-            const float mc = (SPLIT && m_run == -INFINITY) ? 0.f : m_run * c;
+            // (a window or a split can start past the keys a row sees)
+            const float mc = ((SPLIT || WINDOW) && m_run == -INFINITY) ? 0.f : m_run * c;
             float psum = 0.f;
             uint32_t pk[2][8];
 #pragma unroll
@@ -389,38 +429,48 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 
 }  // namespace
 
-template <int D, bool CAUSAL, bool SPLIT>
+template <int D, int MASK, bool SPLIT>
 static hipError_t launch_one(const PrefillArgs& a, int n_split, const DecodeWorkspace* ws,
                              hipStream_t stream) {
     const int64_t n_mblk = prefill_row_blocks(a.T_q, a.H_q / a.H_kv);
     const int64_t grid = n_mblk * a.B * a.H_kv * (SPLIT ? n_split : 1);
     if (grid < 1 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     const float c = a.scale * kLog2e;
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, SPLIT>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, MASK, SPLIT>), dim3((unsigned)grid),
                        dim3(kThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.T_q, a.S_kv, a.H_q,
                        a.H_kv, a.H_q / a.H_kv, c, a.q_offset, (int)n_mblk, n_split,
-                       SPLIT ? ws->m : nullptr, SPLIT ? ws->l : nullptr, SPLIT ? ws->o : nullptr);
+                       SPLIT ? ws->m : nullptr, SPLIT ? ws->l : nullptr, SPLIT ? ws->o : nullptr,
+                       a.window, a.sink);
     return hipGetLastError();
 }
 
 int64_t prefill_row_blocks(int T_q, int G) { return ((int64_t)T_q * G + kBlockM - 1) / kBlockM; }
 
-hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
+template <bool SPLIT>
+static hipError_t dispatch(const PrefillArgs& a, int n_split, const DecodeWorkspace* ws,
+                           hipStream_t stream) {
+    if constexpr (!SPLIT) {   // the window mask is built without the key split
+        if (a.window > 0)
+            return a.d == 128 ? launch_one<128, kMaskWindow, false>(a, 1, nullptr, stream)
+                              : launch_one<64, kMaskWindow, false>(a, 1, nullptr, stream);
+    } else {
+        if (a.window > 0) return hipErrorInvalidValue;
+    }
     if (a.d == 128)
-        return a.causal ? launch_one<128, true, false>(a, 1, nullptr, stream)
-                        : launch_one<128, false, false>(a, 1, nullptr, stream);
-    return a.causal ? launch_one<64, true, false>(a, 1, nullptr, stream)
-                    : launch_one<64, false, false>(a, 1, nullptr, stream);
+        return a.causal ? launch_one<128, kMaskCausal, SPLIT>(a, n_split, ws, stream)
+                        : launch_one<128, kMaskNone, SPLIT>(a, n_split, ws, stream);
+    return a.causal ? launch_one<64, kMaskCausal, SPLIT>(a, n_split, ws, stream)
+                    : launch_one<64, kMaskNone, SPLIT>(a, n_split, ws, stream);
+}
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
+    return dispatch<false>(a, 1, nullptr, stream);
 }
 
 hipError_t launch_prefill_split_bf16(const PrefillArgs& a, int n_split, const DecodeWorkspace& ws,
                                      hipStream_t stream) {
-    if (a.d == 128)
-        return a.causal ? launch_one<128, true, true>(a, n_split, &ws, stream)
-                        : launch_one<128, false, true>(a, n_split, &ws, stream);
-    return a.causal ? launch_one<64, true, true>(a, n_split, &ws, stream)
-                    : launch_one<64, false, true>(a, n_split, &ws, stream);
+    return dispatch<true>(a, n_split, &ws, stream);
 }
 
 }  // namespace gqa

@@ -34,6 +34,8 @@ class Workload:
     causal: bool = False
     q_offset: int = 0
     kv_len_range: tuple | None = None   # varlen decode: (lo, hi) inclusive
+    window: int = 0         # > 0: sink + local-window mask (keys j < sink or j > p - window)
+    sink: int = 0
 
     @property
     def G(self) -> int:
@@ -58,6 +60,8 @@ WORKLOADS = {
                  T_q=2048, S_kv=67584, causal=True, q_offset=65536),
         Workload("prefill_chunk_256_64k", "prefill", "bf16", B=1, H_q=64, H_kv=8, d=128,
                  T_q=256, S_kv=65792, causal=True, q_offset=65536),
+        Workload("prefill_8k_window1k", "prefill", "bf16", B=1, H_q=64, H_kv=8, d=128,
+                 T_q=8192, S_kv=8192, causal=True, window=1024, sink=4),
         Workload("decode_t4_varlen_b16", "decode", "bf16", B=16, H_q=64, H_kv=8, d=128,
                  T_q=4, kv_len_range=(1024, 32768)),
     ]

@@ -101,6 +101,23 @@ int gqa_attn_prefill_kvsplit(const void *q, const void *k, const void *v, void *
                              int causal, int q_offset, int num_splits, int dtype, void *stream);
 
 /*
+ * Causal prefill with attention sinks and a local window (the sink +
+ * local-window policy of the hard-cap ring-buffer KV cache, pccx page "Gemma
+ * 3N E4B on pccx v002 -- Execution / Scheduling", section 4; ADR-0060 section
+ * 5.4 tile classes extended to it): the query at position p = q_offset + t
+ * sees key j iff j <= p and (j < sink or j > p - window).  Arguments and
+ * layouts as gqa_attn_prefill with causal = 1 (bf16 only).  Key tiles that
+ * no row of a block sees (between the sink tiles and the block's window) are
+ * never loaded.  Requires window >= 1 and sink >= 0 (sink >= S_kv means every
+ * earlier key is a sink, i.e. plain causal).
+ * Errors: as gqa_attn_prefill; GQA_ERR_RANGE for window < 1 or sink < 0;
+ * GQA_ERR_UNSUPPORTED for dtype != GQA_BF16.
+ */
+int gqa_attn_prefill_window(const void *q, const void *k, const void *v, void *o, float *lse,
+                            int B, int T_q, int S_kv, int H_q, int H_kv, int d, float scale,
+                            int q_offset, int window, int sink, int dtype, void *stream);
+
+/*
  * Host only: the number of key ranges n that gqa_attn_prefill_kvsplit uses for
  * these arguments (>= 1), or minus a gqa_status code for invalid sizes.
  */

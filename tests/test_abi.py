@@ -25,6 +25,7 @@ def test_header_declares_the_boundary():
     for n in ["gqa_attn_prefill", "gqa_attn_decode", "gqa_attn_decode_split",
               "gqa_attn_decode_combine", "gqa_attn_decode_plan", "gqa_attn_decode_multi",
               "gqa_attn_prefill_kvsplit", "gqa_attn_prefill_kvsplit_count",
+              "gqa_attn_prefill_window",
               "gqa_attn_status_string", "gqa_attn_version"]:
         assert n in names
 
@@ -119,6 +120,19 @@ def test_kvsplit_rejects_and_counts():
     # a large grid needs no split; a short chunk over a long cache gets several
     assert gq.prefill_kvsplit_count(1, 8192, 8192, 64, 8, 128, causal=True) == 1
     assert gq.prefill_kvsplit_count(1, 256, 65792, 64, 8, 128, causal=True, q_offset=65536) > 1
+
+
+def test_window_prefill_rejects():
+    lib = gq.load_library()
+    args = lambda **kw: [kw.get("q", P), P, P, kw.get("o", P), None, 1, 4, 8, 8, 2,
+                         kw.get("d", 128), 0.1, kw.get("qoff", 4), kw.get("window", 3),
+                         kw.get("sink", 0), kw.get("dtype", 0), None]
+    assert lib.gqa_attn_prefill_window(*args(q=None)) == 1
+    assert lib.gqa_attn_prefill_window(*args(d=96)) == 3
+    assert lib.gqa_attn_prefill_window(*args(dtype=1)) == 3
+    assert lib.gqa_attn_prefill_window(*args(qoff=5)) == 4
+    assert lib.gqa_attn_prefill_window(*args(window=0)) == 4
+    assert lib.gqa_attn_prefill_window(*args(sink=-1)) == 4
 
 
 def test_split_and_combine_reject_small_workspace():
