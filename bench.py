@@ -81,7 +81,19 @@ def decode_algorithmic_bytes(w, kv_len):
 def prefill_algorithmic_flops(w):
     t = np.arange(w.T_q, dtype=np.float64)
     vis = np.minimum(w.q_offset + t + 1, w.S_kv) if w.causal else np.full(w.T_q, w.S_kv)
+    if w.window > 0:     # sinks + local window: min(sink, p+1) + keys in (max(sink, p-window), p]
+        p = w.q_offset + t
+        sinks = np.minimum(w.sink, p + 1)
+        vis = sinks + np.maximum(0.0, p - np.maximum(w.sink, p - w.window + 1) + 1)
     return float(4.0 * w.d * w.H_q * w.B * vis.sum())
+
+
+def ring_walk_lengths(w, kv_len):
+    """Keys a ring-buffer decode reads per sequence (resident sinks + window)."""
+    n = np.asarray(kv_len, np.int64)
+    s_end = np.minimum(w.sink, n)
+    w_lo = np.maximum(s_end, n - w.T_q - w.window + 1)
+    return s_end + (n - w_lo)
 
 
 def bench_decode(name, steps, warmup):
@@ -215,6 +227,55 @@ def bench_prefill_kvsplit(name, steps):
                 lse_gpu=lse.cpu().numpy())
 
 
+def bench_prefill_window(name, steps):
+    import torch
+    import gqa_attention_flashattention_amd as gq
+    from gqa_attention_flashattention_amd import inputs as gin
+    inp = gin.make(name)
+    w = inp.workload
+    q, k, v = (dev_tensor(x) for x in (inp.q_store, inp.k_store, inp.v_store))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    fn = lambda: gq.prefill_window(q, k, v, q_offset=w.q_offset, window=w.window, sink=w.sink,
+                                   out=o, lse=lse)
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    ms = time_graph([fn] * steps)
+    return dict(inp=inp, ms=ms, flops=prefill_algorithmic_flops(w), o_gpu=o.float().cpu().numpy(),
+                lse_gpu=lse.cpu().numpy())
+
+
+def bench_decode_ring(name, steps):
+    """Ring-buffer decode; rotating copies of the cache keep every call cold."""
+    import torch
+    import gqa_attention_flashattention_amd as gq
+    from gqa_attention_flashattention_amd import inputs as gin
+    inp = gin.make(name)
+    w = inp.workload
+    walk = ring_walk_lengths(w, inp.kv_len)
+    kv_bytes = int(walk.sum()) * w.H_kv * w.d * 2 * 2
+    q = dev_tensor(inp.q_store)
+    k0 = dev_tensor(inp.k_store)
+    v0 = dev_tensor(inp.v_store)
+    n_copies = max(1, min(64, math.ceil(ROTATE_BYTES / kv_bytes)))
+    ks = [k0] + [k0.clone() for _ in range(n_copies - 1)]
+    vs = [v0] + [v0.clone() for _ in range(n_copies - 1)]
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+
+    def call(i):
+        return lambda: gq.decode_ring(q, ks[i % n_copies], vs[i % n_copies], inp.kv_len,
+                                      window=w.window, sink=w.sink, out=out, lse=lse)
+
+    for i in range(3):
+        call(i)()
+    torch.cuda.synchronize()
+    ms = time_graph([call(i) for i in range(steps)])
+    return dict(inp=inp, ms=ms, kv_bytes=kv_bytes, n_copies=n_copies,
+                o_gpu=out.float().cpu().numpy(), lse_gpu=lse.cpu().numpy())
+
+
 def copy_calibration(mib: int):
     """A plain device-to-device copy of `mib` MiB, three times (rocprofv3
     counter runs scale FETCH_SIZE / WRITE_SIZE by what this copy reads)."""
@@ -315,6 +376,45 @@ def parity_prefill_kvsplit(kvs, n_rows=64):
             "prefill_kvsplit_sample_max_abs_dLSE": float(np.abs(lg - l).max())}
 
 
+def parity_prefill_window(pw_, n_rows=64):
+    import oracle
+    inp = pw_["inp"]
+    w = inp.workload
+    rng = np.random.default_rng(0)
+    total = w.B * w.T_q * w.H_q
+    rows = np.unique(np.concatenate([[0, total - 1], rng.integers(0, total, n_rows - 2)]))
+    o, l = oracle.prefill_window(inp.q, inp.k, inp.v, q_offset=w.q_offset, window=w.window,
+                                 sink=w.sink, rows=rows)
+    og = pw_["o_gpu"].reshape(-1, w.d)[rows].astype(np.float64)
+    lg = pw_["lse_gpu"].reshape(-1)[rows].astype(np.float64)
+    return {"prefill_window_sample_max_abs_dO": float(np.abs(og - o).max()),
+            "prefill_window_sample_max_abs_dLSE": float(np.abs(lg - l).max())}
+
+
+def parity_decode_ring(dr, n_seq=2):
+    """Oracle check of the first n_seq sequences: the logical sequence each
+    ring cache holds, rebuilt from the ring rule, through the window oracle."""
+    import oracle
+    inp = dr["inp"]
+    w = inp.workload
+    wrap = w.capacity - w.sink
+    eo, el = [], []
+    for b, n in enumerate(np.asarray(inp.kv_len).tolist()[:n_seq]):
+        pos = np.arange(n)
+        keep = (pos < w.sink) | (pos >= n - wrap)
+        slot = np.where(pos < w.sink, pos, w.sink + (pos - w.sink) % wrap)
+        kl = np.zeros((n, w.H_kv, w.d), np.float32)
+        vl = np.zeros((n, w.H_kv, w.d), np.float32)
+        kl[keep] = inp.k[b, slot[keep]]
+        vl[keep] = inp.v[b, slot[keep]]
+        o, l = oracle.prefill_window(inp.q[b:b + 1], kl[None], vl[None], q_offset=n - w.T_q,
+                                     window=w.window, sink=w.sink)
+        eo.append(np.abs(dr["o_gpu"][b] - o[0]).max())
+        el.append(np.abs(dr["lse_gpu"][b] - l[0]).max())
+    return {"decode_ring_sample_max_abs_dO": float(max(eo)),
+            "decode_ring_sample_max_abs_dLSE": float(max(el))}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -325,10 +425,15 @@ def main():
     ap.add_argument("--prefill-workload", default="prefill_8k_causal")
     ap.add_argument("--kvsplit-workload", default="prefill_chunk_256_64k",
                     help="KV-parallel prefill workload (reported under prefill_kvsplit)")
+    ap.add_argument("--window-workload", default="prefill_8k_window1k",
+                    help="sink + local-window prefill workload (reported under prefill_window)")
+    ap.add_argument("--ring-workload", default="decode_ring_8k_b16",
+                    help="ring-buffer decode workload (reported under decode_ring)")
     ap.add_argument("--multi-workload", default="decode_t4_varlen_b16",
                     help="multi-token decode workload (reported under decode_multi)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["decode", "prefill", "decode_multi", "prefill_kvsplit"],
+    ap.add_argument("--only", choices=["decode", "prefill", "decode_multi", "prefill_kvsplit",
+                                       "prefill_window", "decode_ring"],
                     default=None,
                     help="run one path only (profiling runs); prints a partial line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -352,6 +457,16 @@ def main():
         mul = bench_decode_multi(args.multi_workload, min(args.steps, 200), args.warmup)
         log(f"[bench] decode_multi {mul['ms'] * 1e3:.2f} us/call "
             f"{mul['kv_bytes'] / (mul['ms'] * 1e-3) / 1e9:.1f} GB/s")
+        return
+    if args.only == "prefill_window":
+        pw_ = bench_prefill_window(args.window_workload, args.prefill_steps)
+        log(f"[bench] prefill_window {pw_['ms'] * 1e3:.1f} us/call "
+            f"{pw_['flops'] / (pw_['ms'] * 1e-3) / 1e12:.1f} TFLOP/s")
+        return
+    if args.only == "decode_ring":
+        dr = bench_decode_ring(args.ring_workload, min(args.steps, 200))
+        log(f"[bench] decode_ring {dr['ms'] * 1e3:.1f} us/call "
+            f"{dr['kv_bytes'] / (dr['ms'] * 1e-3) / 1e9:.1f} GB/s")
         return
     if args.only == "prefill_kvsplit":
         kvs = bench_prefill_kvsplit(args.kvsplit_workload, args.prefill_steps)
@@ -381,6 +496,11 @@ def main():
     log(f"[bench] prefill_kvsplit {args.kvsplit_workload}")
     kvs = bench_prefill_kvsplit(args.kvsplit_workload, args.prefill_steps)
     log(f"[bench] prefill_kvsplit {kvs['ms'] * 1e3:.1f} us/call (plain {kvs['ms_plain'] * 1e3:.1f} us)")
+
+    log(f"[bench] prefill_window {args.window_workload}")
+    pwin = bench_prefill_window(args.window_workload, args.prefill_steps)
+    log(f"[bench] decode_ring {args.ring_workload}")
+    dring = bench_decode_ring(args.ring_workload, min(args.steps, 200))
 
     dw = dec["inp"].workload
     gbs = dec["kv_bytes"] / (dec["ms_call"] * 1e-3) / 1e9
@@ -449,6 +569,28 @@ def main():
                      "algorithmic_flops_per_call": kvs["flops"],
                      "note": "whole call (split prefill + combine kernels)"},
     }
+    ww = pwin["inp"].workload
+    tf_win = pwin["flops"] / (pwin["ms"] * 1e-3) / 1e12
+    result["prefill_window"] = {
+        "workload": ww.name, "T_q": ww.T_q, "S_kv": ww.S_kv, "window": ww.window,
+        "sink": ww.sink, "ms_per_call": pwin["ms"], "value": round(tf_win, 2), "unit": "TFLOP/s",
+        "roofline": {"bound": "mfma", "achieved": round(tf_win, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf_win / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "algorithmic_flops_per_call": pwin["flops"],
+                     "note": "visible (sink + window) pairs only"},
+    }
+    rw = dring["inp"].workload
+    gbs_ring = dring["kv_bytes"] / (dring["ms"] * 1e-3) / 1e9
+    result["decode_ring"] = {
+        "workload": rw.name, "B": rw.B, "T_q": rw.T_q, "capacity": rw.capacity,
+        "window": rw.window, "sink": rw.sink, "kv_len_range": list(rw.kv_len_range),
+        "ms_per_call": dring["ms"], "value": round(gbs_ring, 2), "unit": "GB/s",
+        "kv_copies_rotated": dring["n_copies"],
+        "roofline": {"bound": "hbm", "achieved": round(gbs_ring, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs_ring / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes_per_call": dring["kv_bytes"],
+                     "note": "whole call (split + combine kernels); bytes = resident keys read"},
+    }
     if not args.no_cpu:
         log("[bench] cpu oracle baseline (decode)")
         cb, o_ref, lse_ref = cpu_baseline_decode(dec["inp"], dec["kv_bytes"])
@@ -462,6 +604,10 @@ def main():
         result["parity"]["prefill_sample_max_abs_dLSE"] = float(np.abs(pre["lse_rows"] - lp).max())
         log("[bench] oracle check (prefill_kvsplit sample)")
         result["parity"].update(parity_prefill_kvsplit(kvs))
+        log("[bench] oracle check (prefill_window sample)")
+        result["parity"].update(parity_prefill_window(pwin))
+        log("[bench] oracle check (decode_ring sample)")
+        result["parity"].update(parity_decode_ring(dring))
         log("[bench] oracle check (decode_multi sample)")
         result["parity"].update(parity_decode_multi(mul))
     print(json.dumps(result), flush=True)

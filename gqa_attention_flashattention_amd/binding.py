@@ -64,6 +64,9 @@ def load_library():
     lib.gqa_attn_prefill_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, i, vp]
     lib.gqa_attn_prefill_kvsplit_count.restype = i
     lib.gqa_attn_prefill_kvsplit_count.argtypes = [i] * 9
+    lib.gqa_attn_decode_ring.restype = i
+    lib.gqa_attn_decode_ring.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, i, f, i, i,
+                                         vp]
     lib.gqa_attn_decode_multi.restype = i
     lib.gqa_attn_decode_multi.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, f, i, i, vp]
     lib.gqa_attn_decode_combine.restype = i
@@ -301,6 +304,34 @@ def decode_multi(q, k, v, kv_len, *, scale: float | None = None, num_splits: int
                                               float(scale), int(num_splits), _dtype_code(q),
                                               _stream(q.device))
     _check(rc, "gqa_attn_decode_multi")
+    return out, lse
+
+
+def decode_ring(q, k_cache, v_cache, kv_len, *, window: int, sink: int = 0,
+                scale: float | None = None, num_splits: int = 0, out=None, lse=None,
+                return_lse: bool = True):
+    """Decode over a ring-buffer cache.  q [B,T_q,H_q,d] bf16 (T_q new tokens,
+    already written); k_cache/v_cache [B,capacity,H_kv,d]; kv_len = tokens
+    written per sequence.  Returns (o [B,T_q,H_q,d], lse [B,T_q,H_q] or None)."""
+    import torch
+    _require(q, "q", 4)
+    _require(k_cache, "k_cache", 4)
+    _require(v_cache, "v_cache", 4)
+    B, T_q, H_q, d = q.shape
+    if k_cache.shape != v_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != d:
+        raise GQAError("k_cache and v_cache must be [B, capacity, H_kv, d] matching q", 2)
+    a = _kv_len_array(kv_len, B)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, T_q, H_q), dtype=torch.float32, device=q.device)
+    rc = load_library().gqa_attn_decode_ring(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), B, T_q, H_q,
+        k_cache.shape[2], d, k_cache.shape[1], a.ctypes.data, int(window), int(sink),
+        float(scale), int(num_splits), _dtype_code(q), _stream(q.device))
+    _check(rc, "gqa_attn_decode_ring")
     return out, lse
 
 

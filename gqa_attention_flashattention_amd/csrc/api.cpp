@@ -126,9 +126,12 @@ int check_decode_args(const void* q, const void* k, const void* v, int B, int H_
 
 // Split the batch into launches of at most kDecodeSeqPerLaunch sequences and
 // call fn(chunk) for each.
+// ring_cap > 0: a ring-buffer cache of ring_cap slots per sequence (sequence
+// b starts at row b * ring_cap); kv_len are then the walked key counts and
+// ntok the tokens written.
 template <typename Fn>
 int for_each_chunk(int B, const int32_t* kv_len, const int32_t* splits, const int32_t* lens,
-                   Fn fn) {
+                   Fn fn, int ring_cap = 0, const int32_t* ntok = nullptr) {
     int64_t key_off = 0, split_base = 0;
     for (int b0 = 0; b0 < B; b0 += gqa::kDecodeSeqPerLaunch) {
         DecodePlanChunk c;
@@ -139,8 +142,9 @@ int for_each_chunk(int B, const int32_t* kv_len, const int32_t* splits, const in
         c.split_base = (int)split_base;
         int units = 0;
         for (int i = 0; i < c.nseq; ++i) {
-            c.key_off[i] = key_off;
+            c.key_off[i] = ring_cap > 0 ? (int64_t)(b0 + i) * ring_cap : key_off;
             c.len[i] = kv_len[b0 + i];
+            c.ntok[i] = ntok ? ntok[b0 + i] : kv_len[b0 + i];
             c.split_len[i] = lens[b0 + i];
             c.unit_base[i] = units;
             units += splits[b0 + i];
@@ -416,6 +420,59 @@ int gqa_attn_prefill_kvsplit_count(int B, int T_q, int S_kv, int H_q, int H_kv, 
     if (B < 1 || T_q < 1 || S_kv < 1 || check_heads(H_q, H_kv, d)) return -GQA_ERR_SHAPE;
     if (causal && (q_offset < 0 || (int64_t)q_offset + T_q > S_kv)) return -GQA_ERR_RANGE;
     return prefill_splits(B, T_q, S_kv, H_q, H_kv, d, causal, causal ? q_offset : 0, num_splits);
+}
+
+int gqa_attn_decode_ring(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                         int T_q, int H_q, int H_kv, int d, int capacity, const int32_t* kv_len,
+                         int window, int sink, float scale, int num_splits, int dtype,
+                         void* stream) {
+    int rc = check_decode_args(q, k, v, B, H_q, H_kv, d, kv_len, scale, dtype);
+    if (rc) return rc;
+    if (!o) return GQA_ERR_NULL;
+    if (T_q < 1 || T_q > kMaxDecodeTokens || capacity < 1) return GQA_ERR_SHAPE;
+    // every key a new token may see must still be resident
+    if (sink < 0 || sink >= capacity || window < 1 ||
+        (int64_t)window + T_q - 1 > (int64_t)capacity - sink)
+        return GQA_ERR_RANGE;
+    int32_t* walk = (int32_t*)malloc(sizeof(int32_t) * (size_t)B);
+    if (!walk) return GQA_ERR_SHAPE;
+    for (int b = 0; b < B; ++b) {
+        const int64_t n = kv_len[b];
+        if (n < T_q) {
+            free(walk);
+            return GQA_ERR_SHAPE;
+        }
+        const int64_t s_end = n < sink ? n : sink;
+        int64_t w_lo = n - T_q - window + 1;
+        if (w_lo < s_end) w_lo = s_end;
+        walk[b] = (int32_t)(s_end + (n - w_lo));
+    }
+    HostPlan hp;
+    rc = hp.build(B, H_q, H_kv, walk, num_splits, T_q);
+    if (rc) {
+        free(walk);
+        return rc;
+    }
+    const int rows = T_q * H_q;
+    void* base = nullptr;
+    rc = get_workspace(workspace_bytes_for(hp.p.total, rows, d), &base);
+    if (rc) {
+        free(walk);
+        return rc;
+    }
+    DecodeWorkspace ws = carve(base, hp.p.total, rows);
+    const gqa::RingArgs ring{capacity, sink, window};
+    (void)hipGetLastError();
+    rc = for_each_chunk(B, walk, hp.splits, hp.lens, [&](const DecodePlanChunk& c) {
+        return gqa::launch_decode_ring_split_bf16(q, k, v, ws, c, T_q, H_q, H_kv, d, scale, ring,
+                                                  (hipStream_t)stream);
+    }, capacity, kv_len);
+    if (!rc)
+        rc = for_each_chunk(B, walk, hp.splits, hp.lens, [&](const DecodePlanChunk& c) {
+            return gqa::launch_decode_combine_bf16(ws, c, o, lse, T_q, H_q, d, (hipStream_t)stream);
+        }, capacity, kv_len);
+    free(walk);
+    return rc;
 }
 
 int gqa_attn_decode_multi(const void* q, const void* k, const void* v, void* o, float* lse,

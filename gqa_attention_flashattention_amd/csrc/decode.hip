@@ -72,15 +72,31 @@ struct WaveTile {
 // for it on the spot): keys past the split end are clamped to its last key.
 // Their scores are masked to -inf, so their P is exactly 0 and the clamped
 // (finite) K/V values do not contribute.
-template <int D>
+// Cache row of walk index kk: the identity for a packed cache; for a ring
+// cache, the sinks [0, s_end) and then the window positions, whose slots
+// start at ring offset r0 and wrap at the ring length.
+struct RowMap {
+    int s_end, sink, r0, wrap;
+    __device__ __forceinline__ int operator()(int kk) const {
+        if (kk < s_end) return kk;
+        int r = r0 + (kk - s_end);
+        r = r >= wrap ? r - wrap : r;
+        return sink + r;
+    }
+};
+struct Identity {
+    __device__ __forceinline__ int operator()(int kk) const { return kk; }
+};
+
+template <int D, typename Map>
 __device__ __forceinline__ void load_wave_tile(WaveTile<D>& w, const uint16_t* __restrict__ kseq,
                                                const uint16_t* __restrict__ vseq,
                                                int64_t row_stride, int key0, int key_end,
-                                               int lane) {
+                                               int lane, const Map& row_of) {
     const int m = lane & 15, g4 = lane >> 4;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-        const int kk = min(key0 + tile_key(m, blk), key_end - 1);
+        const int kk = row_of(min(key0 + tile_key(m, blk), key_end - 1));
 #pragma unroll
         for (int s = 0; s < WaveTile<D>::KSTEPS; ++s)
             w.kf[blk][s] = *(const u32x4*)(kseq + (int64_t)kk * row_stride + s * 32 + g4 * 8);
@@ -90,7 +106,7 @@ __device__ __forceinline__ void load_wave_tile(WaveTile<D>& w, const uint16_t* _
     const int dc = lane % CPR, kg = lane / CPR;
 #pragma unroll
     for (int e = 0; e < WaveTile<D>::KPL; ++e) {
-        const int kk = min(key0 + e * RPI + kg, key_end - 1);
+        const int kk = row_of(min(key0 + e * RPI + kg, key_end - 1));
         w.vr[e] = *(const u32x4*)(vseq + (int64_t)kk * row_stride + dc * 8);
     }
 }
@@ -113,12 +129,15 @@ __device__ __forceinline__ void wave_lds_fence() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D, int NH>
+// RING: keys come from a ring-buffer cache (see RowMap); each new token t at
+// position n - T_q + t sees the sinks and the `window` newest positions up
+// to its own, which in walk order is [0, s_end) and [wbeg_t, vend_t).
+template <int D, int NH, bool RING>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ ws_m, float* __restrict__ ws_l,
     float* __restrict__ ws_o, const DecodePlanChunk plan, int T_q, int H_q, int H_kv, int G,
-    int n_hg, float c) {
+    int n_hg, float c, RingArgs ring) {
     using SM = DecodeSmem<D>;
     constexpr int KSTEPS = WaveTile<D>::KSTEPS;
     constexpr int DBLK = D / 16;             // 16-row blocks of O^T
@@ -146,12 +165,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int kend = min(len, kbeg + L);
     const int b = plan.seq0 + sq;
     const int ncols = T_q * G;
+    // walk index <-> position: [0, s_end) are positions 0.., then w_lo.. (ring);
+    // a packed cache is the identity (s_end = w_lo = 0)
+    int s_end = 0, w_lo = 0, pos0 = len - T_q;   // pos0: position of new token 0
+    RowMap rmap{0, 0, 0, 1};
+    if (RING) {
+        const int n = plan.ntok[sq];
+        pos0 = n - T_q;
+        s_end = min(ring.sink, n);
+        w_lo = max(s_end, pos0 - ring.window + 1);
+        const int wrap = ring.capacity - ring.sink;
+        rmap = RowMap{s_end, ring.sink, w_lo >= ring.sink ? (w_lo - ring.sink) % wrap : 0, wrap};
+    }
 
     // MFMA columns: the G * T_q query rows (new token t, query head g) of a KV
     // head, in blocks of 16; this work-group takes blocks hg*NH .. hg*NH+NH-1,
     // so every K/V tile it loads serves up to 16*NH rows.
     // vis_end[h]: new token t sits at position len - T_q + t and sees keys up to it.
     int vis_end[NH];
+    int wbeg[NH];                            // ring: window part of token t starts here
     bf16x8 qf[NH][KSTEPS];
     const int64_t row_stride = (int64_t)H_kv * D;
     const uint16_t* kseq = k + (plan.key_off[sq] * H_kv + kv) * (int64_t)D;
@@ -160,7 +192,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // the first tile's K/V loads go out before anything else
     WaveTile<D> wt;
     int tt = wave;
-    if (tt < n_tiles) load_wave_tile<D>(wt, kseq, vseq, row_stride, kbeg + tt * kTile, kend, lane);
+    auto load = [&](int key0) {
+        if (RING) load_wave_tile<D>(wt, kseq, vseq, row_stride, key0, kend, lane, rmap);
+        else load_wave_tile<D>(wt, kseq, vseq, row_stride, key0, kend, lane, Identity{});
+    };
+    if (tt < n_tiles) load(kbeg + tt * kTile);
 
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
@@ -169,14 +205,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int fc = min(f, ncols - 1);
         const int tq = fc / G;
         const int hq = kv * G + fc % G;
-        vis_end[h] = min(kend, len - T_q + tq + 1);
+        const int pos = pos0 + tq;
+        if (RING) {
+            vis_end[h] = min(kend, pos < s_end ? pos + 1 : s_end + (pos - w_lo + 1));
+            wbeg[h] = s_end + max(0, pos - ring.window + 1 - w_lo);
+        } else {
+            vis_end[h] = min(kend, pos + 1);
+            wbeg[h] = 0;
+        }
         // Q^T operand: column = query row, k-group g4 = 8 dims per k-step.
         const uint16_t* qrow = q + (((int64_t)b * T_q + tq) * H_q + hq) * D + g4 * 8;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s)
             qf[h][s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + s * 32));
     }
-    const int mask_from = min(kend, len - T_q + 1);   // keys before this are visible to all
+    // walk indices before mask_from are visible to all tokens (apart from the
+    // ring window starts, all below wbeg_max)
+    const int mask_from = RING ? min(kend, pos0 < s_end ? pos0 + 1 : s_end + (pos0 - w_lo + 1))
+                               : min(kend, len - T_q + 1);
+    const int wbeg_max = RING ? s_end + max(0, pos0 + T_q - 1 - ring.window + 1 - w_lo) : 0;
     uint16_t* vt = vtiles + wave * SM::VT_ELEMS;
     // transposed-read source address: lane L of group g4 points at key row
     // g4 + 4 (L / 4) (+ 16 for the second read), dims 4 (L % 4) of each 16-dim block
@@ -209,15 +256,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         wave_lds_fence();                    // previous tile's V reads are done
         store_v<D>(wt, vt, lane);
         const int nt = tt + kWaves;
-        if (nt < n_tiles) load_wave_tile<D>(wt, kseq, vseq, row_stride, kbeg + nt * kTile, kend, lane);
-        if (key0 + kTile > mask_from) {
+        if (nt < n_tiles) load(kbeg + nt * kTile);
+        if (key0 + kTile > mask_from || (RING && key0 + kTile > s_end && key0 < wbeg_max)) {
 #pragma unroll
             for (int h = 0; h < NH; ++h)
 #pragma unroll
                 for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (key0 + g4 + 16 * blk + 4 * i >= vis_end[h]) s[h][blk][i] = -INFINITY;
+                    for (int i = 0; i < 4; ++i) {
+                        const int key = key0 + g4 + 16 * blk + 4 * i;
+                        bool hide = key >= vis_end[h];
+                        if (RING) hide = hide || (key >= s_end && key < wbeg[h]);
+                        if (hide) s[h][blk][i] = -INFINITY;
+                    }
         }
         float corr[NH];
         bf16x8 pb[NH];
@@ -388,31 +439,54 @@ int decode_column_groups(int T_q, int G) {
     return (blocks + nh - 1) / nh;
 }
 
-template <int D, int NH>
+template <int D, int NH, bool RING>
 static void launch_split(dim3 grid, const void* q, const void* k, const void* v,
                          const DecodeWorkspace& ws, const DecodePlanChunk& plan, int T_q, int H_q,
-                         int H_kv, int G, int n_hg, float c, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_split_kernel<D, NH>), grid, dim3(kThreads), 0, stream,
+                         int H_kv, int G, int n_hg, float c, const RingArgs& ring,
+                         hipStream_t stream) {
+    hipLaunchKernelGGL((decode_split_kernel<D, NH, RING>), grid, dim3(kThreads), 0, stream,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, ws.m, ws.l,
-                       ws.o, plan, T_q, H_q, H_kv, G, n_hg, c);
+                       ws.o, plan, T_q, H_q, H_kv, G, n_hg, c, ring);
+}
+
+template <bool RING>
+static hipError_t split_dispatch(const void* q, const void* k, const void* v,
+                                 const DecodeWorkspace& ws, const DecodePlanChunk& plan, int T_q,
+                                 int H_q, int H_kv, int d, float scale, const RingArgs& ring,
+                                 hipStream_t stream) {
+    const int G = H_q / H_kv;
+    const int n_hg = decode_column_groups(T_q, G);
+    const int nh = decode_column_blocks_per_group(T_q, G);
+    const int64_t grid = (int64_t)plan.units * n_hg * H_kv;
+    if (grid < 1 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (RING && (ring.sink < 0 || ring.capacity - ring.sink < 1 || ring.window < 1))
+        return hipErrorInvalidValue;
+    const float c = scale * kLog2e;
+    const dim3 g((unsigned)grid);
+    if (d == 128 && nh == 1)
+        launch_split<128, 1, RING>(g, q, k, v, ws, plan, T_q, H_q, H_kv, G, n_hg, c, ring, stream);
+    else if (d == 128)
+        launch_split<128, 2, RING>(g, q, k, v, ws, plan, T_q, H_q, H_kv, G, n_hg, c, ring, stream);
+    else if (nh == 1)
+        launch_split<64, 1, RING>(g, q, k, v, ws, plan, T_q, H_q, H_kv, G, n_hg, c, ring, stream);
+    else
+        launch_split<64, 2, RING>(g, q, k, v, ws, plan, T_q, H_q, H_kv, G, n_hg, c, ring, stream);
+    return hipGetLastError();
 }
 
 hipError_t launch_decode_split_bf16(const void* q, const void* k, const void* v,
                                     const DecodeWorkspace& ws, const DecodePlanChunk& plan,
                                     int T_q, int H_q, int H_kv, int d, float scale,
                                     hipStream_t stream) {
-    const int G = H_q / H_kv;
-    const int n_hg = decode_column_groups(T_q, G);
-    const int nh = decode_column_blocks_per_group(T_q, G);
-    const int64_t grid = (int64_t)plan.units * n_hg * H_kv;
-    if (grid < 1 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const float c = scale * kLog2e;
-    const dim3 g((unsigned)grid);
-    if (d == 128 && nh == 1) launch_split<128, 1>(g, q, k, v, ws, plan, T_q, H_q, H_kv, G, n_hg, c, stream);
-    else if (d == 128) launch_split<128, 2>(g, q, k, v, ws, plan, T_q, H_q, H_kv, G, n_hg, c, stream);
-    else if (nh == 1) launch_split<64, 1>(g, q, k, v, ws, plan, T_q, H_q, H_kv, G, n_hg, c, stream);
-    else launch_split<64, 2>(g, q, k, v, ws, plan, T_q, H_q, H_kv, G, n_hg, c, stream);
-    return hipGetLastError();
+    return split_dispatch<false>(q, k, v, ws, plan, T_q, H_q, H_kv, d, scale, RingArgs{1, 0, 1},
+                                 stream);
+}
+
+hipError_t launch_decode_ring_split_bf16(const void* q, const void* k, const void* v,
+                                         const DecodeWorkspace& ws, const DecodePlanChunk& plan,
+                                         int T_q, int H_q, int H_kv, int d, float scale,
+                                         const RingArgs& ring, hipStream_t stream) {
+    return split_dispatch<true>(q, k, v, ws, plan, T_q, H_q, H_kv, d, scale, ring, stream);
 }
 
 hipError_t launch_decode_combine_bf16(const DecodeWorkspace& ws, const DecodePlanChunk& plan,

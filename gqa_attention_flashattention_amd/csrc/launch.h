@@ -29,7 +29,8 @@ struct DecodePlanChunk {
     int split_base;                          // global split index of this launch's first split
     int units;                               // sum of splits over this launch's sequences
     int64_t key_off[kDecodeSeqPerLaunch];    // first key row of each sequence
-    int32_t len[kDecodeSeqPerLaunch];        // kv_len
+    int32_t len[kDecodeSeqPerLaunch];        // keys the kernel walks (kv_len; ring: resident visible keys)
+    int32_t ntok[kDecodeSeqPerLaunch];       // ring cache only: tokens written so far
     int32_t split_len[kDecodeSeqPerLaunch];  // L_b
     int32_t unit_base[kDecodeSeqPerLaunch + 1];  // prefix of splits within the launch
     int32_t seq0;                            // batch index of the first sequence
@@ -66,6 +67,20 @@ hipError_t launch_decode_split_bf16(const void* q, const void* k, const void* v,
                                     const DecodeWorkspace& ws, const DecodePlanChunk& plan,
                                     int T_q, int H_q, int H_kv, int d, float scale,
                                     hipStream_t stream);
+
+// Ring-buffer cache (capacity slots per sequence, key_off = b * capacity): the
+// first `sink` positions stay in slots 0..sink-1, position j >= sink lives in
+// slot sink + (j - sink) mod (capacity - sink).  The kernel walks plan.len[sq]
+// keys: the resident sinks, then the window positions in order.
+struct RingArgs {
+    int capacity;
+    int sink;
+    int window;
+};
+hipError_t launch_decode_ring_split_bf16(const void* q, const void* k, const void* v,
+                                         const DecodeWorkspace& ws, const DecodePlanChunk& plan,
+                                         int T_q, int H_q, int H_kv, int d, float scale,
+                                         const RingArgs& ring, hipStream_t stream);
 hipError_t launch_decode_combine_bf16(const DecodeWorkspace& ws, const DecodePlanChunk& plan,
                                       void* o, float* lse, int T_q, int H_q, int d,
                                       hipStream_t stream);

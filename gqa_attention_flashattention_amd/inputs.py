@@ -36,6 +36,7 @@ class Workload:
     kv_len_range: tuple | None = None   # varlen decode: (lo, hi) inclusive
     window: int = 0         # > 0: sink + local-window mask (keys j < sink or j > p - window)
     sink: int = 0
+    capacity: int = 0       # > 0: decode over a ring-buffer cache of this many slots
 
     @property
     def G(self) -> int:
@@ -62,6 +63,8 @@ WORKLOADS = {
                  T_q=256, S_kv=65792, causal=True, q_offset=65536),
         Workload("prefill_8k_window1k", "prefill", "bf16", B=1, H_q=64, H_kv=8, d=128,
                  T_q=8192, S_kv=8192, causal=True, window=1024, sink=4),
+        Workload("decode_ring_8k_b16", "decode", "bf16", B=16, H_q=64, H_kv=8, d=128,
+                 kv_len_range=(1024, 32768), capacity=8192, window=8188, sink=4),
         Workload("decode_t4_varlen_b16", "decode", "bf16", B=16, H_q=64, H_kv=8, d=128,
                  T_q=4, kv_len_range=(1024, 32768)),
     ]
@@ -109,6 +112,8 @@ def shapes(w: Workload, kv_len: np.ndarray | None):
     if w.kind == "prefill":
         return ((w.B, w.T_q, w.H_q, w.d), (w.B, w.S_kv, w.H_kv, w.d))
     total = int(np.asarray(kv_len, np.int64).sum())
+    if w.capacity > 0:     # ring-buffer cache [B, capacity, H_kv, d], kv_len = tokens written
+        return ((w.B, w.T_q, w.H_q, w.d), (w.B, w.capacity, w.H_kv, w.d))
     if w.T_q > 1:   # multi-token decode: T_q new tokens per sequence
         return ((w.B, w.T_q, w.H_q, w.d), (total, w.H_kv, w.d))
     return ((w.B, w.H_q, w.d), (total, w.H_kv, w.d))

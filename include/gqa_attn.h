@@ -217,6 +217,34 @@ int gqa_attn_decode_multi(const void *q, const void *k, const void *v, void *o, 
                           int B, int T_q, int H_q, int H_kv, int d, const int32_t *kv_len,
                           float scale, int num_splits, int dtype, void *stream);
 
+/*
+ * Decode over a hard-cap ring-buffer KV cache with attention sinks and a local
+ * window (pccx page "Gemma 3N E4B on pccx v002 -- Execution / Scheduling":
+ * KV ring buffer of max_tokens set at init, section 4: once the ring wraps,
+ * the oldest entries are overwritten under an attention-sink + local-window
+ * policy).  T_q >= 1 new tokens per sequence, already written to the cache.
+ *   k, v [B, capacity, H_kv, d] (dtype): the first `sink` positions of
+ *        sequence b stay in slots 0 .. sink-1; position j >= sink is in slot
+ *        sink + (j - sink) mod (capacity - sink), so the ring keeps the
+ *        capacity - sink newest positions.
+ *   kv_len HOST [B]: tokens written so far (positions 0 .. kv_len[b]-1; may
+ *        exceed capacity).  Requires kv_len[b] >= T_q.
+ *   q, o [B, T_q, H_q, d]; lse [B, T_q, H_q] fp32, may be NULL.
+ * New token t (position p = kv_len[b] - T_q + t) attends to key j iff j <= p
+ * and (j < sink or j > p - window), as gqa_attn_prefill_window.  Requires
+ * 0 <= sink < capacity, window >= 1 and window + T_q - 1 <= capacity - sink
+ * (every key a new token sees is still resident).  Only the resident keys
+ * that some new token sees are read; the split plan (num_splits as in
+ * gqa_attn_decode) runs over them.  Library-owned workspace as
+ * gqa_attn_decode.
+ * Errors: GQA_ERR_NULL, GQA_ERR_SHAPE, GQA_ERR_UNSUPPORTED, GQA_ERR_RANGE
+ * (sink/window/capacity), GQA_ERR_HIP.
+ */
+int gqa_attn_decode_ring(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                         int T_q, int H_q, int H_kv, int d, int capacity, const int32_t *kv_len,
+                         int window, int sink, float scale, int num_splits, int dtype,
+                         void *stream);
+
 #ifdef __cplusplus
 }
 #endif

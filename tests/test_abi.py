@@ -25,7 +25,7 @@ def test_header_declares_the_boundary():
     for n in ["gqa_attn_prefill", "gqa_attn_decode", "gqa_attn_decode_split",
               "gqa_attn_decode_combine", "gqa_attn_decode_plan", "gqa_attn_decode_multi",
               "gqa_attn_prefill_kvsplit", "gqa_attn_prefill_kvsplit_count",
-              "gqa_attn_prefill_window",
+              "gqa_attn_prefill_window", "gqa_attn_decode_ring",
               "gqa_attn_status_string", "gqa_attn_version"]:
         assert n in names
 
@@ -133,6 +133,24 @@ def test_window_prefill_rejects():
     assert lib.gqa_attn_prefill_window(*args(qoff=5)) == 4
     assert lib.gqa_attn_prefill_window(*args(window=0)) == 4
     assert lib.gqa_attn_prefill_window(*args(sink=-1)) == 4
+
+
+def test_ring_decode_rejects():
+    lib = gq.load_library()
+
+    def call(kv=(10,), **kw):
+        a = dict(q=P, o=P, T=2, cap=16, window=10, sink=4, dtype=0, d=128)
+        a.update(kw)
+        arr = np.asarray(kv, np.int32)
+        return lib.gqa_attn_decode_ring(a["q"], P, P, a["o"], None, len(kv), a["T"], 8, 2, a["d"],
+                                        a["cap"], arr.ctypes.data, a["window"], a["sink"], 0.1, 0,
+                                        a["dtype"], None)
+    assert call(q=None) == 1 and call(o=None) == 1
+    assert call(kv=(1,)) == 2                   # fewer tokens than new tokens
+    assert call(T=0) == 2 and call(cap=0) == 2
+    assert call(d=32) == 3 and call(dtype=1) == 3
+    assert call(sink=16) == 4 and call(sink=-1) == 4 and call(window=0) == 4
+    assert call(window=13) == 4                 # window + T_q - 1 > capacity - sink
 
 
 def test_split_and_combine_reject_small_workspace():
