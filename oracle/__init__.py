@@ -204,3 +204,30 @@ def decode(q, k, v, kv_len, **kw):
 def prefill_window(q, k, v, **kw):
     """See OracleLib.prefill_window."""
     return _lib().prefill_window(q, k, v, **kw)
+
+
+def unpack_int4(packed: np.ndarray) -> np.ndarray:
+    """Two's-complement int4 codes stored two per byte, channel 2i in the low
+    nibble of byte i (pccx page, section 4 item 3: optional INT4 KV cache),
+    -> int8 codes with the channel axis doubled."""
+    b = np.asarray(packed, np.uint8).astype(np.int16)
+    lo = b & 0x0F
+    hi = b >> 4
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+def dequantize(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """Symmetric per-channel dequantisation: value[j, kv, x] = code[j, kv, x] *
+    scale[kv, x] (codes int8 [N, H_kv, d], scale [H_kv, d]).  Returned as
+    float32, which must hold every product exactly (the oracle's inputs are
+    exact float32 values); raises otherwise."""
+    prod = np.asarray(codes, np.float64) * np.asarray(scale, np.float64)[None]
+    out = prod.astype(np.float32)
+    if not np.array_equal(out.astype(np.float64), prod):
+        raise ValueError("dequantised values are not exactly representable in float32")
+    return out

@@ -97,3 +97,26 @@ def test_oracle_rejects_bad_arguments():
                       np.zeros((3, 2, 8), np.float32), np.array([0], np.int32))
     with pytest.raises(ValueError):
         oracle.prefill(np.full((1, 1, 2, 2), 0.1), k[:, :, :, :2], k[:, :, :, :2], causal=False)
+
+
+def test_unpack_int4_fixed_bytes():
+    """The int4 storage rule on hand-picked bytes: low nibble = even channel,
+    two's complement (0xF = -1, 0x8 = -8, 0x7 = 7)."""
+    packed = np.array([[0x00, 0x0F, 0x8F, 0x71, 0xF8, 0x80]], np.uint8)
+    assert oracle.unpack_int4(packed).tolist() == [[0, 0, -1, 0, -1, -8, 1, 7, -8, -1, 0, -8]]
+
+
+def test_unpack_inverts_input_packing():
+    """Every code pair survives the input generator's packing and the
+    oracle's unpacking (two independently written codecs)."""
+    from gqa_attention_flashattention_amd import inputs as gin
+    a = np.array([[x, y] for x in range(-8, 8) for y in range(-8, 8)], np.int8)
+    assert np.array_equal(oracle.unpack_int4(gin.pack_int4(a)), a)
+
+
+def test_dequantize_exact_and_rejects_inexact():
+    codes = np.array([[[127, -128, 5]]], np.int8)
+    scale = np.array([[0.03125, 1.5, 0.1015625]], np.float32)   # bf16-representable
+    assert oracle.dequantize(codes, scale).tolist() == [[[3.96875, -192.0, 0.5078125]]]
+    with pytest.raises(ValueError):
+        oracle.dequantize(np.array([[[3]]], np.int8), np.array([[0.1]], np.float32))
