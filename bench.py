@@ -276,6 +276,38 @@ def bench_decode_ring(name, steps):
                 o_gpu=out.float().cpu().numpy(), lse_gpu=lse.cpu().numpy())
 
 
+def bench_decode_quant(name, steps):
+    """Quantised-cache decode over rotated copies of the code tensors."""
+    import torch
+    import gqa_attention_flashattention_amd as gq
+    from gqa_attention_flashattention_amd import inputs as gin
+    inp = gin.make_quant(name)
+    w = inp.workload
+    pack = (lambda c: c) if w.kv_bits == 8 else gin.pack_int4
+    k0 = torch.from_numpy(pack(inp.k_codes)).cuda()
+    v0 = torch.from_numpy(pack(inp.v_codes)).cuda()
+    kv_bytes = 2 * k0.numel()
+    n_copies = max(1, min(64, math.ceil(ROTATE_BYTES / kv_bytes)))
+    ks = [k0] + [k0.clone() for _ in range(n_copies - 1)]
+    vs = [v0] + [v0.clone() for _ in range(n_copies - 1)]
+    q = dev_tensor(inp.q_store)
+    ksc = torch.from_numpy(inp.k_scale).cuda()
+    vsc = torch.from_numpy(inp.v_scale).cuda()
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+
+    def call(i):
+        return lambda: gq.decode_quant(q, ks[i % n_copies], vs[i % n_copies], ksc, vsc,
+                                       inp.kv_len, kv_bits=w.kv_bits, out=out, lse=lse)
+
+    for i in range(3):
+        call(i)()
+    torch.cuda.synchronize()
+    ms = time_graph([call(i) for i in range(steps)])
+    return dict(inp=inp, ms=ms, kv_bytes=kv_bytes, n_copies=n_copies,
+                o_gpu=out.float().cpu().numpy(), lse_gpu=lse.cpu().numpy())
+
+
 def copy_calibration(mib: int):
     """A plain device-to-device copy of `mib` MiB, three times (rocprofv3
     counter runs scale FETCH_SIZE / WRITE_SIZE by what this copy reads)."""
@@ -415,6 +447,27 @@ def parity_decode_ring(dr, n_seq=2):
             "decode_ring_sample_max_abs_dLSE": float(max(el))}
 
 
+def parity_decode_quant(dq, n_seq=1):
+    """Oracle over the dequantised cache for the first n_seq sequences."""
+    import oracle
+    inp = dq["inp"]
+    w = inp.workload
+    n_keys = int(np.asarray(inp.kv_len[:n_seq], np.int64).sum())
+    k = oracle.dequantize(inp.k_codes[:n_keys], inp.k_scale)
+    v = oracle.dequantize(inp.v_codes[:n_keys], inp.v_scale)
+    eo, el = [], []
+    off = 0
+    for b, n in enumerate(np.asarray(inp.kv_len).tolist()[:n_seq]):
+        o, l = oracle.prefill(inp.q[b:b + 1], k[None, off:off + n], v[None, off:off + n],
+                              causal=True, q_offset=n - w.T_q)
+        eo.append(np.abs(dq["o_gpu"][b] - o[0]).max())
+        el.append(np.abs(dq["lse_gpu"][b] - l[0]).max())
+        off += n
+    tag = w.name
+    return {f"{tag}_sample_max_abs_dO": float(max(eo)),
+            f"{tag}_sample_max_abs_dLSE": float(max(el))}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -429,11 +482,13 @@ def main():
                     help="sink + local-window prefill workload (reported under prefill_window)")
     ap.add_argument("--ring-workload", default="decode_ring_8k_b16",
                     help="ring-buffer decode workload (reported under decode_ring)")
+    ap.add_argument("--quant-workloads", default="decode_int8_varlen_b16,decode_int4_varlen_b16",
+                    help="quantised-cache decode workloads (reported under decode_quant)")
     ap.add_argument("--multi-workload", default="decode_t4_varlen_b16",
                     help="multi-token decode workload (reported under decode_multi)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", choices=["decode", "prefill", "decode_multi", "prefill_kvsplit",
-                                       "prefill_window", "decode_ring"],
+                                       "prefill_window", "decode_ring", "decode_quant"],
                     default=None,
                     help="run one path only (profiling runs); prints a partial line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -468,6 +523,12 @@ def main():
         log(f"[bench] decode_ring {dr['ms'] * 1e3:.1f} us/call "
             f"{dr['kv_bytes'] / (dr['ms'] * 1e-3) / 1e9:.1f} GB/s")
         return
+    if args.only == "decode_quant":
+        for name in args.quant_workloads.split(","):
+            dq = bench_decode_quant(name, min(args.steps, 200))
+            log(f"[bench] {name} {dq['ms'] * 1e3:.1f} us/call "
+                f"{dq['kv_bytes'] / (dq['ms'] * 1e-3) / 1e9:.1f} GB/s")
+        return
     if args.only == "prefill_kvsplit":
         kvs = bench_prefill_kvsplit(args.kvsplit_workload, args.prefill_steps)
         log(f"[bench] prefill_kvsplit {kvs['ms'] * 1e3:.1f} us/call (plain "
@@ -501,6 +562,11 @@ def main():
     pwin = bench_prefill_window(args.window_workload, args.prefill_steps)
     log(f"[bench] decode_ring {args.ring_workload}")
     dring = bench_decode_ring(args.ring_workload, min(args.steps, 200))
+
+    dquant = []
+    for name in args.quant_workloads.split(","):
+        log(f"[bench] decode_quant {name}")
+        dquant.append(bench_decode_quant(name, min(args.steps, 200)))
 
     dw = dec["inp"].workload
     gbs = dec["kv_bytes"] / (dec["ms_call"] * 1e-3) / 1e9
@@ -591,6 +657,20 @@ def main():
                      "algorithmic_bytes_per_call": dring["kv_bytes"],
                      "note": "whole call (split + combine kernels); bytes = resident keys read"},
     }
+    result["decode_quant"] = []
+    for dq in dquant:
+        qw = dq["inp"].workload
+        gbs_q = dq["kv_bytes"] / (dq["ms"] * 1e-3) / 1e9
+        result["decode_quant"].append({
+            "workload": qw.name, "kv_bits": qw.kv_bits, "B": qw.B, "H_q": qw.H_q,
+            "H_kv": qw.H_kv, "d": qw.d, "kv_len_range": list(qw.kv_len_range),
+            "ms_per_call": dq["ms"], "value": round(gbs_q, 2), "unit": "GB/s",
+            "bf16_equivalent_GBps": round(gbs_q * 16 / qw.kv_bits, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs_q, 2), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs_q / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_call": dq["kv_bytes"],
+                         "note": "whole call; bytes = K and V codes read (scales negligible)"},
+        })
     if not args.no_cpu:
         log("[bench] cpu oracle baseline (decode)")
         cb, o_ref, lse_ref = cpu_baseline_decode(dec["inp"], dec["kv_bytes"])
@@ -608,6 +688,9 @@ def main():
         result["parity"].update(parity_prefill_window(pwin))
         log("[bench] oracle check (decode_ring sample)")
         result["parity"].update(parity_decode_ring(dring))
+        for dq in dquant:
+            log(f"[bench] oracle check ({dq['inp'].workload.name} sample)")
+            result["parity"].update(parity_decode_quant(dq))
         log("[bench] oracle check (decode_multi sample)")
         result["parity"].update(parity_decode_multi(mul))
     print(json.dumps(result), flush=True)

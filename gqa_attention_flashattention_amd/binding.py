@@ -64,6 +64,9 @@ def load_library():
     lib.gqa_attn_prefill_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, i, vp]
     lib.gqa_attn_prefill_kvsplit_count.restype = i
     lib.gqa_attn_prefill_kvsplit_count.argtypes = [i] * 9
+    lib.gqa_attn_decode_quant.restype = i
+    lib.gqa_attn_decode_quant.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp, i, f, i,
+                                          vp]
     lib.gqa_attn_decode_ring.restype = i
     lib.gqa_attn_decode_ring.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, i, f, i, i,
                                          vp]
@@ -304,6 +307,47 @@ def decode_multi(q, k, v, kv_len, *, scale: float | None = None, num_splits: int
                                               float(scale), int(num_splits), _dtype_code(q),
                                               _stream(q.device))
     _check(rc, "gqa_attn_decode_multi")
+    return out, lse
+
+
+def decode_quant(q, k_codes, v_codes, k_scale, v_scale, kv_len, *, kv_bits: int,
+                 scale: float | None = None, num_splits: int = 0, out=None, lse=None,
+                 return_lse: bool = True):
+    """Decode over a quantised cache.  q [B,T_q,H_q,d] bf16; k_codes/v_codes
+    int8 tensors [sum(kv_len), H_kv, d] (kv_bits=8) or uint8 [.., d/2] holding
+    two int4 codes per byte (kv_bits=4, even channel in the low nibble);
+    k_scale/v_scale fp32 [H_kv, d].  Returns (o, lse)."""
+    import torch
+    _require(q, "q", 4)
+    _require(k_codes, "k_codes", 3)
+    _require(v_codes, "v_codes", 3)
+    B, T_q, H_q, d = q.shape
+    width = d if kv_bits == 8 else d // 2
+    if k_codes.shape != v_codes.shape or k_codes.shape[2] != width:
+        raise GQAError(f"k/v codes must be [sum(kv_len), H_kv, {width}] bytes", 2)
+    if k_codes.element_size() != 1 or v_codes.element_size() != 1:
+        raise GQAError("k/v codes must be 1-byte tensors", 3)
+    if q.dtype != torch.bfloat16:
+        raise GQAError("q must be bf16", 3)
+    H_kv = k_codes.shape[1]
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        _require(t, name, 2)
+        if t.dtype != torch.float32 or tuple(t.shape) != (H_kv, d):
+            raise GQAError(f"{name} must be fp32 [{H_kv}, {d}]", 2)
+    a = _kv_len_array(kv_len, B)
+    if int(a.astype(np.int64).sum()) != k_codes.shape[0]:
+        raise GQAError("k/v rows must equal sum(kv_len)", 2)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, T_q, H_q), dtype=torch.float32, device=q.device)
+    rc = load_library().gqa_attn_decode_quant(
+        _ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_scale), _ptr(v_scale), _ptr(out),
+        _ptr(lse), B, T_q, H_q, H_kv, d, a.ctypes.data, int(kv_bits), float(scale),
+        int(num_splits), _stream(q.device))
+    _check(rc, "gqa_attn_decode_quant")
     return out, lse
 
 

@@ -475,6 +475,36 @@ int gqa_attn_decode_ring(const void* q, const void* k, const void* v, void* o, f
     return rc;
 }
 
+int gqa_attn_decode_quant(const void* q, const void* k, const void* v, const float* k_scale,
+                          const float* v_scale, void* o, float* lse, int B, int T_q, int H_q,
+                          int H_kv, int d, const int32_t* kv_len, int kv_bits, float scale,
+                          int num_splits, void* stream) {
+    int rc = check_decode_args(q, k, v, B, H_q, H_kv, d, kv_len, scale, GQA_BF16);
+    if (rc) return rc;
+    if (!o || !k_scale || !v_scale) return GQA_ERR_NULL;
+    if (kv_bits != 8 && kv_bits != 4) return GQA_ERR_UNSUPPORTED;
+    if (T_q < 1 || T_q > kMaxDecodeTokens) return GQA_ERR_SHAPE;
+    for (int b = 0; b < B; ++b)
+        if (kv_len[b] < T_q) return GQA_ERR_SHAPE;
+    HostPlan hp;
+    rc = hp.build(B, H_q, H_kv, kv_len, num_splits, T_q);
+    if (rc) return rc;
+    const int rows = T_q * H_q;
+    void* base = nullptr;
+    rc = get_workspace(workspace_bytes_for(hp.p.total, rows, d), &base);
+    if (rc) return rc;
+    DecodeWorkspace ws = carve(base, hp.p.total, rows);
+    (void)hipGetLastError();
+    rc = for_each_chunk(B, kv_len, hp.splits, hp.lens, [&](const DecodePlanChunk& c) {
+        return gqa::launch_decode_quant_split(q, k, v, k_scale, v_scale, kv_bits, ws, c, T_q, H_q,
+                                              H_kv, d, scale, (hipStream_t)stream);
+    });
+    if (rc) return rc;
+    return for_each_chunk(B, kv_len, hp.splits, hp.lens, [&](const DecodePlanChunk& c) {
+        return gqa::launch_decode_combine_bf16(ws, c, o, lse, T_q, H_q, d, (hipStream_t)stream);
+    });
+}
+
 int gqa_attn_decode_multi(const void* q, const void* k, const void* v, void* o, float* lse,
                           int B, int T_q, int H_q, int H_kv, int d, const int32_t* kv_len,
                           float scale, int num_splits, int dtype, void* stream) {

@@ -60,13 +60,11 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
         (__attribute__((address_space(3))) s16x4*)(p));
 }
 
-template <int D>
-struct WaveTile {
-    static constexpr int KSTEPS = D / 32;     // MFMA k-steps over the head dim
-    static constexpr int KPL = D / 16;        // V rows per lane (8 for D = 128, 4 for D = 64)
-    u32x4 kf[2][KSTEPS];                      // K A operands, two 16-key blocks
-    u32x4 vr[KPL];                            // V chunks: KPL rows x 8 dims
-};
+// Storage formats of the K/V cache.  Quantised caches hold signed integer
+// codes with one fp32 scale per (KV head, channel): K = code_k * k_scale,
+// V = code_v * v_scale.  int4 packs two codes per byte, the even channel in
+// the low nibble.
+constexpr int kKvBf16 = 0, kKvInt8 = 1, kKvInt4 = 2;
 
 // Loads are never predicated (a predicated load forces the compiler to wait
 // for it on the spot): keys past the split end are clamped to its last key.
@@ -88,40 +86,110 @@ struct Identity {
     __device__ __forceinline__ int operator()(int kk) const { return kk; }
 };
 
-template <int D, typename Map>
-__device__ __forceinline__ void load_wave_tile(WaveTile<D>& w, const uint16_t* __restrict__ kseq,
-                                               const uint16_t* __restrict__ vseq,
-                                               int64_t row_stride, int key0, int key_end,
-                                               int lane, const Map& row_of) {
-    const int m = lane & 15, g4 = lane >> 4;
+// Eight signed codes -> eight bf16 values (exact: |code| <= 128).
+__device__ __forceinline__ bf16x8 i8x8_to_bf16(uint32_t lo, uint32_t hi) {
+    bf16x8 r;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-        const int kk = row_of(min(key0 + tile_key(m, blk), key_end - 1));
-#pragma unroll
-        for (int s = 0; s < WaveTile<D>::KSTEPS; ++s)
-            w.kf[blk][s] = *(const u32x4*)(kseq + (int64_t)kk * row_stride + s * 32 + g4 * 8);
+    for (int i = 0; i < 4; ++i) {
+        r[i] = (__bf16)(float)(int)__builtin_amdgcn_sbfe(lo, 8 * i, 8);
+        r[4 + i] = (__bf16)(float)(int)__builtin_amdgcn_sbfe(hi, 8 * i, 8);
     }
-    constexpr int CPR = D / 8;                // 16-byte chunks per row
-    constexpr int RPI = 64 / CPR;             // rows per wave instruction
-    const int dc = lane % CPR, kg = lane / CPR;
+    return r;
+}
+__device__ __forceinline__ bf16x8 i4x8_to_bf16(uint32_t w) {
+    bf16x8 r;
 #pragma unroll
-    for (int e = 0; e < WaveTile<D>::KPL; ++e) {
-        const int kk = row_of(min(key0 + e * RPI + kg, key_end - 1));
-        w.vr[e] = *(const u32x4*)(vseq + (int64_t)kk * row_stride + dc * 8);
-    }
+    for (int i = 0; i < 8; ++i) r[i] = (__bf16)(float)(int)__builtin_amdgcn_sbfe(w, 4 * i, 4);
+    return r;
 }
 
-// V tile into the wave's LDS area, row-major (key rows, head dims contiguous).
-template <int D>
-__device__ __forceinline__ void store_v(const WaveTile<D>& w, uint16_t* __restrict__ vt, int lane) {
-    using SM = DecodeSmem<D>;
-    constexpr int CPR = D / 8;
-    constexpr int RPI = 64 / CPR;
-    const int dc = lane % CPR, kg = lane / CPR;
+// One wave's 32-key tile in registers.  K: the A operands of two 16-key
+// blocks (lane row m = lane % 16 of block blk holds key tile_key(m, blk));
+// V: KPL 16-byte chunks of rows, later stored to LDS as bf16 row-major.
+// bf16: k-step s of lane group g4 covers dims 32 s + 8 g4 .. + 7.  Quantised:
+// lane group g4 owns the contiguous dims g4 * D / 4 .. + D / 4 - 1 and
+// k-step s covers g4 * D / 4 + 8 s .. + 7 (one contiguous load per row); the
+// Q operand is laid out to match.
+template <int D, int KVF>
+struct WaveTile {
+    static constexpr int KSTEPS = D / 32;                        // MFMA k-steps over the head dim
+    static constexpr int ROW_BYTES = KVF == kKvBf16 ? 2 * D : KVF == kKvInt8 ? D : D / 2;
+    static constexpr int KWORDS = ROW_BYTES / 16;                // K words per lane per row
+    static constexpr int CPR = ROW_BYTES / 16;                   // 16-byte V chunks per row
+    static constexpr int RPI = 64 / CPR;                         // V rows per wave load
+    static constexpr int KPL = kTile / RPI;                      // V loads per lane
+    static constexpr int DPC = KVF == kKvBf16 ? 8 : KVF == kKvInt8 ? 16 : 32;   // dims per chunk
+    uint32_t kw[2][KWORDS];
+    u32x4 vr[KPL];
+
+    template <typename Map>
+    __device__ __forceinline__ void load(const uint8_t* __restrict__ kseq,
+                                         const uint8_t* __restrict__ vseq, int64_t row_bytes,
+                                         int key0, int key_end, int lane, const Map& row_of) {
+        const int m = lane & 15, g4 = lane >> 4;
 #pragma unroll
-    for (int e = 0; e < WaveTile<D>::KPL; ++e)
-        *(u32x4*)(vt + (e * RPI + kg) * SM::VS + dc * 8) = w.vr[e];
-}
+        for (int blk = 0; blk < 2; ++blk) {
+            const int kk = row_of(min(key0 + tile_key(m, blk), key_end - 1));
+            const uint8_t* row = kseq + (int64_t)kk * row_bytes;
+            if constexpr (KVF == kKvBf16) {
+#pragma unroll
+                for (int s = 0; s < KSTEPS; ++s) {
+                    const u32x4 x = *(const u32x4*)(row + 2 * (s * 32 + g4 * 8));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) kw[blk][4 * s + i] = x[i];
+                }
+            } else if constexpr (KWORDS >= 4) {
+#pragma unroll
+                for (int c4 = 0; c4 < KWORDS / 4; ++c4) {
+                    const u32x4 x = *(const u32x4*)(row + g4 * (ROW_BYTES / 4) + 16 * c4);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) kw[blk][4 * c4 + i] = x[i];
+                }
+            } else {
+                const u32x2 x = *(const u32x2*)(row + g4 * (ROW_BYTES / 4));
+                kw[blk][0] = x[0];
+                kw[blk][1] = x[1];
+            }
+        }
+        const int dc = lane % CPR, kg = lane / CPR;
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) {
+            const int kk = row_of(min(key0 + e * RPI + kg, key_end - 1));
+            vr[e] = *(const u32x4*)(vseq + (int64_t)kk * row_bytes + dc * 16);
+        }
+    }
+
+    __device__ __forceinline__ bf16x8 k_operand(int blk, int s) const {
+        if constexpr (KVF == kKvBf16) {
+            const u32x4 x = {kw[blk][4 * s], kw[blk][4 * s + 1], kw[blk][4 * s + 2],
+                             kw[blk][4 * s + 3]};
+            return __builtin_bit_cast(bf16x8, x);
+        } else if constexpr (KVF == kKvInt8) {
+            return i8x8_to_bf16(kw[blk][2 * s], kw[blk][2 * s + 1]);
+        } else {
+            return i4x8_to_bf16(kw[blk][s]);
+        }
+    }
+
+    // V tile into the wave's LDS area as bf16, row-major (key rows, head dims contiguous).
+    __device__ __forceinline__ void store_v(uint16_t* __restrict__ vt, int lane) const {
+        using SM = DecodeSmem<D>;
+        const int dc = lane % CPR, kg = lane / CPR;
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) {
+            uint16_t* dst = vt + (e * RPI + kg) * SM::VS + dc * DPC;
+            if constexpr (KVF == kKvBf16) {
+                *(u32x4*)dst = vr[e];
+            } else if constexpr (KVF == kKvInt8) {
+                *(bf16x8*)dst = i8x8_to_bf16(vr[e][0], vr[e][1]);
+                *(bf16x8*)(dst + 8) = i8x8_to_bf16(vr[e][2], vr[e][3]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) *(bf16x8*)(dst + 8 * i) = i4x8_to_bf16(vr[e][i]);
+            }
+        }
+    }
+};
 
 __device__ __forceinline__ void wave_lds_fence() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -132,14 +200,22 @@ __device__ __forceinline__ void wave_lds_fence() {
 // RING: keys come from a ring-buffer cache (see RowMap); each new token t at
 // position n - T_q + t sees the sinks and the `window` newest positions up
 // to its own, which in walk order is [0, s_end) and [wbeg_t, vend_t).
-template <int D, int NH, bool RING>
+// KVF: cache storage format.  For a quantised cache the K scale of each
+// channel is folded into Q (q' = q * k_scale, split into a bf16 high and low
+// part so the fold loses nothing: two MFMAs per k-step against the exact
+// bf16 image of the codes), and the V scale multiplies the partial O once,
+// since O[x] = v_scale[x] * sum_j p_j code_v[j, x].
+template <int D, int NH, bool RING, int KVF>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, float* __restrict__ ws_m, float* __restrict__ ws_l,
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ k,
+    const uint8_t* __restrict__ v, float* __restrict__ ws_m, float* __restrict__ ws_l,
     float* __restrict__ ws_o, const DecodePlanChunk plan, int T_q, int H_q, int H_kv, int G,
-    int n_hg, float c, RingArgs ring) {
+    int n_hg, float c, RingArgs ring, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale) {
     using SM = DecodeSmem<D>;
-    constexpr int KSTEPS = WaveTile<D>::KSTEPS;
+    using WT = WaveTile<D, KVF>;
+    constexpr bool QUANT = KVF != kKvBf16;
+    constexpr int KSTEPS = WT::KSTEPS;
     constexpr int DBLK = D / 16;             // 16-row blocks of O^T
     constexpr int WSTRIDE = kCols * (D + 2);        // per wave: O [16][D], then m[16], l[16]
     __shared__ __attribute__((aligned(16))) uint16_t vtiles[kWaves * SM::VT_ELEMS];
@@ -185,16 +261,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     int vis_end[NH];
     int wbeg[NH];                            // ring: window part of token t starts here
     bf16x8 qf[NH][KSTEPS];
-    const int64_t row_stride = (int64_t)H_kv * D;
-    const uint16_t* kseq = k + (plan.key_off[sq] * H_kv + kv) * (int64_t)D;
-    const uint16_t* vseq = v + (plan.key_off[sq] * H_kv + kv) * (int64_t)D;
+    bf16x8 qlo[QUANT ? NH : 1][QUANT ? KSTEPS : 1];   // low part of q * k_scale
+    const int64_t row_bytes = (int64_t)H_kv * WT::ROW_BYTES;
+    const uint8_t* kseq = k + plan.key_off[sq] * row_bytes + (int64_t)kv * WT::ROW_BYTES;
+    const uint8_t* vseq = v + plan.key_off[sq] * row_bytes + (int64_t)kv * WT::ROW_BYTES;
     const int n_tiles = (kend - kbeg + kTile - 1) / kTile;
     // the first tile's K/V loads go out before anything else
-    WaveTile<D> wt;
+    WT wt;
     int tt = wave;
     auto load = [&](int key0) {
-        if (RING) load_wave_tile<D>(wt, kseq, vseq, row_stride, key0, kend, lane, rmap);
-        else load_wave_tile<D>(wt, kseq, vseq, row_stride, key0, kend, lane, Identity{});
+        if (RING) wt.load(kseq, vseq, row_bytes, key0, kend, lane, rmap);
+        else wt.load(kseq, vseq, row_bytes, key0, kend, lane, Identity{});
     };
     if (tt < n_tiles) load(kbeg + tt * kTile);
 
@@ -213,11 +290,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             vis_end[h] = min(kend, pos + 1);
             wbeg[h] = 0;
         }
-        // Q^T operand: column = query row, k-group g4 = 8 dims per k-step.
-        const uint16_t* qrow = q + (((int64_t)b * T_q + tq) * H_q + hq) * D + g4 * 8;
+        // Q^T operand: column = query row, k-group g4 = 8 dims per k-step
+        // (the same dims as the K operand of that k-step).
+        if constexpr (!QUANT) {
+            const uint16_t* qrow = q + (((int64_t)b * T_q + tq) * H_q + hq) * D + g4 * 8;
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s)
-            qf[h][s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + s * 32));
+            for (int s = 0; s < KSTEPS; ++s)
+                qf[h][s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + s * 32));
+        } else {
+            const int d0 = g4 * (D / 4);
+            const uint16_t* qrow = q + (((int64_t)b * T_q + tq) * H_q + hq) * D + d0;
+            const float* ks = k_scale + (int64_t)kv * D + d0;
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s) {
+                const bf16x8 raw = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 8 * s));
+                const f32x4 s0 = *(const f32x4*)(ks + 8 * s);
+                const f32x4 s1 = *(const f32x4*)(ks + 8 * s + 4);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float qs = (float)raw[i] * (i < 4 ? s0[i] : s1[i - 4]);
+                    const __bf16 hi = (__bf16)qs;
+                    qf[h][s][i] = hi;
+                    qlo[h][s][i] = (__bf16)(qs - (float)hi);
+                }
+            }
+        }
     }
     // walk indices before mask_from are visible to all tokens (apart from the
     // ring window starts, all below wbeg_max)
@@ -249,12 +346,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             for (int blk = 0; blk < 2; ++blk) {
                 s[h][blk] = f32x4{};
 #pragma unroll
-                for (int ks = 0; ks < KSTEPS; ++ks)
-                    s[h][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, wt.kf[blk][ks]), qf[h][ks], s[h][blk], 0, 0, 0);
+                for (int ks = 0; ks < KSTEPS; ++ks) {
+                    const bf16x8 ka = wt.k_operand(blk, ks);
+                    s[h][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[h][ks], s[h][blk],
+                                                                         0, 0, 0);
+                    if constexpr (QUANT)
+                        s[h][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qlo[h][ks],
+                                                                             s[h][blk], 0, 0, 0);
+                }
             }
         wave_lds_fence();                    // previous tile's V reads are done
-        store_v<D>(wt, vt, lane);
+        wt.store_v(vt, lane);
         const int nt = tt + kWaves;
         if (nt < n_tiles) load(kbeg + nt * kTile);
         if (key0 + kTile > mask_from || (RING && key0 + kTile > s_end && key0 < wbeg_max)) {
@@ -344,6 +446,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 acc += sc * *(const f32x4*)(base + cc * D + x);
                 lsum += sc * base[kCols * D + kCols + cc];
             }
+            if constexpr (QUANT) acc *= *(const f32x4*)(v_scale + (int64_t)kv * D + x);
             // partial row: (split, new token, query head)
             const int64_t hrow = (pidx * T_q + fo / G) * H_q + (int64_t)kv * G + fo % G;
             *(f32x4*)(ws_o + hrow * D + x) = acc;
@@ -439,21 +542,26 @@ int decode_column_groups(int T_q, int G) {
     return (blocks + nh - 1) / nh;
 }
 
-template <int D, int NH, bool RING>
+struct KvScales {
+    const float* k = nullptr;
+    const float* v = nullptr;
+};
+
+template <int D, int NH, bool RING, int KVF>
 static void launch_split(dim3 grid, const void* q, const void* k, const void* v,
                          const DecodeWorkspace& ws, const DecodePlanChunk& plan, int T_q, int H_q,
                          int H_kv, int G, int n_hg, float c, const RingArgs& ring,
-                         hipStream_t stream) {
-    hipLaunchKernelGGL((decode_split_kernel<D, NH, RING>), grid, dim3(kThreads), 0, stream,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, ws.m, ws.l,
-                       ws.o, plan, T_q, H_q, H_kv, G, n_hg, c, ring);
+                         const KvScales& sc, hipStream_t stream) {
+    hipLaunchKernelGGL((decode_split_kernel<D, NH, RING, KVF>), grid, dim3(kThreads), 0, stream,
+                       (const uint16_t*)q, (const uint8_t*)k, (const uint8_t*)v, ws.m, ws.l,
+                       ws.o, plan, T_q, H_q, H_kv, G, n_hg, c, ring, sc.k, sc.v);
 }
 
-template <bool RING>
+template <bool RING, int KVF = kKvBf16>
 static hipError_t split_dispatch(const void* q, const void* k, const void* v,
                                  const DecodeWorkspace& ws, const DecodePlanChunk& plan, int T_q,
                                  int H_q, int H_kv, int d, float scale, const RingArgs& ring,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, const KvScales& sc = KvScales{}) {
     const int G = H_q / H_kv;
     const int n_hg = decode_column_groups(T_q, G);
     const int nh = decode_column_blocks_per_group(T_q, G);
@@ -464,13 +572,13 @@ static hipError_t split_dispatch(const void* q, const void* k, const void* v,
     const float c = scale * kLog2e;
     const dim3 g((unsigned)grid);
     if (d == 128 && nh == 1)
-        launch_split<128, 1, RING>(g, q, k, v, ws, plan, T_q, H_q, H_kv, G, n_hg, c, ring, stream);
+        launch_split<128, 1, RING, KVF>(g, q, k, v, ws, plan, T_q, H_q, H_kv, G, n_hg, c, ring, sc, stream);
     else if (d == 128)
-        launch_split<128, 2, RING>(g, q, k, v, ws, plan, T_q, H_q, H_kv, G, n_hg, c, ring, stream);
+        launch_split<128, 2, RING, KVF>(g, q, k, v, ws, plan, T_q, H_q, H_kv, G, n_hg, c, ring, sc, stream);
     else if (nh == 1)
-        launch_split<64, 1, RING>(g, q, k, v, ws, plan, T_q, H_q, H_kv, G, n_hg, c, ring, stream);
+        launch_split<64, 1, RING, KVF>(g, q, k, v, ws, plan, T_q, H_q, H_kv, G, n_hg, c, ring, sc, stream);
     else
-        launch_split<64, 2, RING>(g, q, k, v, ws, plan, T_q, H_q, H_kv, G, n_hg, c, ring, stream);
+        launch_split<64, 2, RING, KVF>(g, q, k, v, ws, plan, T_q, H_q, H_kv, G, n_hg, c, ring, sc, stream);
     return hipGetLastError();
 }
 
@@ -480,6 +588,22 @@ hipError_t launch_decode_split_bf16(const void* q, const void* k, const void* v,
                                     hipStream_t stream) {
     return split_dispatch<false>(q, k, v, ws, plan, T_q, H_q, H_kv, d, scale, RingArgs{1, 0, 1},
                                  stream);
+}
+
+hipError_t launch_decode_quant_split(const void* q, const void* k, const void* v,
+                                     const float* k_scale, const float* v_scale, int bits,
+                                     const DecodeWorkspace& ws, const DecodePlanChunk& plan,
+                                     int T_q, int H_q, int H_kv, int d, float scale,
+                                     hipStream_t stream) {
+    const KvScales sc{k_scale, v_scale};
+    const RingArgs none{1, 0, 1};
+    if (bits == 8)
+        return split_dispatch<false, kKvInt8>(q, k, v, ws, plan, T_q, H_q, H_kv, d, scale, none,
+                                              stream, sc);
+    if (bits == 4)
+        return split_dispatch<false, kKvInt4>(q, k, v, ws, plan, T_q, H_q, H_kv, d, scale, none,
+                                              stream, sc);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode_ring_split_bf16(const void* q, const void* k, const void* v,

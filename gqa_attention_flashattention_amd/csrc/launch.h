@@ -68,6 +68,15 @@ hipError_t launch_decode_split_bf16(const void* q, const void* k, const void* v,
                                     int T_q, int H_q, int H_kv, int d, float scale,
                                     hipStream_t stream);
 
+// Quantised cache (bits = 8 or 4): k, v packed [sum kv_len, H_kv, d] signed
+// int8 codes, or int4 codes two per byte (even channel in the low nibble);
+// k_scale, v_scale fp32 [H_kv, d]; the value is code * scale.
+hipError_t launch_decode_quant_split(const void* q, const void* k, const void* v,
+                                     const float* k_scale, const float* v_scale, int bits,
+                                     const DecodeWorkspace& ws, const DecodePlanChunk& plan,
+                                     int T_q, int H_q, int H_kv, int d, float scale,
+                                     hipStream_t stream);
+
 // Ring-buffer cache (capacity slots per sequence, key_off = b * capacity): the
 // first `sink` positions stay in slots 0..sink-1, position j >= sink lives in
 // slot sink + (j - sink) mod (capacity - sink).  The kernel walks plan.len[sq]

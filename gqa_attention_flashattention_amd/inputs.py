@@ -37,6 +37,7 @@ class Workload:
     window: int = 0         # > 0: sink + local-window mask (keys j < sink or j > p - window)
     sink: int = 0
     capacity: int = 0       # > 0: decode over a ring-buffer cache of this many slots
+    kv_bits: int = 16       # 8 / 4: quantised K/V codes with per-channel scales
 
     @property
     def G(self) -> int:
@@ -65,6 +66,10 @@ WORKLOADS = {
                  T_q=8192, S_kv=8192, causal=True, window=1024, sink=4),
         Workload("decode_ring_8k_b16", "decode", "bf16", B=16, H_q=64, H_kv=8, d=128,
                  kv_len_range=(1024, 32768), capacity=8192, window=8188, sink=4),
+        Workload("decode_int8_varlen_b16", "decode", "bf16", B=16, H_q=64, H_kv=8, d=128,
+                 kv_len_range=(1024, 32768), kv_bits=8),
+        Workload("decode_int4_varlen_b16", "decode", "bf16", B=16, H_q=64, H_kv=8, d=128,
+                 kv_len_range=(1024, 32768), kv_bits=4),
         Workload("decode_t4_varlen_b16", "decode", "bf16", B=16, H_q=64, H_kv=8, d=128,
                  T_q=4, kv_len_range=(1024, 32768)),
     ]
@@ -152,3 +157,63 @@ def random_case(kind: str, dtype: str, *, B: int, H_q: int, H_kv: int, d: int, T
         return Inputs(w, bf16_bits_to_f32(qb), bf16_bits_to_f32(kb), bf16_bits_to_f32(vb),
                       qb, kb, vb, kv_len)
     return Inputs(w, q, k, v, q, k, v, kv_len)
+
+
+@dataclasses.dataclass
+class QuantInputs:
+    """A quantised-cache decode case: bf16 queries, integer K/V codes and
+    per-(KV head, channel) scales.  Codes are int8 [N, H_kv, d] (kv_bits 8)
+    or unpacked int4 values in int8 [N, H_kv, d] (kv_bits 4; ``pack_int4``
+    gives the two-per-byte storage).  Scales are bfloat16-representable fp32,
+    so that code * scale is exact in float32."""
+    workload: Workload
+    q: np.ndarray
+    q_store: np.ndarray
+    k_codes: np.ndarray
+    v_codes: np.ndarray
+    k_scale: np.ndarray
+    v_scale: np.ndarray
+    kv_len: np.ndarray
+
+
+def quant_case(*, B: int, H_q: int, H_kv: int, d: int, kv_len, kv_bits: int, T_q: int = 1,
+               seed: int = 0, name: str = "custom") -> QuantInputs:
+    """Seeded quantised-cache case.  Draw order: kv_len (if a range workload
+    drew it), Q, K codes, V codes, K scales, V scales.  Codes are rounded
+    normals clipped to the code range (sigma = 127/4 for int8, 7/3 for int4);
+    scales are bf16(uniform(0.5, 1.5) * 4/127) or bf16(uniform(0.5, 1.5) * 3/7),
+    so values are roughly standard normal."""
+    rng = np.random.default_rng(seed)
+    return _quant_draw(rng, Workload(name, "decode", "bf16", B=B, H_q=H_q, H_kv=H_kv, d=d,
+                                     T_q=T_q, kv_bits=kv_bits), np.asarray(kv_len, np.int32))
+
+
+def _quant_draw(rng, w: Workload, kv_len: np.ndarray) -> QuantInputs:
+    total = int(kv_len.astype(np.int64).sum())
+    qs = (w.B, w.T_q, w.H_q, w.d)
+    q = rng.standard_normal(qs, dtype=np.float32)
+    lo, hi, sigma, unit = (-128, 127, 127 / 4, 4 / 127) if w.kv_bits == 8 else (-8, 7, 7 / 3, 3 / 7)
+    codes = []
+    for _ in range(2):
+        c = np.rint(rng.standard_normal((total, w.H_kv, w.d)) * sigma)
+        codes.append(np.clip(c, lo, hi).astype(np.int8))
+    scales = []
+    for _ in range(2):
+        sc = (rng.uniform(0.5, 1.5, size=(w.H_kv, w.d)) * unit).astype(np.float32)
+        scales.append(bf16_bits_to_f32(bf16_round_bits(sc)))
+    qb = bf16_round_bits(q)
+    return QuantInputs(w, bf16_bits_to_f32(qb), qb, codes[0], codes[1], scales[0], scales[1],
+                       kv_len)
+
+
+def make_quant(name: str, seed: int = 0) -> QuantInputs:
+    w = WORKLOADS[name]
+    rng = np.random.default_rng(seed)
+    return _quant_draw(rng, w, kv_lengths(w, rng))
+
+
+def pack_int4(codes: np.ndarray) -> np.ndarray:
+    """int4 codes int8 [..., d] in [-8, 7] -> uint8 [..., d/2], channel 2i in
+    the low nibble of byte i (two's complement nibbles)."""
+    u = codes.astype(np.uint8) & np.uint8(0x0F)
+    return (u[..., 0::2] | (u[..., 1::2] << np.uint8(4))).astype(np.uint8)

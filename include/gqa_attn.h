@@ -218,6 +218,30 @@ int gqa_attn_decode_multi(const void *q, const void *k, const void *v, void *o, 
                           float scale, int num_splits, int dtype, void *stream);
 
 /*
+ * Decode over a quantised KV cache (pccx page "Gemma 3N E4B on pccx v002 --
+ * Execution / Scheduling", section 4 item 3: optional INT4 / INT8 KV cache,
+ * the default for long contexts; section 6: INT4 KV cache in the base
+ * configuration).  Symmetric per-channel quantisation: the value of K at
+ * (key j, KV head kv, channel x) is code_k[j, kv, x] * k_scale[kv, x], and
+ * likewise for V with v_scale.
+ *   k, v packed [sum_b kv_len[b], H_kv, d] codes (same packing as
+ *        gqa_attn_decode): kv_bits = 8: int8 in [-128, 127], one byte per
+ *        channel; kv_bits = 4: two's-complement int4 in [-8, 7], two per byte,
+ *        channel 2i in the low nibble of byte i.
+ *   k_scale, v_scale fp32 [H_kv, d] (device).
+ *   q, o [B, T_q, H_q, d] bf16; lse [B, T_q, H_q] fp32, may be NULL.
+ * T_q new tokens per sequence with the causal rule of gqa_attn_decode_multi
+ * (T_q = 1: plain decode).  The result is attention over the dequantised
+ * K and V; fp32 accumulation as gqa_attn_decode.  Library-owned workspace.
+ * Errors: GQA_ERR_NULL, GQA_ERR_SHAPE, GQA_ERR_UNSUPPORTED (kv_bits, d),
+ * GQA_ERR_RANGE, GQA_ERR_HIP.
+ */
+int gqa_attn_decode_quant(const void *q, const void *k, const void *v, const float *k_scale,
+                          const float *v_scale, void *o, float *lse, int B, int T_q, int H_q,
+                          int H_kv, int d, const int32_t *kv_len, int kv_bits, float scale,
+                          int num_splits, void *stream);
+
+/*
  * Decode over a hard-cap ring-buffer KV cache with attention sinks and a local
  * window (pccx page "Gemma 3N E4B on pccx v002 -- Execution / Scheduling":
  * KV ring buffer of max_tokens set at init, section 4: once the ring wraps,

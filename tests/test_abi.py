@@ -25,7 +25,7 @@ def test_header_declares_the_boundary():
     for n in ["gqa_attn_prefill", "gqa_attn_decode", "gqa_attn_decode_split",
               "gqa_attn_decode_combine", "gqa_attn_decode_plan", "gqa_attn_decode_multi",
               "gqa_attn_prefill_kvsplit", "gqa_attn_prefill_kvsplit_count",
-              "gqa_attn_prefill_window", "gqa_attn_decode_ring",
+              "gqa_attn_prefill_window", "gqa_attn_decode_ring", "gqa_attn_decode_quant",
               "gqa_attn_status_string", "gqa_attn_version"]:
         assert n in names
 
@@ -151,6 +151,21 @@ def test_ring_decode_rejects():
     assert call(d=32) == 3 and call(dtype=1) == 3
     assert call(sink=16) == 4 and call(sink=-1) == 4 and call(window=0) == 4
     assert call(window=13) == 4                 # window + T_q - 1 > capacity - sink
+
+
+def test_quant_decode_rejects():
+    lib = gq.load_library()
+
+    def call(kv=(10,), **kw):
+        a = dict(q=P, o=P, ks=P, vs=P, T=1, bits=8, d=128)
+        a.update(kw)
+        arr = np.asarray(kv, np.int32)
+        return lib.gqa_attn_decode_quant(a["q"], P, P, a["ks"], a["vs"], a["o"], None, len(kv),
+                                         a["T"], 8, 2, a["d"], arr.ctypes.data, a["bits"], 0.1, 0,
+                                         None)
+    assert call(q=None) == 1 and call(o=None) == 1 and call(ks=None) == 1 and call(vs=None) == 1
+    assert call(bits=2) == 3 and call(bits=16) == 3 and call(d=32) == 3
+    assert call(T=0) == 2 and call(kv=(1,), T=2) == 2 and call(kv=(0,)) == 2
 
 
 def test_split_and_combine_reject_small_workspace():
