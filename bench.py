@@ -321,17 +321,33 @@ def copy_calibration(mib: int):
     del src, dst
 
 
-def traffic_record(kernel: str):
-    """HBM bytes per dispatch of `kernel` from profiles/traffic.json, or None
-    when absent or measured on a different kernel source."""
+def traffic_record(kernel: str, grid: int):
+    """HBM bytes per dispatch of `kernel` launched with `grid` threads, from
+    profiles/traffic.json, or None when absent or measured on a different
+    kernel source."""
     from gqa_attention_flashattention_amd import profile_summary as ps
     path = ps.TRAFFIC_JSON
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path)).get(kernel)
+    rec = json.load(open(path)).get(f"{kernel}@{grid}")
     if not rec or rec.get("source_sha256") != ps.source_sha(kernel):
         return None
     return rec["bytes_per_dispatch"]
+
+
+# Launch geometry of the two headline kernels (threads per grid), to match
+# rocprofv3 records: the decode split kernel runs 256 threads per (split, KV
+# head) at G * T_q <= 16; the prefill kernel 512 threads per 256-row block.
+DECODE_SPLIT_KERNEL = "decode_split_kernel<128,1,false,0>"
+PREFILL_KERNEL = "prefill_bf16_kernel<128,1,false>"
+
+
+def decode_split_grid(plan, w):
+    return int(plan["total_splits"]) * w.H_kv * 256
+
+
+def prefill_grid(w):
+    return -(-w.T_q * w.G // 256) * w.B * w.H_kv * 512
 
 
 def cpu_threads():
@@ -593,20 +609,24 @@ def main():
                    "kv_copies_rotated": dec["n_copies"], "timed_via": "hip graph replay"},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "hot_cache_GBps": round(dec["kv_bytes"] / (dec["ms_hot"] * 1e-3) / 1e9, 2),
-        "roofline": {"bound": "hbm", "kernel": "decode_split_kernel<128>",
+        "roofline": {"bound": "hbm", "kernel": DECODE_SPLIT_KERNEL,
+                     "grid_threads": decode_split_grid(dec["plan"], dw),
                      "achieved": round(gbs_split, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs_split / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_record("decode_split_kernel<128>"),
+                     "traffic": traffic_record(DECODE_SPLIT_KERNEL,
+                                               decode_split_grid(dec["plan"], dw)),
                      "algorithmic_bytes_per_launch": dec["kv_bytes"],
                      "avg_launch_us": round(dec["ms_split"] * 1e3, 3)},
         "prefill": {
             "workload": pw.name, "T_q": pw.T_q, "S_kv": pw.S_kv, "q_offset": pw.q_offset,
             "causal": pw.causal, "ms_per_call": pre["ms"], "value": round(tflops, 2),
             "unit": "TFLOP/s",
-            "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel<128,true>",
+            "roofline": {"bound": "mfma", "kernel": PREFILL_KERNEL,
+                         "grid_threads": prefill_grid(pw),
                          "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "traffic": traffic_record("prefill_bf16_kernel<128,true>"), "algorithmic_flops_per_launch": pre["flops"],
+                         "traffic": traffic_record(PREFILL_KERNEL, prefill_grid(pw)),
+                         "algorithmic_flops_per_launch": pre["flops"],
                          "avg_launch_us": round(pre["ms"] * 1e3, 3)},
         },
     }

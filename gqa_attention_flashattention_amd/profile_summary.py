@@ -2,15 +2,17 @@
 
     python -m gqa_attention_flashattention_amd.profile_summary trace <results.db> --title T --cmd C
         per-kernel dispatch count and duration statistics from a
-        `rocprofv3 --kernel-trace` database (markdown table on stdout)
+        `rocprofv3 --kernel-trace` database (markdown table on stdout), one
+        row per (kernel, grid size): one kernel serves several workloads
     python -m gqa_attention_flashattention_amd.profile_summary traffic \
             --fetch <dir> --write <dir> --cmd-fetch C1 --cmd-write C2 --copy-mib N
         FETCH_SIZE / WRITE_SIZE per dispatch from two `rocprofv3 --pmc` runs,
         each scaled by what the same counter reads for the plain device copy of
         N MiB that `bench.py --copy-calibration N` runs first; writes a
-        markdown table on stdout and updates profiles/traffic.json, which
-        bench.py reports as `roofline.traffic` while the kernel source it was
-        measured on is unchanged (sha256 recorded per kernel).
+        markdown table on stdout and updates profiles/traffic.json (keyed
+        "kernel@grid threads"), which bench.py reports as `roofline.traffic`
+        while the kernel source it was measured on is unchanged (sha256
+        recorded per kernel).
 """
 from __future__ import annotations
 
@@ -56,18 +58,18 @@ def source_sha(kernel_short: str) -> str | None:
 
 def trace_table(db_path: str) -> list[tuple]:
     db = sqlite3.connect(db_path)
-    rows = db.execute("select name, duration from kernels").fetchall()
+    rows = db.execute("select name, grid_x * grid_y * grid_z, duration from kernels").fetchall()
     agg = collections.defaultdict(list)
-    for name, dur in rows:
-        agg[short_name(name)].append(dur / 1e3)
+    for name, grid, dur in rows:
+        agg[(short_name(name), int(grid))].append(dur / 1e3)
     out = []
-    for k, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
-        out.append((k, len(v), statistics.mean(v), statistics.median(v), min(v), max(v)))
+    for (k, g), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        out.append((k, g, len(v), statistics.mean(v), statistics.median(v), min(v), max(v)))
     return out
 
 
 def counters(run_dir: str) -> dict:
-    """{kernel short name: {counter: [value per dispatch]}}"""
+    """{"kernel short name@grid threads": {counter: [value per dispatch]}}"""
     files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
     if not files:
         raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
@@ -77,7 +79,7 @@ def counters(run_dir: str) -> dict:
         for r in csv.DictReader(open(f)):
             key = (r["Dispatch_Id"], r["Counter_Name"])
             per[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
-            names[r["Dispatch_Id"]] = short_name(r["Kernel_Name"])
+            names[r["Dispatch_Id"]] = f'{short_name(r["Kernel_Name"])}@{int(r["Grid_Size"])}'
     out = collections.defaultdict(lambda: collections.defaultdict(list))
     for d, cs in per.items():
         for c, v in cs.items():
@@ -105,10 +107,12 @@ def main():
         print(f"# {args.title}\n")
         if args.cmd:
             print(f"Command:\n\n    {args.cmd}\n")
-        print("| kernel | dispatches | avg us | median us | min us | max us |")
-        print("|---|---|---|---|---|---|")
-        for k, n, a, m, lo, hi in trace_table(args.db):
-            print(f"| `{k}` | {n} | {a:.2f} | {m:.2f} | {lo:.2f} | {hi:.2f} |")
+        print("| kernel | grid threads | dispatches | avg us | median us | min us | max us |")
+        print("|---|---|---|---|---|---|---|")
+        for k, g, n, a, m, lo, hi in trace_table(args.db):
+            if len(k) > 90:
+                k = k[:87] + "..."
+            print(f"| `{k}` | {g} | {n} | {a:.2f} | {m:.2f} | {lo:.2f} | {hi:.2f} |")
         return
 
     fetch = counters(args.fetch)
@@ -144,7 +148,8 @@ def main():
             continue
         fm, wm = statistics.median(fv), statistics.median(wv)
         scaled = (fm * f_scale + wm * w_scale) * 1024.0
-        print(f"| `{k}` | {len(fv)} | {fm:.0f} | {wm:.0f} | {scaled:.4g} |")
+        shown = k if len(k) <= 90 else k[:87] + "..."
+        print(f"| `{shown}` | {len(fv)} | {fm:.0f} | {wm:.0f} | {scaled:.4g} |")
         sha = source_sha(k)
         if sha:
             record[k] = {"fetch_kib": fm, "write_kib": wm, "fetch_scale": f_scale,
