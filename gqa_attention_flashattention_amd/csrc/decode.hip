@@ -532,14 +532,268 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
         lse[(int64_t)b * R + r] = (m + fast_log2(l)) * kLn2;
 }
 
+// ---------------------------------------------------------------------------
+// Wide variant for many query rows per KV head (G * T_q > 32, e.g. multi-token
+// decode): the four waves of a work-group split the column blocks instead of
+// the keys.  Every 128-key K/V tile of the split is loaded into LDS once per
+// work-group (each thread moves eight 16-byte chunks of K and eight of V at
+// D = 128; the next tile's loads are in flight in registers while a tile is
+// computed, in four 32-key parts) and each
+// wave reads it for its own NHW blocks of 16 query rows, so the tile feeds up
+// to 4 * NHW * 16 rows; each wave keeps the softmax state of its rows over the
+// whole split and writes its partials itself (no cross-wave merge).  K rows in
+// LDS: 16-byte chunk c of row r at chunk position c ^ swz(r) (the A-operand
+// reads of 16 rows x one chunk are then bank-conflict free); V rows
+// row-major at stride VS as in the split kernel.
+
+constexpr int kWideWaves = 4;
+
+// Chunk permutation of K row r: distinct modulo 8 over the 8 rows that eight
+// consecutive lanes read together, and below the chunks per row (16 at
+// D = 128, 8 at D = 64).
+template <int D>
+__device__ __forceinline__ int wide_swz(int r) {
+    const int f = ((r & 3) << 2) | ((r >> 2) & 3);
+    return D == 128 ? f : (f & 7);
+}
+
+template <int D, int NHW>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_wide_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, float* __restrict__ ws_m, float* __restrict__ ws_l,
+    float* __restrict__ ws_o, const DecodePlanChunk plan, int T_q, int H_q, int H_kv, int G,
+    int n_hg, float c) {
+    using SM = DecodeSmem<D>;
+    constexpr int KSTEPS = D / 32;
+    constexpr int DBLK = D / 16;
+    constexpr int CPR = D / 8;                    // 16-byte chunks per row
+    constexpr int NSUB = 4;                       // 32-key sub-tiles per tile
+    constexpr int WT = NSUB * kTile;              // keys per tile
+    constexpr int KT_ELEMS = WT * D;              // K tile (swizzled, unpadded)
+    constexpr int VT_ELEMS = WT * SM::VS;
+    constexpr int CH_PER_THREAD = WT * CPR / kThreads;   // 8 (D = 128) or 4 (D = 64)
+    __shared__ __attribute__((aligned(16))) uint16_t kst[KT_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t vst[VT_ELEMS];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int col = lane & 15;
+    const int g4 = lane >> 4;
+
+    int bid = blockIdx.x;
+    const int kv = bid % H_kv;
+    bid /= H_kv;
+    const int hg = bid % n_hg;
+    const int unit = bid / n_hg;
+    int sq = 0;
+    while (sq + 1 < plan.nseq && plan.unit_base[sq + 1] <= unit) ++sq;
+    const int split = unit - plan.unit_base[sq];
+    const int len = plan.len[sq];
+    const int L = plan.split_len[sq];
+    const int kbeg = split * L;
+    const int kend = min(len, kbeg + L);
+    const int b = plan.seq0 + sq;
+    const int ncols = T_q * G;
+    const int pos0 = len - T_q;
+    const int n_tiles = (kend - kbeg + WT - 1) / WT;
+
+    const int64_t row_stride = (int64_t)H_kv * D;
+    const uint16_t* kseq = k + (plan.key_off[sq] * H_kv + kv) * (int64_t)D;
+    const uint16_t* vseq = v + (plan.key_off[sq] * H_kv + kv) * (int64_t)D;
+
+    // tile loads: thread chunk ci = tid + kThreads * u -> row ci / CPR, chunk ci % CPR
+    u32x4 kr[CH_PER_THREAD], vr[CH_PER_THREAD];
+    auto load = [&](int t) {
+        const int key0 = kbeg + t * WT;
+#pragma unroll
+        for (int u = 0; u < CH_PER_THREAD; ++u) {
+            const int ci = tid + kThreads * u;
+            const int key = min(key0 + ci / CPR, kend - 1);
+            kr[u] = *(const u32x4*)(kseq + (int64_t)key * row_stride + (ci % CPR) * 8);
+            vr[u] = *(const u32x4*)(vseq + (int64_t)key * row_stride + (ci % CPR) * 8);
+        }
+    };
+    auto store = [&]() {
+#pragma unroll
+        for (int u = 0; u < CH_PER_THREAD; ++u) {
+            const int ci = tid + kThreads * u;
+            const int r = ci / CPR, ch = ci % CPR;
+            *(u32x4*)(&kst[r * D + ((ch ^ wide_swz<D>(r)) << 3)]) = kr[u];
+            *(u32x4*)(&vst[r * SM::VS + ch * 8]) = vr[u];
+        }
+    };
+
+    // this wave's column blocks: (hg * kWideWaves + wave) * NHW + h
+    int vis_end[NHW];
+    bf16x8 qf[NHW][KSTEPS];
+#pragma unroll
+    for (int h = 0; h < NHW; ++h) {
+        const int f = ((hg * kWideWaves + wave) * NHW + h) * kCols + col;
+        const int fc = min(f, ncols - 1);
+        const int tq = fc / G;
+        const int hq = kv * G + fc % G;
+        vis_end[h] = min(kend, pos0 + tq + 1);
+        const uint16_t* qrow = q + (((int64_t)b * T_q + tq) * H_q + hq) * D + g4 * 8;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s)
+            qf[h][s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + s * 32));
+    }
+    const int wave_cols = ((hg * kWideWaves + wave) * NHW) * kCols;
+    const bool wave_live = wave_cols < ncols;     // wave-uniform
+    const int mask_from = min(kend, pos0 + 1);
+
+    // per-lane LDS read offsets: K A-operand row tile_key(col, blk), logical chunk 4 s + g4
+    int koff[2][KSTEPS];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        const int r = tile_key(col, blk);
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) koff[blk][s] = r * D + (((s * 4 + g4) ^ wide_swz<D>(r)) << 3);
+    }
+    const int vrd = (g4 + 4 * ((lane & 15) >> 2)) * SM::VS + 4 * (lane & 3);
+
+    f32x4 oacc[NHW][DBLK];
+    float m_run[NHW], l_run[NHW];
+#pragma unroll
+    for (int h = 0; h < NHW; ++h) {
+#pragma unroll
+        for (int i = 0; i < DBLK; ++i) oacc[h][i] = f32x4{};
+        m_run[h] = -INFINITY;
+        l_run[h] = 0.f;
+    }
+
+    // one LDS tile; the next tile waits in registers (its loads are in
+    // flight while this one is computed)
+    if (n_tiles > 0) {
+        load(0);
+        store();
+    }
+    __syncthreads();
+    for (int t = 0; t < n_tiles; ++t) {
+        if (t + 1 < n_tiles) load(t + 1);
+#pragma unroll
+        for (int half = 0; half < NSUB; ++half) {
+          const int key0 = kbeg + t * WT + half * kTile;
+          if (wave_live && key0 < kend) {
+            const uint16_t* kt = kst + half * kTile * D;
+            const uint16_t* vt = vst + half * kTile * SM::VS;
+            f32x4 s[NHW][2];
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+                for (int h = 0; h < NHW; ++h) s[h][blk] = f32x4{};
+#pragma unroll
+                for (int ks = 0; ks < KSTEPS; ++ks) {
+                    const bf16x8 a = *(const bf16x8*)(kt + koff[blk][ks]);
+#pragma unroll
+                    for (int h = 0; h < NHW; ++h)
+                        s[h][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[h][ks], s[h][blk],
+                                                                             0, 0, 0);
+                }
+            }
+            if (key0 + kTile > mask_from) {
+#pragma unroll
+                for (int h = 0; h < NHW; ++h)
+#pragma unroll
+                    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (key0 + g4 + 16 * blk + 4 * i >= vis_end[h]) s[h][blk][i] = -INFINITY;
+            }
+            float corr[NHW];
+            bf16x8 pb[NHW];
+#pragma unroll
+            for (int h = 0; h < NHW; ++h) {
+                float mt = fmaxf(fmaxf(fmaxf(s[h][0][0], s[h][0][1]), fmaxf(s[h][0][2], s[h][0][3])),
+                                 fmaxf(fmaxf(s[h][1][0], s[h][1][1]), fmaxf(s[h][1][2], s[h][1][3])));
+                mt = fmaxf(mt, xor16(mt));
+                mt = fmaxf(mt, xor32(mt));
+                const float m_new = fmaxf(m_run[h], mt);
+                const float mc = (m_new == -INFINITY) ? 0.f : m_new * c;
+                corr[h] = fast_exp2(m_run[h] * c - mc);
+                float p[8];
+#pragma unroll
+                for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        p[blk * 4 + i] = fast_exp2(__builtin_fmaf(s[h][blk][i], c, -mc));
+                l_run[h] = l_run[h] * corr[h] +
+                           (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+                m_run[h] = m_new;
+                u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                            pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+                pb[h] = __builtin_bit_cast(bf16x8, pw);
+            }
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db) {
+                const s16x4 lo = lds_read_tr16(vt + vrd + db * 16);
+                const s16x4 hi = lds_read_tr16(vt + vrd + 16 * SM::VS + db * 16);
+                const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+                for (int h = 0; h < NHW; ++h) {
+                    oacc[h][db] *= corr[h];
+                    oacc[h][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, a8), pb[h], oacc[h][db], 0, 0, 0);
+                }
+            }
+          }
+        }
+        if (t + 1 < n_tiles) {
+            __syncthreads();                  // every wave is done with tile t
+            store();
+        }
+        __syncthreads();
+    }
+
+    // ---- each wave writes the partials of its own rows ----
+    const int64_t pidx = (int64_t)plan.split_base + unit;
+#pragma unroll
+    for (int h = 0; h < NHW; ++h) {
+        float lr = l_run[h];
+        lr += xor16(lr);
+        lr += xor32(lr);
+        const int fo = ((hg * kWideWaves + wave) * NHW + h) * kCols + col;
+        if (fo < ncols) {
+            const int64_t hrow = (pidx * T_q + fo / G) * H_q + (int64_t)kv * G + fo % G;
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db) *(f32x4*)(ws_o + hrow * D + db * 16 + g4 * 4) = oacc[h][db];
+            if (g4 == 0) {
+                ws_m[hrow] = m_run[h] * c;      // base-2 units
+                ws_l[hrow] = lr;
+            }
+        }
+    }
+}
+
 }  // namespace
 
 int decode_column_blocks_per_group(int T_q, int G) { return T_q * G > kCols ? 2 : 1; }
 
+// more than two 16-row column blocks: the wide kernel (bf16, packed cache)
+static bool decode_use_wide(int T_q, int G) { return T_q * G > 2 * kCols; }
+static int decode_wide_nhw(int T_q, int G) { return T_q * G > kWideWaves * kCols ? 2 : 1; }
+
 int decode_column_groups(int T_q, int G) {
     const int blocks = (T_q * G + kCols - 1) / kCols;
-    const int nh = decode_column_blocks_per_group(T_q, G);
-    return (blocks + nh - 1) / nh;
+    const int per = decode_use_wide(T_q, G) ? kWideWaves * decode_wide_nhw(T_q, G)
+                                            : decode_column_blocks_per_group(T_q, G);
+    return (blocks + per - 1) / per;
+}
+
+template <int D, int NHW>
+static hipError_t launch_wide(const void* q, const void* k, const void* v,
+                              const DecodeWorkspace& ws, const DecodePlanChunk& plan, int T_q,
+                              int H_q, int H_kv, float c, hipStream_t stream) {
+    const int G = H_q / H_kv;
+    const int blocks = (T_q * G + kCols - 1) / kCols;
+    const int n_hg = (blocks + kWideWaves * NHW - 1) / (kWideWaves * NHW);
+    const int64_t grid = (int64_t)plan.units * n_hg * H_kv;
+    if (grid < 1 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((decode_wide_kernel<D, NHW>), dim3((unsigned)grid), dim3(kThreads), 0,
+                       stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, ws.m,
+                       ws.l, ws.o, plan, T_q, H_q, H_kv, G, n_hg, c);
+    return hipGetLastError();
 }
 
 struct KvScales {
@@ -563,8 +817,9 @@ static hipError_t split_dispatch(const void* q, const void* k, const void* v,
                                  int H_q, int H_kv, int d, float scale, const RingArgs& ring,
                                  hipStream_t stream, const KvScales& sc = KvScales{}) {
     const int G = H_q / H_kv;
-    const int n_hg = decode_column_groups(T_q, G);
+    // this kernel covers nh column blocks per work-group (not the wide kernel's count)
     const int nh = decode_column_blocks_per_group(T_q, G);
+    const int n_hg = ((T_q * G + kCols - 1) / kCols + nh - 1) / nh;
     const int64_t grid = (int64_t)plan.units * n_hg * H_kv;
     if (grid < 1 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     if (RING && (ring.sink < 0 || ring.capacity - ring.sink < 1 || ring.window < 1))
@@ -586,6 +841,16 @@ hipError_t launch_decode_split_bf16(const void* q, const void* k, const void* v,
                                     const DecodeWorkspace& ws, const DecodePlanChunk& plan,
                                     int T_q, int H_q, int H_kv, int d, float scale,
                                     hipStream_t stream) {
+    const int G = H_q / H_kv;
+    if (decode_use_wide(T_q, G)) {
+        const float c = scale * kLog2e;
+        const bool two = decode_wide_nhw(T_q, G) == 2;
+        if (d == 128)
+            return two ? launch_wide<128, 2>(q, k, v, ws, plan, T_q, H_q, H_kv, c, stream)
+                       : launch_wide<128, 1>(q, k, v, ws, plan, T_q, H_q, H_kv, c, stream);
+        return two ? launch_wide<64, 2>(q, k, v, ws, plan, T_q, H_q, H_kv, c, stream)
+                   : launch_wide<64, 1>(q, k, v, ws, plan, T_q, H_q, H_kv, c, stream);
+    }
     return split_dispatch<false>(q, k, v, ws, plan, T_q, H_q, H_kv, d, scale, RingArgs{1, 0, 1},
                                  stream);
 }

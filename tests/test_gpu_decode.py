@@ -47,6 +47,8 @@ def _decode_with_lse(inp, num_splits=0):
     ([129, 17], 32, 1, 128),             # G = 32: two 16-head groups
     ([250], 20, 1, 64),                  # G = 20: partial second head group
     ([513, 1], 8, 8, 128),               # G = 1
+    ([300, 1, 65], 64, 1, 128),          # G = 64: four column blocks per KV head
+    ([77, 5000], 48, 1, 64),             # G = 48, d = 64
 ])
 def test_decode_parity(kv_len, Hq, Hkv, d):
     inp = gin.random_case("decode", "bf16", B=len(kv_len), H_q=Hq, H_kv=Hkv, d=d, kv_len=kv_len,
@@ -163,6 +165,9 @@ def _decode_multi(inp, num_splits=0):
     (5, [77, 300, 5], 12, 4, 128),        # G = 3, odd T_q
     (2, [250, 40], 20, 1, 64),            # G = 20
     (7, [129, 7], 8, 8, 128),             # G = 1
+    (16, [16, 300, 2000], 64, 8, 64),     # 128 rows, d = 64
+    (32, [32, 33, 700], 64, 8, 128),      # 256 rows: two work-groups per KV head
+    (3, [3, 100, 4097], 96, 8, 128),      # G = 12, 36 rows: three column blocks
 ])
 def test_decode_multi_parity(T_q, kv_len, Hq, Hkv, d):
     inp = _as_multi(gin.random_case("decode", "bf16", B=len(kv_len), H_q=Hq, H_kv=Hkv, d=d,
