@@ -111,6 +111,40 @@ def _require(t, name: str, ndim: int):
         raise GQAError(f"{name} must be contiguous", 2)
 
 
+def _same(ref, *ts):
+    """Every tensor in ts on ref's device and of ref's dtype (None entries skipped)."""
+    for t in ts:
+        if t is None:
+            continue
+        if t.device != ref.device:
+            raise GQAError(f"tensors must be on {ref.device}, got {t.device}", 2)
+        if t.dtype != ref.dtype:
+            raise GQAError(f"tensors must share dtype {ref.dtype}, got {t.dtype}", 3)
+
+
+def _out_like(out, ref, shape, name="out"):
+    """A caller-given output must be a contiguous GPU tensor of exactly the shape
+    and dtype the kernels write (the library trusts the sizes it is given)."""
+    import torch
+    if out is None:
+        return torch.empty(shape, dtype=ref.dtype, device=ref.device)
+    _require(out, name, len(shape))
+    if tuple(out.shape) != tuple(shape) or out.dtype != ref.dtype or out.device != ref.device:
+        raise GQAError(f"{name} must be {ref.dtype} {tuple(shape)} on {ref.device}, got "
+                       f"{out.dtype} {tuple(out.shape)} on {out.device}", 2)
+    return out
+
+
+def _lse_buf(lse, ref, shape, wanted: bool):
+    import torch
+    if lse is None:
+        return torch.empty(shape, dtype=torch.float32, device=ref.device) if wanted else None
+    _require(lse, "lse", len(shape))
+    if tuple(lse.shape) != tuple(shape) or lse.dtype != torch.float32 or lse.device != ref.device:
+        raise GQAError(f"lse must be float32 {tuple(shape)} on {ref.device}", 2)
+    return lse
+
+
 def _kv_len_array(kv_len, B: int) -> np.ndarray:
     try:
         import torch
@@ -138,18 +172,11 @@ def prefill(q, k, v, *, causal: bool, q_offset: int = 0, scale: float | None = N
     S_kv, H_kv = k.shape[1], k.shape[2]
     if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
         raise GQAError("k and v must be [B, S_kv, H_kv, d] matching q", 2)
-    if not (q.dtype == k.dtype == v.dtype):
-        raise GQAError("q, k, v must share one dtype", 3)
+    _same(q, k, v)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
-    else:
-        _require(out, "out", 4)
-    if lse is None and return_lse:
-        lse = torch.empty((B, T_q, H_q), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _require(lse, "lse", 3)
+    out = _out_like(out, q, (B, T_q, H_q, d))
+    lse = _lse_buf(lse, q, (B, T_q, H_q), return_lse)
     rc = load_library().gqa_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, T_q,
                                          S_kv, H_q, H_kv, d, float(scale), int(bool(causal)),
                                          int(q_offset), _dtype_code(q), _stream(q.device))
@@ -169,18 +196,11 @@ def prefill_kvsplit(q, k, v, *, causal: bool, q_offset: int = 0, scale: float | 
     S_kv, H_kv = k.shape[1], k.shape[2]
     if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
         raise GQAError("k and v must be [B, S_kv, H_kv, d] matching q", 2)
-    if not (q.dtype == k.dtype == v.dtype):
-        raise GQAError("q, k, v must share one dtype", 3)
+    _same(q, k, v)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
-    else:
-        _require(out, "out", 4)
-    if lse is None and return_lse:
-        lse = torch.empty((B, T_q, H_q), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _require(lse, "lse", 3)
+    out = _out_like(out, q, (B, T_q, H_q, d))
+    lse = _lse_buf(lse, q, (B, T_q, H_q), return_lse)
     rc = load_library().gqa_attn_prefill_kvsplit(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, T_q, S_kv, H_q, H_kv, d,
         float(scale), int(bool(causal)), int(q_offset), int(num_splits), _dtype_code(q),
@@ -202,18 +222,11 @@ def prefill_window(q, k, v, *, window: int, sink: int = 0, q_offset: int = 0,
     S_kv, H_kv = k.shape[1], k.shape[2]
     if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
         raise GQAError("k and v must be [B, S_kv, H_kv, d] matching q", 2)
-    if not (q.dtype == k.dtype == v.dtype):
-        raise GQAError("q, k, v must share one dtype", 3)
+    _same(q, k, v)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
-    else:
-        _require(out, "out", 4)
-    if lse is None and return_lse:
-        lse = torch.empty((B, T_q, H_q), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _require(lse, "lse", 3)
+    out = _out_like(out, q, (B, T_q, H_q, d))
+    lse = _lse_buf(lse, q, (B, T_q, H_q), return_lse)
     rc = load_library().gqa_attn_prefill_window(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, T_q, S_kv, H_q, H_kv, d,
         float(scale), int(q_offset), int(window), int(sink), _dtype_code(q), _stream(q.device))
@@ -260,6 +273,7 @@ def _decode_shapes(q, k, v, kv_len):
     B, H_q, d = q.shape
     if k.shape != v.shape or k.shape[2] != d:
         raise GQAError("k and v must be [sum(kv_len), H_kv, d] matching q", 2)
+    _same(q, k, v)
     a = _kv_len_array(kv_len, B)
     if int(a.astype(np.int64).sum()) != k.shape[0]:
         raise GQAError("k/v rows must equal sum(kv_len)", 2)
@@ -272,8 +286,7 @@ def decode(q, k, v, kv_len, *, scale: float | None = None, num_splits: int = 0, 
     B, H_q, H_kv, d, a = _decode_shapes(q, k, v, kv_len)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
+    out = _out_like(out, q, (B, H_q, d))
     rc = load_library().gqa_attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H_q, H_kv, d,
                                         a.ctypes.data, float(scale), int(num_splits),
                                         _dtype_code(q), _stream(q.device))
@@ -293,15 +306,14 @@ def decode_multi(q, k, v, kv_len, *, scale: float | None = None, num_splits: int
     B, T_q, H_q, d = q.shape
     if k.shape != v.shape or k.shape[2] != d:
         raise GQAError("k and v must be [sum(kv_len), H_kv, d] matching q", 2)
+    _same(q, k, v)
     a = _kv_len_array(kv_len, B)
     if int(a.astype(np.int64).sum()) != k.shape[0]:
         raise GQAError("k/v rows must equal sum(kv_len)", 2)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None and return_lse:
-        lse = torch.empty((B, T_q, H_q), dtype=torch.float32, device=q.device)
+    out = _out_like(out, q, (B, T_q, H_q, d))
+    lse = _lse_buf(lse, q, (B, T_q, H_q), return_lse)
     rc = load_library().gqa_attn_decode_multi(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                               B, T_q, H_q, k.shape[1], d, a.ctypes.data,
                                               float(scale), int(num_splits), _dtype_code(q),
@@ -332,17 +344,17 @@ def decode_quant(q, k_codes, v_codes, k_scale, v_scale, kv_len, *, kv_bits: int,
     H_kv = k_codes.shape[1]
     for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
         _require(t, name, 2)
-        if t.dtype != torch.float32 or tuple(t.shape) != (H_kv, d):
-            raise GQAError(f"{name} must be fp32 [{H_kv}, {d}]", 2)
+        if t.dtype != torch.float32 or tuple(t.shape) != (H_kv, d) or t.device != q.device:
+            raise GQAError(f"{name} must be fp32 [{H_kv}, {d}] on {q.device}", 2)
     a = _kv_len_array(kv_len, B)
     if int(a.astype(np.int64).sum()) != k_codes.shape[0]:
         raise GQAError("k/v rows must equal sum(kv_len)", 2)
+    if k_codes.device != q.device or v_codes.device != q.device:
+        raise GQAError(f"k/v codes must be on {q.device}", 2)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None and return_lse:
-        lse = torch.empty((B, T_q, H_q), dtype=torch.float32, device=q.device)
+    out = _out_like(out, q, (B, T_q, H_q, d))
+    lse = _lse_buf(lse, q, (B, T_q, H_q), return_lse)
     rc = load_library().gqa_attn_decode_quant(
         _ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_scale), _ptr(v_scale), _ptr(out),
         _ptr(lse), B, T_q, H_q, H_kv, d, a.ctypes.data, int(kv_bits), float(scale),
@@ -364,13 +376,12 @@ def decode_ring(q, k_cache, v_cache, kv_len, *, window: int, sink: int = 0,
     B, T_q, H_q, d = q.shape
     if k_cache.shape != v_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != d:
         raise GQAError("k_cache and v_cache must be [B, capacity, H_kv, d] matching q", 2)
+    _same(q, k_cache, v_cache)
     a = _kv_len_array(kv_len, B)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None and return_lse:
-        lse = torch.empty((B, T_q, H_q), dtype=torch.float32, device=q.device)
+    out = _out_like(out, q, (B, T_q, H_q, d))
+    lse = _lse_buf(lse, q, (B, T_q, H_q), return_lse)
     rc = load_library().gqa_attn_decode_ring(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), B, T_q, H_q,
         k_cache.shape[2], d, k_cache.shape[1], a.ctypes.data, int(window), int(sink),
@@ -384,6 +395,9 @@ def decode_split(q, k, v, kv_len, workspace, *, scale: float | None = None, num_
     B, H_q, H_kv, d, a = _decode_shapes(q, k, v, kv_len)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    _require(workspace, "workspace", workspace.dim())
+    if workspace.device != q.device:
+        raise GQAError(f"workspace must be on {q.device}", 2)
     nbytes = workspace.numel() * workspace.element_size()
     rc = load_library().gqa_attn_decode_split(_ptr(q), _ptr(k), _ptr(v), _ptr(workspace), nbytes,
                                               B, H_q, H_kv, d, a.ctypes.data, float(scale),
@@ -397,10 +411,14 @@ def decode_combine(workspace, kv_len, *, H_q: int, H_kv: int, d: int, out, lse=N
     (and ``lse`` [B,H_q] fp32 if given)."""
     _require(out, "out", 3)
     B = out.shape[0]
+    if tuple(out.shape[1:]) != (H_q, d):
+        raise GQAError(f"out must be [B, {H_q}, {d}]", 2)
     a = _kv_len_array(kv_len, B)
+    _require(workspace, "workspace", workspace.dim())
+    if workspace.device != out.device:
+        raise GQAError(f"workspace must be on {out.device}", 2)
     nbytes = workspace.numel() * workspace.element_size()
-    if lse is not None:
-        _require(lse, "lse", 2)
+    lse = _lse_buf(lse, out, (B, H_q), False)
     rc = load_library().gqa_attn_decode_combine(_ptr(workspace), nbytes, _ptr(out), _ptr(lse), B,
                                                 H_q, H_kv, d, a.ctypes.data, int(num_splits),
                                                 _dtype_code(out), _stream(out.device))

@@ -209,3 +209,29 @@ def test_decode_multi_full_size():
     og, lg = _decode_multi(inp)
     oref, lref = _oracle_multi(inp)
     assert_close(og, oref, lg, lref, name="decode_t4_varlen_b16")
+
+
+def test_binding_rejects_mismatched_buffers():
+    """Caller-given outputs of the wrong shape/dtype and mixed-dtype inputs are
+    refused on the host, before anything is launched."""
+    import gqa_attention_flashattention_amd as gq
+    import torch
+    inp = gin.random_case("decode", "bf16", B=2, H_q=16, H_kv=2, d=128, kv_len=[40, 9], seed=60)
+    q, k, v = _dev(inp)
+    with pytest.raises(gq.GQAError):
+        gq.decode(q, k, v, inp.kv_len, out=torch.empty(2, 16, 64, dtype=torch.bfloat16,
+                                                      device="cuda"))
+    with pytest.raises(gq.GQAError):
+        gq.decode(q, k.float(), v, inp.kv_len)
+    with pytest.raises(gq.GQAError):
+        gq.decode_multi(q[:, None], k, v, inp.kv_len,
+                        lse=torch.empty(2, 1, 8, dtype=torch.float32, device="cuda"))
+    with pytest.raises(gq.GQAError):
+        gq.decode_combine(torch.empty(1 << 20, dtype=torch.uint8, device="cuda"), inp.kv_len,
+                          H_q=16, H_kv=2, d=128,
+                          out=torch.empty(2, 8, 128, dtype=torch.bfloat16, device="cuda"))
+    qp = torch.zeros(1, 4, 16, 128, dtype=torch.bfloat16, device="cuda")
+    kp = torch.zeros(1, 8, 2, 128, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(gq.GQAError):
+        gq.prefill(qp, kp, kp, causal=True, q_offset=4,
+                   out=torch.empty(1, 4, 16, 128, dtype=torch.float32, device="cuda"))
