@@ -46,4 +46,15 @@ __device__ __forceinline__ float xor8(float x) {
         __builtin_amdgcn_update_dpp(0u, __float_as_uint(x), 0x128, 0xf, 0xf, false));
 }
 
+// Work-groups are dispatched to the 8 XCDs round-robin (block b runs on XCD
+// b % 8).  This remaps block ids so that each XCD receives one contiguous
+// range of logical ids: XCD x gets logical ids [x*q + min(x, r), ...) where
+// q = n / 8, r = n % 8.  A bijection on [0, n).
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_contiguous(int bid, int n) {
+    const int xcd = bid % kXcds, i = bid / kXcds;
+    const int q = n / kXcds, r = n % kXcds;
+    return xcd * q + min(xcd, r) + i;
+}
+
 }  // namespace gqa

@@ -86,7 +86,16 @@ struct Identity {
     __device__ __forceinline__ int operator()(int kk) const { return kk; }
 };
 
-// Eight signed codes -> eight bf16 values (exact: |code| <= 128).
+// int8 codes enter the MFMAs as their exact bf16 images.  int4 codes enter
+// as offset values: flipping bit 3 of each nibble gives n = code + 8 in
+// [0, 15], and the bf16 bit pattern 0x4300 | n is the number 128 + n = code
+// + 136, so a pair of values costs one byte permute and one OR, with no
+// conversion.  The offset is taken out exactly afterwards: from the scores as
+// 136 * sum_x q'_x, from O as 136 * sum_j p_j (the same bf16 p the MFMA used).
+template <int KVF>
+constexpr float kCodeOffset = KVF == kKvInt4 ? 136.f : 0.f;
+
+// Eight signed int8 codes (two words) -> eight bf16 values (exact: |code| <= 128).
 __device__ __forceinline__ bf16x8 i8x8_to_bf16(uint32_t lo, uint32_t hi) {
     bf16x8 r;
 #pragma unroll
@@ -96,11 +105,16 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16(uint32_t lo, uint32_t hi) {
     }
     return r;
 }
+// Eight int4 codes (one word, code i in bits 4i..4i+3) -> eight bf16 values code + 136.
 __device__ __forceinline__ bf16x8 i4x8_to_bf16(uint32_t w) {
-    bf16x8 r;
+    w ^= 0x88888888u;
+    const uint32_t even = w & 0x0f0f0f0fu;          // n of codes 0, 2, 4, 6 in bytes 0..3
+    const uint32_t odd = (w >> 4) & 0x0f0f0f0fu;    // n of codes 1, 3, 5, 7
+    u32x4 r;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = (__bf16)(float)(int)__builtin_amdgcn_sbfe(w, 4 * i, 4);
-    return r;
+    for (int j = 0; j < 4; ++j)   // byte j of even -> bits 0..7, byte j of odd -> bits 16..23
+        r[j] = __builtin_amdgcn_perm(odd, even, 0x0c000c00u | ((4u + j) << 16) | j) | 0x43004300u;
+    return __builtin_bit_cast(bf16x8, r);
 }
 
 // One wave's 32-key tile in registers.  K: the A operands of two 16-key
@@ -203,8 +217,8 @@ __device__ __forceinline__ void wave_lds_fence() {
 // KVF: cache storage format.  For a quantised cache the K scale of each
 // channel is folded into Q (q' = q * k_scale, split into a bf16 high and low
 // part so the fold loses nothing: two MFMAs per k-step against the exact
-// bf16 image of the codes), and the V scale multiplies the partial O once,
-// since O[x] = v_scale[x] * sum_j p_j code_v[j, x].
+// bf16 image of the offset codes), and the V scale multiplies the partial O
+// once, since O[x] = v_scale[x] * sum_j p_j code_v[j, x].
 template <int D, int NH, bool RING, int KVF>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k,
@@ -215,6 +229,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     using SM = DecodeSmem<D>;
     using WT = WaveTile<D, KVF>;
     constexpr bool QUANT = KVF != kKvBf16;
+    constexpr bool OFFSET = KVF == kKvInt4;   // codes enter the MFMAs as code + 136
     constexpr int KSTEPS = WT::KSTEPS;
     constexpr int DBLK = D / 16;             // 16-row blocks of O^T
     constexpr int WSTRIDE = kCols * (D + 2);        // per wave: O [16][D], then m[16], l[16]
@@ -227,7 +242,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int col = lane & 15;               // MFMA column within a 16-column block
     const int g4 = lane >> 4;
 
-    int bid = blockIdx.x;
+    // Quantised caches: the KV heads of one key range run on one XCD, back to
+    // back, because they share the cache's 128-byte lines (an int4 key row of
+    // one head is 64 bytes) and each line then comes from HBM once.  (bf16
+    // rows are 256 bytes per head; there the round-robin order measures
+    // faster.)
+    int bid = QUANT ? xcd_contiguous(blockIdx.x, gridDim.x) : (int)blockIdx.x;
     const int kv = bid % H_kv;
     bid /= H_kv;
     const int hg = bid % n_hg;
@@ -262,6 +282,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     int wbeg[NH];                            // ring: window part of token t starts here
     bf16x8 qf[NH][KSTEPS];
     bf16x8 qlo[QUANT ? NH : 1][QUANT ? KSTEPS : 1];   // low part of q * k_scale
+    float kc[NH];                            // int4: score offset of the offset codes
+    float lb[NH];                            // int4: sum of the bf16 P fed to P.V
     const int64_t row_bytes = (int64_t)H_kv * WT::ROW_BYTES;
     const uint8_t* kseq = k + plan.key_off[sq] * row_bytes + (int64_t)kv * WT::ROW_BYTES;
     const uint8_t* vseq = v + plan.key_off[sq] * row_bytes + (int64_t)kv * WT::ROW_BYTES;
@@ -292,6 +314,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
         // Q^T operand: column = query row, k-group g4 = 8 dims per k-step
         // (the same dims as the K operand of that k-step).
+        kc[h] = 0.f;
         if constexpr (!QUANT) {
             const uint16_t* qrow = q + (((int64_t)b * T_q + tq) * H_q + hq) * D + g4 * 8;
 #pragma unroll
@@ -314,6 +337,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                     qlo[h][s][i] = (__bf16)(qs - (float)hi);
                 }
             }
+            // 136 * sum over all channels of the q' the MFMAs see (hi + lo)
+            float qsum = 0.f;
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) qsum += (float)qf[h][s][i] + (float)qlo[h][s][i];
+            qsum += xor16(qsum);
+            qsum += xor32(qsum);
+            kc[h] = kCodeOffset<KVF> * qsum;
         }
     }
     // walk indices before mask_from are visible to all tokens (apart from the
@@ -334,6 +366,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int i = 0; i < DBLK; ++i) oacc[h][i] = f32x4{};
         m_run[h] = -INFINITY;
         l_run[h] = 0.f;
+        lb[h] = 0.f;
     }
 
     for (; tt < n_tiles; tt += kWaves) {
@@ -354,6 +387,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                         s[h][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qlo[h][ks],
                                                                              s[h][blk], 0, 0, 0);
                 }
+                if constexpr (OFFSET) s[h][blk] -= kc[h];
             }
         wave_lds_fence();                    // previous tile's V reads are done
         wt.store_v(vt, lane);
@@ -395,6 +429,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                         pack_bf16x2(p[6], p[7])};
             pb[h] = __builtin_bit_cast(bf16x8, pw);
+            if constexpr (OFFSET) {
+                float ps = 0.f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) ps += bf16_lo(pw[w]) + bf16_hi(pw[w]);
+                lb[h] = lb[h] * corr[h] + ps;
+            }
         }
         wave_lds_fence();                    // V of this tile is visible to the wave
 #pragma unroll
@@ -422,6 +462,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         lr += xor16(lr);
         lr += xor32(lr);
         float* mw_o = mrg + wave * WSTRIDE;
+        if constexpr (OFFSET) {   // take the V code offset out: O -= 136 * sum_j p_j
+            float lt = lb[h];
+            lt += xor16(lt);
+            lt += xor32(lt);
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db) oacc[h][db] -= kCodeOffset<KVF> * lt;
+        }
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) *(f32x4*)(mw_o + col * D + db * 16 + g4 * 4) = oacc[h][db];
         if (g4 == 0) {
