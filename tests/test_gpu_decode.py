@@ -235,3 +235,19 @@ def test_binding_rejects_mismatched_buffers():
     with pytest.raises(gq.GQAError):
         gq.prefill(qp, kp, kp, causal=True, q_offset=4,
                    out=torch.empty(1, 4, 16, 128, dtype=torch.float32, device="cuda"))
+
+
+def test_decode_multi_deterministic_and_many_sequences():
+    import gqa_attention_flashattention_amd as gq
+    import torch
+    rng = np.random.default_rng(64)
+    kv_len = rng.integers(8, 500, size=70).tolist()
+    inp = gin.random_case("decode", "bf16", B=70, H_q=64, H_kv=8, d=128, T_q=8, kv_len=kv_len,
+                          seed=64)
+    q, k, v = _dev(inp)
+    o1, l1 = gq.decode_multi(q, k, v, inp.kv_len)
+    o2, l2 = gq.decode_multi(q, k, v, inp.kv_len)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    oref, lref = _oracle_multi(inp)
+    assert_close(to_f64(o1), oref, to_f64(l1), lref, name="decode_multi B=70 T_q=8")

@@ -99,3 +99,32 @@ def test_quant_full_size(name):
     oref, lref = _oracle(inp, seqs)
     sel = sorted(seqs)
     assert_close(og[sel], oref[sel], lg[sel], lref[sel], name=name)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_quant_deterministic(bits):
+    """The same call twice gives bitwise identical outputs."""
+    import gqa_attention_flashattention_amd as gq
+    import torch
+    inp = gin.quant_case(B=3, H_q=64, H_kv=8, d=128, kv_len=[3000, 17, 900], kv_bits=bits,
+                         T_q=2, seed=61)
+    pack = (lambda c: c) if bits == 8 else gin.pack_int4
+    q = to_gpu(inp.q_store, "bf16")
+    kc = torch.from_numpy(pack(inp.k_codes)).cuda()
+    vc = torch.from_numpy(pack(inp.v_codes)).cuda()
+    ks = torch.from_numpy(inp.k_scale).cuda()
+    vs = torch.from_numpy(inp.v_scale).cuda()
+    o1, l1 = gq.decode_quant(q, kc, vc, ks, vs, inp.kv_len, kv_bits=bits)
+    o2, l2 = gq.decode_quant(q, kc, vc, ks, vs, inp.kv_len, kv_bits=bits)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_quant_many_sequences_two_launches():
+    """More sequences than one launch describes (64)."""
+    rng = np.random.default_rng(62)
+    kv_len = rng.integers(1, 400, size=70).tolist()
+    inp = gin.quant_case(B=70, H_q=16, H_kv=2, d=128, kv_len=kv_len, kv_bits=4, seed=62)
+    og, lg = _gpu(inp)
+    oref, lref = _oracle(inp)
+    assert_close(og, oref, lg, lref, name="int4 B=70")

@@ -124,3 +124,19 @@ def test_full_size_ring_workload():
     oref, lref = _oracle_ring((inp.q, inp.k, inp.v), kv_len.tolist(), w.capacity,
                               w.window, w.sink)
     assert_close(to_f64(o), oref, to_f64(lse), lref, name="decode_ring_8k_b16")
+
+
+def test_ring_deterministic_and_many_sequences():
+    """70 sequences (two launches), twice: bitwise identical, and against the oracle."""
+    import gqa_attention_flashattention_amd as gq
+    import torch
+    rng = np.random.default_rng(63)
+    kv_len = rng.integers(3, 700, size=70).tolist()
+    vals, bits = _ring_inputs(70, 3, 16, 2, 128, 256, kv_len, seed=63)
+    q, k, v = (to_gpu(x, "bf16") for x in bits)
+    o1, l1 = gq.decode_ring(q, k, v, kv_len, window=200, sink=4)
+    o2, l2 = gq.decode_ring(q, k, v, kv_len, window=200, sink=4)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    oref, lref = _oracle_ring(vals, kv_len, 256, 200, 4)
+    assert_close(to_f64(o1), oref, to_f64(l1), lref, name="ring B=70")

@@ -32,6 +32,9 @@ def _run(inp, causal, q_offset, scale=None):
     (1, 40, 96, 10, 2, 64, True, 56, "bf16"),         # G = 5
     (3, 1, 130, 8, 2, 128, True, 129, "bf16"),        # one query token
     (1, 513, 700, 64, 8, 128, True, 187, "bf16"),     # Llama3-70B heads, several tiles
+    (1, 300, 100, 16, 2, 128, False, 0, "bf16"),      # more queries than keys, non-causal
+    (2, 40, 300, 64, 1, 128, True, 260, "bf16"),      # G = 64: one KV head for all query heads
+    (1, 33, 33, 16, 2, 64, False, 0, "f32"),          # fp32 non-causal, d = 64
 ])
 def test_prefill_parity(B, T, S, Hq, Hkv, d, causal, q_offset, dtype):
     inp = gin.random_case("prefill", dtype, B=B, H_q=Hq, H_kv=Hkv, d=d, T_q=T, S_kv=S, seed=T + S)
