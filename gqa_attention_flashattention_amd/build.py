@@ -24,7 +24,13 @@ LIB = os.path.join(PKG, "libgqa_attn.so")
 SOURCES = ["prefill_bf16.hip", "prefill_f32.hip", "decode.hip", "api.cpp"]
 # The bf16 kernels never create NaNs (masked scores are -inf, never NaN); this
 # lets fmaxf lower to plain v_max_f32 / v_max3_f32 without quieting operands.
-EXTRA_FLAGS = {"prefill_bf16.hip": ["-fno-honor-nans"], "decode.hip": ["-fno-honor-nans"]}
+# The prefill kernel also gets the scheduler that groups memory instructions
+# into clauses: its K/V tile loads then issue back to back ahead of the MFMA
+# chain (about 1% faster on 8k causal prefill, same results bit for bit).
+EXTRA_FLAGS = {
+    "prefill_bf16.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
+    "decode.hip": ["-fno-honor-nans"],
+}
 ARCH = os.environ.get("GQA_ATTN_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
