@@ -29,13 +29,23 @@
 //    exactly the B operand of O^T = V^T P^T.  K rows are loaded into the A
 //    operand in a permuted order (bits 2 and 3 of the row index swapped) so
 //    that the 8 keys a lane contributes to each P.V step are consecutive.
-//  * K and V tiles go from HBM/L2 straight into LDS with global_load_lds_dwordx4
-//    (no staging registers), three tiles in flight in a ring of LDS stages:
-//    while tile j is computed, tiles j+1 and j+2 are loading.  Rows are not
-//    padded; instead the 16-byte chunks of each row are XOR-swizzled (chunk c
-//    of row r sits at c ^ f(r)), which makes the b128 K reads and the
+//  * K and V tiles go from HBM/L2 straight into LDS with buffer_load_dwordx4
+//    ... lds (no staging registers) through a buffer resource per tile, so
+//    the per-lane offset is a fixed register and rows past S_kv read as
+//    zeros; a ring of four LDS stages holds the tiles being read (i - 1 for
+//    P.V, i for QK) and loading (i + 1, i + 2).  Rows are not padded;
+//    instead the 16-byte chunks of each row are XOR-swizzled (chunk c of row
+//    r sits at c ^ f(r)), which makes the b128 K reads and the
 //    ds_read_b64_tr_b16 V^T reads (each lane of a 16-lane group receives one
 //    head-dim column of four key rows) bank-conflict free.
+//  * Ping-pong: waves w and w + 4 share a SIMD.  Waves 0-3 and 4-7 run the
+//    same per-tile work half a tile apart, separated by a barrier in the
+//    middle of every tile, so on each SIMD one wave is in its MFMA phase
+//    (P.V of the previous tile, then QK of this tile) while the other is in
+//    its softmax phase (VALU).  The MFMA phase runs at raised wave priority,
+//    and its LDS operands are read one group of MFMAs ahead.  The VALU work
+//    per tile is kept small: row max as max3 chains, tile loads without
+//    per-lane address arithmetic.
 //  * Lazy rescaling: the running max used for the exponentials is only moved
 //    when some row's tile max exceeds it by more than 8 (log2 units), so most
 //    tiles skip the O rescale; exact, since O and l always share the same
@@ -52,7 +62,7 @@ constexpr int kRowsPerWave = 32;
 constexpr int kBlockM = kWaves * kRowsPerWave;   // 256 query rows per work-group
 constexpr int kBlockN = 64;                      // keys per tile
 constexpr int kThreads = kWaves * 64;
-constexpr int kStages = 3;                       // LDS ring depth (tiles in flight)
+constexpr int kStages = 4;                       // LDS ring depth (tiles resident)
 constexpr float kRescaleThreshold = 8.f;         // log2 units
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -84,13 +94,12 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
 
-// Issue this wave's direct global->LDS loads of K and V tile `tile` (keys
-// tile*64 ..) into the given stage buffers.  Keys past S_kv are clamped to the
-// last key: their scores are masked to -inf and their P is exactly 0.
+// Issue this wave's direct-to-LDS loads of one K or V tile `tile` (keys
+// tile*64 ..) into the stage buffer dst.  The buffer resource spans only the
+// tile's rows below S_kv: rows past it read as zeros, their scores are masked
+// to -inf and their P is exactly 0.
 template <int D>
-__device__ __forceinline__ void issue_tile(uint16_t* kst, uint16_t* vst,
-                                           const uint16_t* __restrict__ kbase,
-                                           const uint16_t* __restrict__ vbase,
+__device__ __forceinline__ void issue_half(uint16_t* dst, const uint16_t* __restrict__ base,
                                            int64_t row_stride, int tile, int S_kv, int wave,
                                            int lane) {
     using T = Tile<D>;
@@ -99,13 +108,22 @@ __device__ __forceinline__ void issue_tile(uint16_t* kst, uint16_t* vst,
         const int row0 = (wave * T::LOADS + i) * T::ROWS_PER_LOAD;
         const int r = row0 + lane / T::CPR;
         const int cc = (lane % T::CPR) ^ swz<D>(r);
-        const int key = min(tile * kBlockN + r, S_kv - 1);
-        const int64_t off = (int64_t)key * row_stride + cc * 8;
-        __builtin_amdgcn_global_load_lds((const global_void_t*)(kbase + off),
-                                         (lds_void_t*)(kst + row0 * D), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const global_void_t*)(vbase + off),
-                                         (lds_void_t*)(vst + row0 * D), 16, 0, 0);
+        const int rows = min(kBlockN, S_kv - tile * kBlockN);
+        __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(base + (int64_t)tile * kBlockN * row_stride), (short)0,
+            rows * (int)row_stride * 2, 0x00020000);
+        const int lo = (r * (int)row_stride + cc * 8) * 2;   // bytes
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + row0 * D), 16, lo, 0, 0, 0);
     }
+}
+template <int D>
+__device__ __forceinline__ void issue_tile(uint16_t* kst, uint16_t* vst,
+                                           const uint16_t* __restrict__ kbase,
+                                           const uint16_t* __restrict__ vbase,
+                                           int64_t row_stride, int tile, int S_kv, int wave,
+                                           int lane) {
+    issue_half<D>(kst, kbase, row_stride, tile, S_kv, wave, lane);
+    issue_half<D>(vst, vbase, row_stride, tile, S_kv, wave, lane);
 }
 
 // Work-group barrier for LDS traffic only: this wave's LDS operations have
@@ -158,12 +176,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     constexpr int DBLK = D / 32;     // 32-row blocks of O^T
     constexpr int LOADS_PER_TILE = 2 * T::LOADS;   // vmem ops per wave per tile
     static_assert(LOADS_PER_TILE == 2 || LOADS_PER_TILE == 4, "wait_vmcnt covers 2 and 4");
-    __shared__ __attribute__((aligned(1024))) uint16_t ks0[T::ELEMS];
-    __shared__ __attribute__((aligned(1024))) uint16_t ks1[T::ELEMS];
-    __shared__ __attribute__((aligned(1024))) uint16_t ks2[T::ELEMS];
-    __shared__ __attribute__((aligned(1024))) uint16_t vs0[T::ELEMS];
-    __shared__ __attribute__((aligned(1024))) uint16_t vs1[T::ELEMS];
-    __shared__ __attribute__((aligned(1024))) uint16_t vs2[T::ELEMS];
+    static_assert(kStages == 4, "the tile loop below is unrolled over four stages");
+    __shared__ __attribute__((aligned(1024))) uint16_t ksm[kStages * T::ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t vsm[kStages * T::ELEMS];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -244,11 +259,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const uint16_t* kbase = k + ((int64_t)b * S_kv * H_kv + kv) * D;
     const uint16_t* vbase = v + ((int64_t)b * S_kv * H_kv + kv) * D;
 
-    // the first two tiles start loading before anything else
     // global tile of the work-group's compacted tile index j
     auto tile_of = [&](int j) { return WINDOW ? j + (j >= sink_tiles ? gap : 0) : j; };
-    if (n_tiles > 0) issue_tile<D>(ks0, vs0, kbase, vbase, row_stride, tile_of(j_lo), S_kv, wave, lane);
-    if (n_tiles > 1) issue_tile<D>(ks1, vs1, kbase, vbase, row_stride, tile_of(j_lo + 1), S_kv, wave, lane);
+    // loads of the work-group's tile j into LDS stage st; the first two tiles
+    // start loading before anything else
+    auto issue = [&](int j, int st) __attribute__((always_inline)) {
+        issue_tile<D>(ksm + st * T::ELEMS, vsm + st * T::ELEMS, kbase, vbase, row_stride,
+                      tile_of(j_lo + j), S_kv, wave, lane);
+    };
+    if (n_tiles > 0) issue(0, 0);
+    if (n_tiles > 1) issue(1, 1);
 
     // Q^T operand, resident for the whole key sweep.
     bf16x8 qf[KSTEPS];
@@ -283,109 +303,182 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     float m_run = -INFINITY;   // reference max (raw score units) used by P
     float l_run = 0.f;
 
-    // One key tile: the work-group's tile j (global tile j_lo + j) sits in
-    // stage buffers (kt, vt); first tile j + 2 is issued into (kn, vn), the
-    // stage that tile j - 1 used.
-    auto step = [&](int j, const uint16_t* kt, const uint16_t* vt, uint16_t* kn, uint16_t* vn) {
-        const bool issue = j + 2 < n_tiles;
-        if (issue) issue_tile<D>(kn, vn, kbase, vbase, row_stride, tile_of(j_lo + j + 2), S_kv, wave, lane);
+    auto needs = [&](int j) __attribute__((always_inline)) {
         const int key0 = tile_of(j_lo + j) * kBlockN;
-        bool wave_needs = key0 < wave_kend;
-        if (WINDOW) wave_needs = wave_needs && (key0 < sink || key0 + kBlockN > wave_win_any);
-        if (wave_needs) {
-            // ---- S^T = K Q^T (two 32-key blocks) ----
-            f32x16 s[2];
+        bool w = key0 < wave_kend;
+        if (WINDOW) w = w && (key0 < sink || key0 + kBlockN > wave_win_any);
+        return w;
+    };
+    f32x16 s[2];
+    uint32_t pk[2][8];
+    // S^T = K Q^T of tile j (stage st); K operands read one group ahead
+    auto qk = [&](int j, const uint16_t* kt) __attribute__((always_inline)) {
+        if (!needs(j)) return;
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+        constexpr int NQ = 2 * KSTEPS, QG = 4, NG = NQ / QG;
+        auto kread = [&](int n) { return *(const bf16x8*)(kt + (n & 1) * 32 * D + off.k[n >> 1]); };
+        bf16x8 ka[2][QG];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                s[kb] = f32x16{};
+        for (int i = 0; i < QG; ++i) ka[0][i] = kread(i);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int kst = 0; kst < KSTEPS; ++kst) {
-                    const bf16x8 a = *(const bf16x8*)(kt + kb * 32 * D + off.k[kst]);
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kst], s[kb], 0, 0, 0);
-                }
+        for (int g = 0; g < NG; ++g) {
+            if (g + 1 < NG) {
+#pragma unroll
+                for (int i = 0; i < QG; ++i) ka[(g + 1) & 1][i] = kread((g + 1) * QG + i);
             }
-            // element i of s[kb] is key key0 + 32 kb + 16 (i / 8) + 8 hh + (i % 8)
-            bool need_mask = key0 + kBlockN > wave_full;
-            if (WINDOW)
-                need_mask = need_mask || (key0 + kBlockN > sink && key0 < wave_win_all);
-            if (need_mask) {
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = key0 + kb * 32 + (i >> 3) * 16 + hh * 8 + (i & 7);
-                        bool hide = key > last_key;
-                        if (WINDOW) hide = hide || (key >= sink && key < win_lo);
-                        if (hide) s[kb][i] = -INFINITY;
-                    }
+            for (int i = 0; i < QG; ++i) {
+                const int n = g * QG + i;
+                s[n & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[g & 1][i], qf[n >> 1], s[n & 1],
+                                                                 0, 0, 0);
             }
-            // ---- online softmax (base 2), lazy rescale ----
-            float mt = fmaxf(s[0][0], s[1][0]);
-#pragma unroll
-            for (int i = 1; i < 16; ++i) mt = fmaxf(mt, fmaxf(s[0][i], s[1][i]));
-            {
-                auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
-                                                           false, false);
-                mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-            }
-            const bool grow = mt * c > m_run * c + kRescaleThreshold;
-            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-                const float m_new = fmaxf(m_run, mt);
-                // 0 on the first tile; a row with no visible key so far keeps corr = 1
-                const float corr = (m_new == -INFINITY) ? 1.f : fast_exp2((m_run - m_new) * c);
-                l_run *= corr;
-#pragma unroll
-                for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[db][i] *= corr;
-                m_run = m_new;
-            }
-            // a split can start past a row's last key: its m stays -inf, P = 0
-            // (a window or a split can start past the keys a row sees)
-            const float mc = ((SPLIT || WINDOW) && m_run == -INFINITY) ? 0.f : m_run * c;
-            float psum = 0.f;
-            uint32_t pk[2][8];
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // mask, running max, lazy rescale, P (packed bf16) and its row sum
+    auto softmax = [&](int j) __attribute__((always_inline)) {
+        if (!needs(j)) return;
+        const int key0 = tile_of(j_lo + j) * kBlockN;
+        // element i of s[kb] is key key0 + 32 kb + 16 (i / 8) + 8 hh + (i % 8)
+        bool need_mask = key0 + kBlockN > wave_full;
+        if (WINDOW) need_mask = need_mask || (key0 + kBlockN > sink && key0 < wave_win_all);
+        if (need_mask) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; i += 2) {
-                    const float p0 = fast_exp2(__builtin_fmaf(s[kb][i], c, -mc));
-                    const float p1 = fast_exp2(__builtin_fmaf(s[kb][i + 1], c, -mc));
-                    psum += p0 + p1;
-                    pk[kb][i >> 1] = pack_bf16x2(p0, p1);
+                for (int i = 0; i < 16; ++i) {
+                    const int key = key0 + kb * 32 + (i >> 3) * 16 + hh * 8 + (i & 7);
+                    bool hide = key > last_key;
+                    if (WINDOW) hide = hide || (key >= sink && key < win_lo);
+                    if (hide) s[kb][i] = -INFINITY;
                 }
-            l_run += psum;
-            // ---- O^T += V^T P^T, four 16-key steps ----
-#pragma unroll
-            for (int kst = 0; kst < 4; ++kst) {
-                const int kb = kst >> 1, half = kst & 1;
-                const u32x4 pw = {pk[kb][half * 4 + 0], pk[kb][half * 4 + 1],
-                                  pk[kb][half * 4 + 2], pk[kb][half * 4 + 3]};
-                const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-                for (int db = 0; db < DBLK; ++db) {
-                    const s16x4 lo = lds_read_tr16(vt + kst * 16 * D + off.v[0][db]);
-                    const s16x4 hi = lds_read_tr16(vt + kst * 16 * D + off.v[1][db]);
-                    const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, a8), pb, oacc[db], 0, 0, 0);
-                }
-            }
         }
-        // tile j + 1 (issued one step earlier) must be in LDS for every wave
-        if (issue) wait_vmcnt<LOADS_PER_TILE>();
+        float mt0 = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+        float mt1 = fmaxf(fmaxf(s[1][0], s[1][1]), s[1][2]);
+#pragma unroll
+        for (int i = 3; i < 15; i += 2) {
+            mt0 = fmaxf(fmaxf(mt0, s[0][i]), s[0][i + 1]);
+            mt1 = fmaxf(fmaxf(mt1, s[1][i]), s[1][i + 1]);
+        }
+        float mt = fmaxf(fmaxf(mt0, s[0][15]), fmaxf(mt1, s[1][15]));
+        {
+            auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
+                                                       false, false);
+            mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const bool grow = mt * c > m_run * c + kRescaleThreshold;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            const float m_new = fmaxf(m_run, mt);
+            // 0 on the first tile; a row with no visible key so far keeps corr = 1
+            const float corr = (m_new == -INFINITY) ? 1.f : fast_exp2((m_run - m_new) * c);
+            l_run *= corr;
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[db][i] *= corr;
+            m_run = m_new;
+        }
+        // a window or a split can start past the keys a row sees: its m stays
+        // -inf and P = 0
+        const float mc = ((SPLIT || WINDOW) && m_run == -INFINITY) ? 0.f : m_run * c;
+        float psum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) {
+                const float p0 = fast_exp2(__builtin_fmaf(s[kb][i], c, -mc));
+                const float p1 = fast_exp2(__builtin_fmaf(s[kb][i + 1], c, -mc));
+                psum += p0 + p1;
+                pk[kb][i >> 1] = pack_bf16x2(p0, p1);
+            }
+        l_run += psum;
+    };
+    // O^T += V^T P^T of tile j; V^T operands read one 16-key step ahead
+    auto pv = [&](int j, const uint16_t* vt) __attribute__((always_inline)) {
+        if (!needs(j)) return;
+        auto vread = [&](int kst, int db) {
+            const s16x4 lo = lds_read_tr16(vt + kst * 16 * D + off.v[0][db]);
+            const s16x4 hi = lds_read_tr16(vt + kst * 16 * D + off.v[1][db]);
+            return s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        };
+        s16x8 va[2][DBLK];
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) va[0][db] = vread(0, db);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kst = 0; kst < 4; ++kst) {
+            if (kst + 1 < 4) {
+#pragma unroll
+                for (int db = 0; db < DBLK; ++db) va[(kst + 1) & 1][db] = vread(kst + 1, db);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            const int kb = kst >> 1, half = kst & 1;
+            const u32x4 pw = {pk[kb][half * 4 + 0], pk[kb][half * 4 + 1], pk[kb][half * 4 + 2],
+                              pk[kb][half * 4 + 3]};
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db)
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, va[kst & 1][db]), __builtin_bit_cast(bf16x8, pw),
+                    oacc[db], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // tile i + 1 must be in LDS for every wave; tile i + 2 may stay in flight
+    auto end_iter = [&](int i) __attribute__((always_inline)) {
+        if (i + 2 < n_tiles) wait_vmcnt<LOADS_PER_TILE>();
         else wait_vmcnt<0>();
         lds_barrier();
+    };
+    // Iteration i (tile i in stage i & 3), i = 0 .. n_tiles: waves 0-3 run
+    // [PV(i - 1), QK(i)] then [softmax(i)]; waves 4-7 run [softmax(i - 1)]
+    // then [PV(i - 1), QK(i)]; both meet the mid-iteration barrier and the
+    // end barrier.  Each wave issues its part of tile i + 2 at the start of
+    // its softmax phase (the two groups' loads do not queue together), into
+    // the stage of tile i - 2, free everywhere since the end of iteration
+    // i - 1.
+    auto iter0 = [&](int i, int st) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_setprio(1);
+        if (i >= 1) pv(i - 1, vsm + ((st + 3) & 3) * T::ELEMS);
+        if (i < n_tiles) qk(i, ksm + st * T::ELEMS);
+        __builtin_amdgcn_s_setprio(0);
+        lds_barrier();
+        if (i + 2 < n_tiles) issue(i + 2, (st + 2) & 3);
+        if (i < n_tiles) softmax(i);
+        end_iter(i);
+    };
+    auto iter1 = [&](int i, int st) __attribute__((always_inline)) {
+        if (i + 2 < n_tiles) issue(i + 2, (st + 2) & 3);
+        if (i >= 1) softmax(i - 1);
+        lds_barrier();
+        __builtin_amdgcn_s_setprio(1);
+        if (i >= 1) pv(i - 1, vsm + ((st + 3) & 3) * T::ELEMS);
+        if (i < n_tiles) qk(i, ksm + st * T::ELEMS);
+        __builtin_amdgcn_s_setprio(0);
+        end_iter(i);
     };
 
     if (n_tiles > 1) wait_vmcnt<LOADS_PER_TILE>();
     else wait_vmcnt<0>();
     lds_barrier();
-    // (n_tiles == 0 only for an empty split: the loop below does nothing)
-    for (int j = 0; j < n_tiles; j += kStages) {
-        step(j, ks0, vs0, ks2, vs2);
-        if (j + 1 < n_tiles) step(j + 1, ks1, vs1, ks0, vs0);
-        if (j + 2 < n_tiles) step(j + 2, ks2, vs2, ks1, vs1);
+    if (n_tiles > 0) {
+        if (wave < 4) {
+            for (int i = 0; i <= n_tiles; i += 4) {
+                iter0(i, 0);
+                if (i + 1 <= n_tiles) iter0(i + 1, 1);
+                if (i + 2 <= n_tiles) iter0(i + 2, 2);
+                if (i + 3 <= n_tiles) iter0(i + 3, 3);
+            }
+        } else {
+            for (int i = 0; i <= n_tiles; i += 4) {
+                iter1(i, 0);
+                if (i + 1 <= n_tiles) iter1(i + 1, 1);
+                if (i + 2 <= n_tiles) iter1(i + 2, 2);
+                if (i + 3 <= n_tiles) iter1(i + 3, 3);
+            }
+        }
     }
 
     // ---- epilogue: O / l, LSE ----
