@@ -396,23 +396,30 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
             }
         l_run += psum;
     };
-    // O^T += V^T P^T of tile j; V^T operands read one 16-key step ahead
+    // O^T += V^T P^T of tile j; V^T operands read one 16-key step ahead, the
+    // first step's at the end of the preceding softmax phase (vpre)
+    auto vread = [&](const uint16_t* vt, int kst, int db) __attribute__((always_inline)) {
+        const s16x4 lo = lds_read_tr16(vt + kst * 16 * D + off.v[0][db]);
+        const s16x4 hi = lds_read_tr16(vt + kst * 16 * D + off.v[1][db]);
+        return s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    s16x8 vpre[DBLK];
+    auto pv_pre = [&](int j, const uint16_t* vt) __attribute__((always_inline)) {
+        if (!needs(j)) return;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) vpre[db] = vread(vt, 0, db);
+    };
     auto pv = [&](int j, const uint16_t* vt) __attribute__((always_inline)) {
         if (!needs(j)) return;
-        auto vread = [&](int kst, int db) {
-            const s16x4 lo = lds_read_tr16(vt + kst * 16 * D + off.v[0][db]);
-            const s16x4 hi = lds_read_tr16(vt + kst * 16 * D + off.v[1][db]);
-            return s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        };
         s16x8 va[2][DBLK];
 #pragma unroll
-        for (int db = 0; db < DBLK; ++db) va[0][db] = vread(0, db);
+        for (int db = 0; db < DBLK; ++db) va[0][db] = vpre[db];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kst = 0; kst < 4; ++kst) {
             if (kst + 1 < 4) {
 #pragma unroll
-                for (int db = 0; db < DBLK; ++db) va[(kst + 1) & 1][db] = vread(kst + 1, db);
+                for (int db = 0; db < DBLK; ++db) va[(kst + 1) & 1][db] = vread(vt, kst + 1, db);
             }
             __builtin_amdgcn_sched_barrier(0);
             const int kb = kst >> 1, half = kst & 1;
@@ -446,12 +453,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         __builtin_amdgcn_s_setprio(0);
         lds_barrier();
         if (i + 2 < n_tiles) issue(i + 2, (st + 2) & 3);
-        if (i < n_tiles) softmax(i);
+        if (i < n_tiles) {
+            softmax(i);
+            pv_pre(i, vsm + st * T::ELEMS);
+        }
         end_iter(i);
     };
     auto iter1 = [&](int i, int st) __attribute__((always_inline)) {
         if (i + 2 < n_tiles) issue(i + 2, (st + 2) & 3);
-        if (i >= 1) softmax(i - 1);
+        if (i >= 1) {
+            softmax(i - 1);
+            pv_pre(i - 1, vsm + ((st + 3) & 3) * T::ELEMS);
+        }
         lds_barrier();
         __builtin_amdgcn_s_setprio(1);
         if (i >= 1) pv(i - 1, vsm + ((st + 3) & 3) * T::ELEMS);
