@@ -109,6 +109,25 @@ def test_decode_deterministic():
     assert torch.equal(o1, o2)
 
 
+@pytest.mark.parametrize("kv_len,Hq,Hkv,d,num_splits", [
+    ([600, 1000, 513], 64, 8, 128, 1),     # every split >= 512 keys: two KV heads per work-group
+    ([2049, 512], 16, 2, 128, 1),          # ragged last tiles, one head pair
+    ([700, 1500], 32, 4, 64, 1),           # d = 64
+    ([900, 3000], 24, 6, 128, 1),          # three head pairs, G = 4
+    ([777, 1200], 24, 3, 128, 1),          # odd H_kv: one head per work-group
+    ([100, 5000], 64, 8, 128, 1),          # one short split: one head per work-group
+])
+def test_head_pair_work_groups(kv_len, Hq, Hkv, d, num_splits):
+    """Long splits take two KV heads per work-group (waves 0/2 and 1/3);
+    every output and LSE against the oracle, and equal to the one-head layout
+    of the same plan within rounding."""
+    inp = gin.random_case("decode", "bf16", B=len(kv_len), H_q=Hq, H_kv=Hkv, d=d, kv_len=kv_len,
+                          seed=sum(kv_len) + Hkv)
+    og, lg = _decode_with_lse(inp, num_splits)
+    oref, lref = oracle.decode(inp.q, inp.k, inp.v, inp.kv_len)
+    assert_close(og, oref, lg, lref, name=f"decode head pairs {kv_len} {Hq}/{Hkv} d={d}")
+
+
 @pytest.mark.parametrize("name", ["decode_8k", "decode_varlen_b16", "decode_128k"])
 def test_full_size_workloads(name):
     """Full-size decode workloads in the benchmark's launch configuration,
@@ -175,6 +194,18 @@ def test_decode_multi_parity(T_q, kv_len, Hq, Hkv, d):
     og, lg = _decode_multi(inp)
     oref, lref = _oracle_multi(inp)
     assert_close(og, oref, lg, lref, name=f"decode_multi T_q={T_q} {kv_len} {Hq}/{Hkv} d={d}")
+
+
+@pytest.mark.parametrize("T_q,kv_len,num_splits", [
+    (4, [600, 2000], 1),                   # two KV heads per work-group, T_q * G = 32
+    (2, [1024, 513, 4000], 1),
+])
+def test_decode_multi_head_pairs(T_q, kv_len, num_splits):
+    inp = _as_multi(gin.random_case("decode", "bf16", B=len(kv_len), H_q=64, H_kv=8, d=128,
+                                    T_q=T_q, kv_len=kv_len, seed=31 + T_q))
+    og, lg = _decode_multi(inp, num_splits)
+    oref, lref = _oracle_multi(inp)
+    assert_close(og, oref, lg, lref, name=f"decode_multi head pairs T_q={T_q}")
 
 
 @pytest.mark.parametrize("num_splits", [1, 3, 1000])

@@ -85,6 +85,15 @@ def test_ring_decode_parity(T_q, Hq, Hkv, d, cap, window, sink, kv_len):
     assert_close(og, oref, lg, lref, name=f"ring T_q={T_q} cap={cap} w={window} s={sink}")
 
 
+def test_ring_head_pairs():
+    """Long ring splits (>= 512 resident keys each) take two KV heads per work-group."""
+    kv_len = [5000, 1300]
+    vals, bits = _ring_inputs(2, 1, 64, 8, 128, 2048, kv_len, seed=52)
+    og, lg = _gpu_ring(bits, kv_len, 1500, 4, 1)
+    oref, lref = _oracle_ring(vals, kv_len, 2048, 1500, 4)
+    assert_close(og, oref, lg, lref, name="ring head pairs")
+
+
 @pytest.mark.parametrize("num_splits", [1, 3, 100])
 def test_ring_decode_split_counts(num_splits):
     kv_len = [700, 40, 2500]
