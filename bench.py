@@ -338,12 +338,22 @@ def traffic_record(kernel: str, grid: int):
 # Launch geometry of the two headline kernels (threads per grid), to match
 # rocprofv3 records: the decode split kernel runs 256 threads per (split, KV
 # head) at G * T_q <= 16; the prefill kernel 512 threads per 256-row block.
-DECODE_SPLIT_KERNEL = "decode_split_kernel<128,1,false,0>"
 PREFILL_KERNEL = "prefill_bf16_kernel<128,1,false>"
+# bf16 splits of at least this many keys run two KV heads per work-group
+# (the library's rule; the kernel name and grid of the profiled launch follow it)
+DECODE_PAIR_MIN_SPLIT_LEN = 512
+
+
+def decode_heads_per_wg(plan, w):
+    return 2 if (w.H_kv % 2 == 0 and int(plan["split_len"]) >= DECODE_PAIR_MIN_SPLIT_LEN) else 1
+
+
+def decode_split_kernel_name(plan, w):
+    return f"decode_split_kernel<{w.d},1,false,0,{decode_heads_per_wg(plan, w)}>"
 
 
 def decode_split_grid(plan, w):
-    return int(plan["total_splits"]) * w.H_kv * 256
+    return int(plan["total_splits"]) * (w.H_kv // decode_heads_per_wg(plan, w)) * 256
 
 
 def prefill_grid(w):
@@ -609,11 +619,11 @@ def main():
                    "kv_copies_rotated": dec["n_copies"], "timed_via": "hip graph replay"},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "hot_cache_GBps": round(dec["kv_bytes"] / (dec["ms_hot"] * 1e-3) / 1e9, 2),
-        "roofline": {"bound": "hbm", "kernel": DECODE_SPLIT_KERNEL,
+        "roofline": {"bound": "hbm", "kernel": decode_split_kernel_name(dec["plan"], dw),
                      "grid_threads": decode_split_grid(dec["plan"], dw),
                      "achieved": round(gbs_split, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs_split / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_record(DECODE_SPLIT_KERNEL,
+                     "traffic": traffic_record(decode_split_kernel_name(dec["plan"], dw),
                                                decode_split_grid(dec["plan"], dw)),
                      "algorithmic_bytes_per_launch": dec["kv_bytes"],
                      "avg_launch_us": round(dec["ms_split"] * 1e3, 3)},
