@@ -53,15 +53,33 @@ def dev_tensor(arr, dtype="bf16"):
     return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).cuda()
 
 
+WARM_MS = 200.0
+
+
+def warm(fn, min_ms=WARM_MS):
+    """Call fn back to back until the GPU has been busy with it for about
+    min_ms.  The shader clock ramps up over the first tens of milliseconds
+    of sustained load (8k causal prefill: 1.10 ms per call in the first ten
+    calls after an idle GPU, 0.95 ms from about the 30th call on); every
+    figure here is steady-state throughput."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        fn()
+        torch.cuda.synchronize()
+
+
 def time_graph(fn_list, reps=1):
     """Capture the calls in fn_list into one graph, replay it `reps` times
-    between HIP events; returns elapsed ms per call."""
+    between HIP events after warm-up replays; returns elapsed ms per call."""
     import torch
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for fn in fn_list:
             fn()
-    g.replay()                     # warm replay
+    warm(g.replay)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -181,7 +199,7 @@ def bench_prefill(name, steps, warmup):
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
     for _ in range(max(warmup, 1)):
         gq.prefill(q, k, v, causal=w.causal, q_offset=w.q_offset, out=o, lse=lse)
-    torch.cuda.synchronize()
+    warm(lambda: gq.prefill(q, k, v, causal=w.causal, q_offset=w.q_offset, out=o, lse=lse))
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
