@@ -138,9 +138,11 @@ __device__ __forceinline__ void lds_barrier() {
 // Wait until at most N of this wave's vector-memory operations are pending.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N == 0 || N == 2 || N == 4 || N == 8, "vmcnt values used here");
     if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
 }
 
 template <int D>
@@ -267,14 +269,46 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         issue_tile<D>(ksm + st * T::ELEMS, vsm + st * T::ELEMS, kbase, vbase, row_stride,
                       tile_of(j_lo + j), S_kv, wave, lane);
     };
+    // Q and O pass through LDS, each wave through its own 32-row area in the
+    // stages tiles 2 and 3 use later (waves 0-3 in the K stages, 4-7 in the
+    // V stages), so that global accesses move whole rows (a wave instruction
+    // covers 64 / (D / 8) rows) instead of 8 bytes of 32 rows; the 16-byte
+    // chunks of a row are XOR-swizzled as in the K/V tiles.
+    uint16_t* qo_lds = (wave < 4 ? ksm : vsm) + 2 * T::ELEMS + (wave & 3) * kRowsPerWave * D;
+    constexpr int QROWS = 64 / T::CPR;                   // rows per wave instruction
+    // global element offset of row r of the work-group (clamped into range)
+    auto row_off = [&](int r) {
+        const int rc = min(r, rows_total - 1);
+        return (((int64_t)b * T_q + rc / G) * H_q + (int64_t)kv * G + rc % G) * D;
+    };
+    {
+        // rows of the first token of this work-group onwards, < 2^31 bytes away
+        const int t0 = r0 / G;
+        const uint16_t* qbase = q + (((int64_t)b * T_q + t0) * H_q + (int64_t)kv * G) * D;
+        __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)qbase, (short)0,
+                                                                      0x7ffffff0, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave / QROWS; ++i) {
+            const int lr = i * QROWS + lane / T::CPR;
+            const int cc = (lane % T::CPR) ^ swz<D>(lr);
+            const int rc = min(rw0 + lr, rows_total - 1);
+            const int off = (int)((((int64_t)(rc / G - t0) * H_q + rc % G) * D + cc * 8) * 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(qo_lds + i * QROWS * D), 16,
+                                                     off, 0, 0, 0);
+        }
+    }
     if (n_tiles > 0) issue(0, 0);
     if (n_tiles > 1) issue(1, 1);
 
-    // Q^T operand, resident for the whole key sweep.
+    // Q^T operand, resident for the whole key sweep (this wave's Q rows have
+    // landed once at most the tile loads behind them are outstanding).
+    if (n_tiles > 1) wait_vmcnt<2 * LOADS_PER_TILE>();
+    else if (n_tiles > 0) wait_vmcnt<LOADS_PER_TILE>();
+    else wait_vmcnt<0>();
     bf16x8 qf[KSTEPS];
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
-        qf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q + qo_off + ks * 16 + hh * 8));
+        qf[ks] = *(const bf16x8*)(qo_lds + lq * D + (((2 * ks + hh) ^ swz<D>(lq)) << 3));
 
     // Per-lane LDS read offsets (elements), fixed for the whole sweep.
     LaneOffsets<D> off;
@@ -518,18 +552,25 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         }
         return;
     }
-    if (valid) {
-        const float inv = 1.f / l_run;
+    // (every wave is past the last barrier: no LDS reads or loads remain)
+    const float inv = 1.f / l_run;
 #pragma unroll
-        for (int db = 0; db < DBLK; ++db)
+    for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                u32x2 w = {pack_bf16x2(oacc[db][4 * u] * inv, oacc[db][4 * u + 1] * inv),
-                           pack_bf16x2(oacc[db][4 * u + 2] * inv, oacc[db][4 * u + 3] * inv)};
-                *(u32x2*)(o + qo_off + db * 32 + u * 8 + hh * 4) = w;
-            }
-        if (lse != nullptr && hh == 0)
-            lse[qo_off / D] = (m_run * c + fast_log2(l_run)) * kLn2;
+        for (int u = 0; u < 4; ++u) {
+            u32x2 w = {pack_bf16x2(oacc[db][4 * u] * inv, oacc[db][4 * u + 1] * inv),
+                       pack_bf16x2(oacc[db][4 * u + 2] * inv, oacc[db][4 * u + 3] * inv)};
+            *(u32x2*)(qo_lds + lq * D + (((db * 4 + u) ^ swz<D>(lq)) << 3) + hh * 4) = w;
+        }
+    if (valid && lse != nullptr && hh == 0)
+        lse[qo_off / D] = (m_run * c + fast_log2(l_run)) * kLn2;
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave / QROWS; ++i) {
+        const int lr = i * QROWS + lane / T::CPR;
+        const int cp = lane % T::CPR;
+        const u32x4 val = *(const u32x4*)(qo_lds + lr * D + cp * 8);
+        if (rw0 + lr < rows_total)
+            *(u32x4*)(o + row_off(rw0 + lr) + ((cp ^ swz<D>(lr)) << 3)) = val;
     }
 }
 
