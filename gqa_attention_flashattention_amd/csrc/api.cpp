@@ -226,6 +226,8 @@ int check_prefill_args(const void* q, const void* k, const void* v, const void* 
     if (!finite_positive(scale)) return GQA_ERR_RANGE;
     if (causal && (q_offset < 0 || (int64_t)q_offset + T_q > S_kv)) return GQA_ERR_RANGE;
     if ((int64_t)T_q * (H_q / H_kv) > 0x7fffffff - 256) return GQA_ERR_SHAPE;
+    // a work-group addresses its Q rows (at most 257 tokens) with 32-bit byte offsets
+    if ((int64_t)H_q * d * 2 * 257 > 0x7fffffff) return GQA_ERR_SHAPE;
     return GQA_OK;
 }
 

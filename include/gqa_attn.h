@@ -73,8 +73,10 @@ int gqa_attn_version(void);
  * 0 <= q_offset and q_offset + T_q <= S_kv).  causal == 0: every query sees
  * all S_kv keys and q_offset is ignored.  `scale` multiplies q.k before the
  * softmax (1/sqrt(d) for standard attention).
- * Errors: GQA_ERR_NULL (q, k, v or o NULL), GQA_ERR_SHAPE, GQA_ERR_UNSUPPORTED,
- * GQA_ERR_RANGE (bad q_offset), GQA_ERR_HIP.
+ * Errors: GQA_ERR_NULL (q, k, v or o NULL), GQA_ERR_SHAPE (also for
+ * H_q * d * 514 > 2^31 - 1: a work-group addresses its Q rows with 32-bit
+ * byte offsets), GQA_ERR_UNSUPPORTED, GQA_ERR_RANGE (bad q_offset),
+ * GQA_ERR_HIP.
  */
 int gqa_attn_prefill(const void *q, const void *k, const void *v, void *o, float *lse,
                      int B, int T_q, int S_kv, int H_q, int H_kv, int d, float scale,

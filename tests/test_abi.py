@@ -61,6 +61,7 @@ def _prefill(**kw):
     (dict(d=96), 3), (dict(d=256), 3), (dict(dtype=2), 3),
     (dict(qoff=-1), 4), (dict(qoff=5), 4), (dict(scale=0.0), 4), (dict(scale=float("nan")), 4),
     (dict(scale=-1.0), 4),
+    (dict(Hq=32768, Hkv=2), 2),          # H_q * d * 514 > 2^31 - 1
 ])
 def test_prefill_rejects(kw, code):
     assert _prefill(**kw) == code
