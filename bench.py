@@ -530,6 +530,8 @@ def main():
                     help="quantised-cache decode workloads (reported under decode_quant)")
     ap.add_argument("--multi-workload", default="decode_t4_varlen_b16",
                     help="multi-token decode workload (reported under decode_multi)")
+    ap.add_argument("--scale-workloads", default="decode_varlen_b16,decode_128k",
+                    help="larger plain-decode workloads (reported under decode_at_scale)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", choices=["decode", "prefill", "decode_multi", "prefill_kvsplit",
                                        "prefill_window", "decode_ring", "decode_quant"],
@@ -611,6 +613,12 @@ def main():
     for name in args.quant_workloads.split(","):
         log(f"[bench] decode_quant {name}")
         dquant.append(bench_decode_quant(name, min(args.steps, 200)))
+
+    dscale = []
+    for name in filter(None, args.scale_workloads.split(",")):
+        log(f"[bench] decode_at_scale {name}")
+        dscale.append(bench_decode(name, min(args.steps, 100), 3))
+        torch.cuda.empty_cache()
 
     dw = dec["inp"].workload
     gbs = dec["kv_bytes"] / (dec["ms_call"] * 1e-3) / 1e9
@@ -705,6 +713,25 @@ def main():
                      "algorithmic_bytes_per_call": dring["kv_bytes"],
                      "note": "whole call (split + combine kernels); bytes = resident keys read"},
     }
+    result["decode_at_scale"] = []
+    for ds in dscale:
+        sw = ds["inp"].workload
+        g_call = ds["kv_bytes"] / (ds["ms_call"] * 1e-3) / 1e9
+        g_split = ds["kv_bytes"] / (ds["ms_split"] * 1e-3) / 1e9
+        result["decode_at_scale"].append({
+            "workload": sw.name, "B": sw.B, "H_q": sw.H_q, "H_kv": sw.H_kv, "d": sw.d,
+            "kv_len_range": list(sw.kv_len_range) if sw.kv_len_range else None,
+            "S_kv_max": int(ds["inp"].kv_len.max()), "kv_copies_rotated": ds["n_copies"],
+            "ms_per_call": ds["ms_call"], "value": round(g_call, 2), "unit": "GB/s",
+            "hbm_frac": round(g_call / HBM_PEAK_GBS, 4),
+            "roofline": {"bound": "hbm", "kernel": decode_split_kernel_name(ds["plan"], sw),
+                         "grid_threads": decode_split_grid(ds["plan"], sw),
+                         "achieved": round(g_split, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(g_split / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_launch": ds["kv_bytes"],
+                         "avg_launch_us": round(ds["ms_split"] * 1e3, 3),
+                         "note": "split kernel alone; value is the whole call (split + combine)"},
+        })
     result["decode_quant"] = []
     for dq in dquant:
         qw = dq["inp"].workload
