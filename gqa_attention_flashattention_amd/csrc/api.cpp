@@ -52,8 +52,62 @@ int env_split_len() {
     return cached;
 }
 
+int device_cus();
+
+// Automatic split length.  Two split work-groups are resident per compute
+// unit; with W work-groups in a launch and `slots` resident at once, a slot
+// runs about ceil(W / slots) splits one after another, each of up to L keys
+// plus a fixed cost per work-group (Q load, merge, partial writes) counted as
+// kSplitFixedKeys keys.  The length chosen is the multiple of kSplitAlign in
+// [kMinSplitLen, kMaxSplitLen] that minimises ceil(W / slots) * (L +
+// kSplitFixedKeys) summed over the launches (64 sequences each); ties go to
+// the longer split (fewer partials).  A launch a few work-groups over one
+// round of slots pays a second round: on the 16-sequence ragged batch, 132
+// splits of 2176 keys (528 work-groups) measured 196 us, 127 splits of 2304
+// keys (508) 190 us and 129 splits of 2240 keys (516) 222 us.  With the search
+// that batch runs 189 vs 196 us, four new tokens per sequence 211 vs 220 us
+// and the ring batch 84.9 vs 86.8 us.  Quantised caches, whose splits are
+// bound by code unpacking rather than by bytes, and batches above
+// kSearchMaxBatch take the length that gives about kTargetSplitWorkgroups
+// work-groups (the search picked 4864-key splits for the ragged int8 batch:
+// 116 vs 105 us).
+constexpr int kSearchMaxBatch = 256;
+constexpr int kSplitFixedKeys = 256;
+int64_t auto_split_len(int B, const int32_t* kv_len, int T_q, int G, int H_kv,
+                       gqa::DecodeKind kind, int64_t total_keys, int n_hg) {
+    if (B > kSearchMaxBatch || kind == gqa::DecodeKind::Quant) {
+        int64_t per = (total_keys * H_kv * n_hg + kTargetSplitWorkgroups - 1) /
+                      kTargetSplitWorkgroups;
+        per = (per + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+        return per < kMinSplitLen ? kMinSplitLen : per > kMaxSplitLen ? kMaxSplitLen : per;
+    }
+    int64_t max_len = 0;
+    for (int b = 0; b < B; ++b) max_len = kv_len[b] > max_len ? kv_len[b] : max_len;
+    int64_t hi = (max_len + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+    if (hi > kMaxSplitLen) hi = kMaxSplitLen;
+    if (hi < kMinSplitLen) hi = kMinSplitLen;
+    const int64_t slots = (int64_t)gqa::kDecodeWorkgroupsPerCu * device_cus();
+    int64_t best = kMinSplitLen, best_cost = INT64_MAX;
+    for (int64_t L = kMinSplitLen; L <= hi; L += kSplitAlign) {
+        const int64_t per_split = gqa::decode_workgroups_per_split(kind, T_q, G, H_kv, (int)L);
+        int64_t cost = 0;
+        for (int b0 = 0; b0 < B; b0 += gqa::kDecodeSeqPerLaunch) {
+            const int b1 = B - b0 < gqa::kDecodeSeqPerLaunch ? B : b0 + gqa::kDecodeSeqPerLaunch;
+            int64_t n = 0;
+            for (int b = b0; b < b1; ++b) n += (kv_len[b] + L - 1) / L;
+            cost += (n * per_split + slots - 1) / slots * (L + kSplitFixedKeys);
+        }
+        if (cost <= best_cost) {
+            best_cost = cost;
+            best = L;
+        }
+    }
+    return best;
+}
+
 int make_plan(int B, int T_q, int H_q, int H_kv, const int32_t* kv_len, int num_splits,
-              int32_t* splits, int32_t* lens, Plan* out) {
+              int32_t* splits, int32_t* lens, Plan* out,
+              gqa::DecodeKind kind = gqa::DecodeKind::Bf16) {
     if (kv_len == nullptr) return GQA_ERR_NULL;
     if (B < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv) return GQA_ERR_SHAPE;
     int64_t total_keys = 0;
@@ -66,16 +120,8 @@ int make_plan(int B, int T_q, int H_q, int H_kv, const int32_t* kv_len, int num_
     int64_t auto_len = 0;
     if (num_splits <= 0) {
         int forced = env_split_len();
-        if (forced > 0) {
-            auto_len = forced;
-        } else {
-            int64_t per = (total_keys * H_kv * n_hg + kTargetSplitWorkgroups - 1) /
-                          kTargetSplitWorkgroups;
-            per = (per + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
-            if (per < kMinSplitLen) per = kMinSplitLen;
-            if (per > kMaxSplitLen) per = kMaxSplitLen;
-            auto_len = per;
-        }
+        auto_len = forced > 0 ? forced
+                              : auto_split_len(B, kv_len, T_q, G, H_kv, kind, total_keys, n_hg);
     }
     Plan p;
     for (int b = 0; b < B; ++b) {
@@ -167,11 +213,12 @@ struct HostPlan {
         free(splits);
         free(lens);
     }
-    int build(int B, int H_q, int H_kv, const int32_t* kv_len, int num_splits, int T_q = 1) {
+    int build(int B, int H_q, int H_kv, const int32_t* kv_len, int num_splits, int T_q = 1,
+              gqa::DecodeKind kind = gqa::DecodeKind::Bf16) {
         splits = (int32_t*)malloc(sizeof(int32_t) * (size_t)B);
         lens = (int32_t*)malloc(sizeof(int32_t) * (size_t)B);
         if (!splits || !lens) return GQA_ERR_SHAPE;
-        return make_plan(B, T_q, H_q, H_kv, kv_len, num_splits, splits, lens, &p);
+        return make_plan(B, T_q, H_q, H_kv, kv_len, num_splits, splits, lens, &p, kind);
     }
 };
 
@@ -450,7 +497,7 @@ int gqa_attn_decode_ring(const void* q, const void* k, const void* v, void* o, f
         walk[b] = (int32_t)(s_end + (n - w_lo));
     }
     HostPlan hp;
-    rc = hp.build(B, H_q, H_kv, walk, num_splits, T_q);
+    rc = hp.build(B, H_q, H_kv, walk, num_splits, T_q, gqa::DecodeKind::Ring);
     if (rc) {
         free(walk);
         return rc;
@@ -489,7 +536,7 @@ int gqa_attn_decode_quant(const void* q, const void* k, const void* v, const flo
     for (int b = 0; b < B; ++b)
         if (kv_len[b] < T_q) return GQA_ERR_SHAPE;
     HostPlan hp;
-    rc = hp.build(B, H_q, H_kv, kv_len, num_splits, T_q);
+    rc = hp.build(B, H_q, H_kv, kv_len, num_splits, T_q, gqa::DecodeKind::Quant);
     if (rc) return rc;
     const int rows = T_q * H_q;
     void* base = nullptr;

@@ -845,6 +845,25 @@ int decode_column_blocks_per_group(int T_q, int G) { return T_q * G > kCols ? 2 
 static bool decode_use_wide(int T_q, int G) { return T_q * G > 2 * kCols; }
 static int decode_wide_nhw(int T_q, int G) { return T_q * G > kWideWaves * kCols ? 2 : 1; }
 
+// bf16 splits of at least this many keys take two KV heads per work-group
+// (each wave then walks at least eight 32-key tiles); shorter splits keep one
+// head per work-group and four waves on its tiles, which keeps more waves busy.
+constexpr int kPairMinSplitLen = 512;
+
+int64_t decode_workgroups_per_split(DecodeKind kind, int T_q, int G, int H_kv, int split_len) {
+    int64_t n_hg;
+    bool pairs = false;
+    if (kind == DecodeKind::Bf16 && decode_use_wide(T_q, G)) {
+        n_hg = decode_column_groups(T_q, G);
+    } else {
+        const int nh = decode_column_blocks_per_group(T_q, G);
+        n_hg = (((int64_t)T_q * G + kCols - 1) / kCols + nh - 1) / nh;
+        pairs = kind != DecodeKind::Quant;
+    }
+    const int hp = (pairs && H_kv % 2 == 0 && split_len >= kPairMinSplitLen) ? 2 : 1;
+    return n_hg * (H_kv / hp);
+}
+
 int decode_column_groups(int T_q, int G) {
     const int blocks = (T_q * G + kCols - 1) / kCols;
     const int per = decode_use_wide(T_q, G) ? kWideWaves * decode_wide_nhw(T_q, G)
@@ -888,10 +907,6 @@ static void launch_split(int hp, int64_t units_hg, const void* q, const void* k,
                            ws.l, ws.o, plan, T_q, H_q, H_kv, G, n_hg, c, ring, sc.k, sc.v);
 }
 
-// bf16 splits of at least this many keys take two KV heads per work-group
-// (each wave then walks at least eight 32-key tiles); shorter splits keep one
-// head per work-group and four waves on its tiles, which keeps more waves busy.
-constexpr int kPairMinSplitLen = 512;
 
 template <bool RING, int KVF = kKvBf16>
 static hipError_t split_dispatch(const void* q, const void* k, const void* v,

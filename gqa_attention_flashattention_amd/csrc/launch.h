@@ -61,6 +61,14 @@ hipError_t launch_prefill_split_bf16(const PrefillArgs& a, int n_split, const De
 // query rows (each covers up to 32 rows).
 int decode_column_groups(int T_q, int G);
 
+// Work-groups one split of split_len keys occupies, over all KV heads, for
+// the kernel a decode entry point launches: packed bf16 cache (split or wide
+// kernel), quantised cache, or ring cache.  Two such work-groups are
+// resident per compute unit.
+enum class DecodeKind { Bf16, Quant, Ring };
+int64_t decode_workgroups_per_split(DecodeKind kind, int T_q, int G, int H_kv, int split_len);
+constexpr int kDecodeWorkgroupsPerCu = 2;
+
 // T_q new tokens per sequence (1 for plain decode); partial and output rows are
 // (sequence, token, query head).
 hipError_t launch_decode_split_bf16(const void* q, const void* k, const void* v,

@@ -152,9 +152,13 @@ int gqa_attn_decode(const void *q, const void *k, const void *v, void *o, int B,
  * split s covering keys [s*L_b, min((s+1)*L_b, kv_len[b])):
  *   num_splits > 0:  L_b = ceil(kv_len[b] / min(num_splits, kv_len[b])), so
  *                    n_b <= num_splits (fewer when the division rounds up);
- *   num_splits <= 0: L_b = L for all b, a multiple of 64 chosen so that
- *                    H_kv * sum_b n_b is about four work-groups per compute
- *                    unit, with L between 128 and 8192.
+ *   num_splits <= 0: L_b = L for all b, a multiple of 64 between 128 and
+ *                    8192.  For B <= 256 (bf16 and ring caches) L minimises
+ *                    ceil(W / R) * (L + 256) summed over the launches of 64
+ *                    sequences, W being the split work-groups of a launch and
+ *                    R the number resident at once (two per compute unit);
+ *                    otherwise W is about four per compute unit.  The plan
+ *                    of the device current at the call.
  * Writes (every output pointer may be NULL):
  *   splits[b]        n_b (HOST array [B]),
  *   *split_len       L_b of the longest split over all sequences,

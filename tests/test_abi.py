@@ -219,3 +219,47 @@ def test_auto_plan_targets_occupancy():
     p = gq.decode_plan(1, 64, 8, 128, [8192])
     assert p["split_len"] % 64 == 0 and 128 <= p["split_len"] <= 8192
     assert p["total_splits"] * 8 >= 256
+
+
+def _documented_auto_len(kv_len, H_kv, cus=256):
+    """The automatic split length of gqa_attn_decode_plan as its header states
+    it (bf16 cache, one new token, G <= 16): the multiple of 64 in [128, 8192]
+    minimising ceil(W / R) * (L + 256) summed over launches of 64 sequences,
+    W = split work-groups (H_kv / 2 per split from 512 keys on, else H_kv),
+    R = 2 per compute unit; ties to the longer L."""
+    slots = 2 * cus
+    hi = min(8192, max(128, -(-max(kv_len) // 64) * 64))
+    best, best_cost = None, None
+    for L in range(128, hi + 1, 64):
+        per = H_kv // 2 if (H_kv % 2 == 0 and L >= 512) else H_kv
+        cost = 0
+        for b0 in range(0, len(kv_len), 64):
+            n = sum(-(-x // L) for x in kv_len[b0:b0 + 64])
+            cost += -(-(n * per) // slots) * (L + 256)
+        if best_cost is None or cost <= best_cost:
+            best, best_cost = L, cost
+    return best
+
+
+@pytest.mark.parametrize("seed,B", [(0, 1), (1, 3), (2, 16), (3, 16), (4, 70), (5, 200)])
+def test_auto_plan_follows_the_documented_rule(seed, B):
+    """Without a device (256 compute units assumed, as on MI355X) the
+    automatic split length is the argmin of the documented cost."""
+    rng = np.random.default_rng(seed)
+    kv_len = rng.integers(1, 40000, size=B).tolist()
+    p = gq.decode_plan(B, 64, 8, 128, kv_len)
+    assert p["split_len"] == _documented_auto_len(kv_len, 8)
+
+
+def test_auto_plan_on_the_benchmark_batches():
+    """One full round of resident work-groups where that is cheapest: the
+    16-sequence ragged batch takes 127 splits of 2304 keys (508 work-groups,
+    two KV heads each), decode_8k 64 splits of 128 keys (512)."""
+    from gqa_attention_flashattention_amd import inputs as gin
+    kv_len = gin.kv_lengths(gin.WORKLOADS["decode_varlen_b16"], np.random.default_rng(0))
+    p = gq.decode_plan(16, 64, 8, 128, kv_len)
+    assert (p["split_len"], p["total_splits"]) == (2304, 127)
+    p = gq.decode_plan(1, 64, 8, 128, [8192])
+    assert (p["split_len"], p["total_splits"]) == (128, 64)
+    p = gq.decode_plan(1, 64, 8, 128, [131072])
+    assert (p["split_len"], p["total_splits"]) == (1024, 128)
