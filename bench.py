@@ -400,7 +400,7 @@ def cpu_baseline_decode(inp, kv_bytes, min_seconds=10.0):
                        f"every key), {reps} passes in {el:.1f} s"), o, lse
 
 
-def cpu_baseline_prefill(inp, rows, min_seconds=5.0):
+def cpu_baseline_prefill(inp, rows, min_seconds=10.0):
     import oracle
     w = inp.workload
     threads = oracle.num_threads(cpu_threads())
