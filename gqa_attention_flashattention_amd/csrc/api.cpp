@@ -58,10 +58,12 @@ int device_cus();
 // unit; with W work-groups in a launch and `slots` resident at once, a slot
 // runs about ceil(W / slots) splits one after another, each of up to L keys
 // plus a fixed cost per work-group (Q load, merge, partial writes) counted as
-// kSplitFixedKeys keys.  The length chosen is the multiple of kSplitAlign in
-// [kMinSplitLen, kMaxSplitLen] that minimises ceil(W / slots) * (L +
-// kSplitFixedKeys) summed over the launches (64 sequences each); ties go to
-// the longer split (fewer partials).  A launch a few work-groups over one
+// kSplitFixedKeys keys.  The length chosen is the candidate in [kMinSplitLen,
+// kMaxSplitLen] that minimises ceil(W / slots) * (L + kSplitFixedKeys) summed
+// over the launches (64 sequences each); ties go to the longer split (fewer
+// partials).  Candidates: multiples of 64 up to 1024, of 128 up to 2048, of
+// 256 beyond (47 at most; the search costs ~10 us of host time at 64
+// sequences).  A launch a few work-groups over one
 // round of slots pays a second round: on the 16-sequence ragged batch, 132
 // splits of 2176 keys (528 work-groups) measured 196 us, 127 splits of 2304
 // keys (508) 190 us and 129 splits of 2240 keys (516) 222 us.  With the search
@@ -88,7 +90,7 @@ int64_t auto_split_len(int B, const int32_t* kv_len, int T_q, int G, int H_kv,
     if (hi < kMinSplitLen) hi = kMinSplitLen;
     const int64_t slots = (int64_t)gqa::kDecodeWorkgroupsPerCu * device_cus();
     int64_t best = kMinSplitLen, best_cost = INT64_MAX;
-    for (int64_t L = kMinSplitLen; L <= hi; L += kSplitAlign) {
+    for (int64_t L = kMinSplitLen; L <= hi; L += L < 1024 ? 64 : L < 2048 ? 128 : 256) {
         const int64_t per_split = gqa::decode_workgroups_per_split(kind, T_q, G, H_kv, (int)L);
         int64_t cost = 0;
         for (int b0 = 0; b0 < B; b0 += gqa::kDecodeSeqPerLaunch) {

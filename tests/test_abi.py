@@ -223,14 +223,17 @@ def test_auto_plan_targets_occupancy():
 
 def _documented_auto_len(kv_len, H_kv, cus=256):
     """The automatic split length of gqa_attn_decode_plan as its header states
-    it (bf16 cache, one new token, G <= 16): the multiple of 64 in [128, 8192]
+    it (bf16 cache, one new token, G <= 16): the candidate in [128, 8192]
+    (multiples of 64 up to 1024, of 128 up to 2048, of 256 beyond)
     minimising ceil(W / R) * (L + 256) summed over launches of 64 sequences,
     W = split work-groups (H_kv / 2 per split from 512 keys on, else H_kv),
     R = 2 per compute unit; ties to the longer L."""
     slots = 2 * cus
     hi = min(8192, max(128, -(-max(kv_len) // 64) * 64))
     best, best_cost = None, None
-    for L in range(128, hi + 1, 64):
+    cands = [L for L in range(128, hi + 1, 64)
+             if L <= 1024 or (L <= 2048 and L % 128 == 0) or L % 256 == 0]
+    for L in cands:
         per = H_kv // 2 if (H_kv % 2 == 0 and L >= 512) else H_kv
         cost = 0
         for b0 in range(0, len(kv_len), 64):
