@@ -534,11 +534,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // One wave per (sequence, query head, 32-dim chunk of O).  Lane (sg, dq):
 // split group sg = lane / 8 takes splits sg, sg + 8, sg + 16, ...; dim quad
 // dq = lane % 8 owns dims 4 dq .. 4 dq + 3 of the chunk.  A lane loads a
-// batch of its splits at once and folds them into a running (m, l, O) with
-// the section 4 merge; the eight split groups are then merged with a fixed
-// butterfly, so the result does not depend on timing (bitwise reproducible
-// for a given split plan).  All in base 2.
-constexpr int kCombineBatch = 8;
+// batch of NB of its splits at once and folds them, in split order, into a
+// running (m, l, O) with the section 4 merge; the eight split groups are then
+// merged with a fixed butterfly, so the result does not depend on timing
+// (bitwise reproducible for a given split plan, and the same for every NB: a
+// missing split folds in as an exact no-op).  NB follows the launch's
+// longest sequence, so short plans do not issue loads for absent splits.
+// All in base 2.
 
 __device__ __forceinline__ void merge_lse(float& m, float& l, f32x4& o, float m2, float l2,
                                           const f32x4& o2) {
@@ -550,7 +552,7 @@ __device__ __forceinline__ void merge_lse(float& m, float& l, f32x4& o, float m2
     m = mm;
 }
 
-template <int D>
+template <int D, int NB>
 __global__ __launch_bounds__(64) void decode_combine_kernel(
     const float* __restrict__ ws_m, const float* __restrict__ ws_l,
     const float* __restrict__ ws_o, uint16_t* __restrict__ o, float* __restrict__ lse,
@@ -570,11 +572,11 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
     const int dim = chunk * 32 + dq * 4;
     float m = -INFINITY, l = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = sg; s0 < n; s0 += 8 * kCombineBatch) {
-        float mv[kCombineBatch], lv[kCombineBatch];
-        f32x4 ov[kCombineBatch];
+    for (int s0 = sg; s0 < n; s0 += 8 * NB) {
+        float mv[NB], lv[NB];
+        f32x4 ov[NB];
 #pragma unroll
-        for (int u = 0; u < kCombineBatch; ++u) {
+        for (int u = 0; u < NB; ++u) {
             const int s = s0 + 8 * u;
             const int64_t hrow = (p0 + (s < n ? s : 0)) * R + r;
             mv[u] = s < n ? ws_m[hrow] : -INFINITY;
@@ -583,7 +585,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
             if (s >= n) ov[u] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
-        for (int u = 0; u < kCombineBatch; ++u) merge_lse(m, l, acc, mv[u], lv[u], ov[u]);
+        for (int u = 0; u < NB; ++u) merge_lse(m, l, acc, mv[u], lv[u], ov[u]);
     }
 #pragma unroll
     for (int step = 0; step < 3; ++step) {   // partner lanes l ^ 8, l ^ 16, l ^ 32
@@ -988,12 +990,26 @@ hipError_t launch_decode_combine_bf16(const DecodeWorkspace& ws, const DecodePla
                                       hipStream_t stream) {
     const int64_t grid = (int64_t)plan.nseq * T_q * H_q * (d / 32);   // one wave per item
     if (grid < 1 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    if (d == 128)
-        hipLaunchKernelGGL((decode_combine_kernel<128>), dim3((unsigned)grid), dim3(64), 0, stream,
-                           ws.m, ws.l, ws.o, (uint16_t*)o, lse, plan, T_q, H_q);
-    else
-        hipLaunchKernelGGL((decode_combine_kernel<64>), dim3((unsigned)grid), dim3(64), 0, stream,
-                           ws.m, ws.l, ws.o, (uint16_t*)o, lse, plan, T_q, H_q);
+    int max_n = 1;
+    for (int i = 0; i < plan.nseq; ++i)
+        max_n = std::max(max_n, (int)(plan.unit_base[i + 1] - plan.unit_base[i]));
+    const int per_lane = (max_n + 7) / 8;   // splits of one lane group
+    const int nb = per_lane <= 1 ? 1 : per_lane <= 2 ? 2 : per_lane <= 4 ? 4 : 8;
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(64), 0, stream, ws.m, ws.l, ws.o,
+                           (uint16_t*)o, lse, plan, T_q, H_q);
+    };
+    if (d == 128) {
+        if (nb == 1) go(decode_combine_kernel<128, 1>);
+        else if (nb == 2) go(decode_combine_kernel<128, 2>);
+        else if (nb == 4) go(decode_combine_kernel<128, 4>);
+        else go(decode_combine_kernel<128, 8>);
+    } else {
+        if (nb == 1) go(decode_combine_kernel<64, 1>);
+        else if (nb == 2) go(decode_combine_kernel<64, 2>);
+        else if (nb == 4) go(decode_combine_kernel<64, 4>);
+        else go(decode_combine_kernel<64, 8>);
+    }
     return hipGetLastError();
 }
 
