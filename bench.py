@@ -326,6 +326,41 @@ def bench_decode_quant(name, steps):
                 o_gpu=out.float().cpu().numpy(), lse_gpu=lse.cpu().numpy())
 
 
+def bench_decode_ring_quant(name, steps):
+    """Quantised ring-buffer decode (the pccx base configuration) over rotated
+    copies of the code tensors; bytes = codes of the resident keys read."""
+    import torch
+    import gqa_attention_flashattention_amd as gq
+    from gqa_attention_flashattention_amd import inputs as gin
+    inp = gin.make_quant(name)
+    w = inp.workload
+    pack = (lambda c: c) if w.kv_bits == 8 else gin.pack_int4
+    k0 = torch.from_numpy(pack(inp.k_codes)).cuda()
+    v0 = torch.from_numpy(pack(inp.v_codes)).cuda()
+    walk = ring_walk_lengths(w, inp.kv_len)
+    kv_bytes = int(walk.sum()) * w.H_kv * (w.d * w.kv_bits // 8) * 2
+    n_copies = max(1, min(64, math.ceil(ROTATE_BYTES / kv_bytes)))
+    ks = [k0] + [k0.clone() for _ in range(n_copies - 1)]
+    vs = [v0] + [v0.clone() for _ in range(n_copies - 1)]
+    q = dev_tensor(inp.q_store)
+    ksc = torch.from_numpy(inp.k_scale).cuda()
+    vsc = torch.from_numpy(inp.v_scale).cuda()
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+
+    def call(i):
+        return lambda: gq.decode_ring_quant(q, ks[i % n_copies], vs[i % n_copies], ksc, vsc,
+                                            inp.kv_len, kv_bits=w.kv_bits, window=w.window,
+                                            sink=w.sink, out=out, lse=lse)
+
+    for i in range(3):
+        call(i)()
+    torch.cuda.synchronize()
+    ms = time_graph([call(i) for i in range(steps)])
+    return dict(inp=inp, ms=ms, kv_bytes=kv_bytes, n_copies=n_copies,
+                o_gpu=out.float().cpu().numpy(), lse_gpu=lse.cpu().numpy())
+
+
 def copy_calibration(mib: int):
     """A plain device-to-device copy of `mib` MiB, three times (rocprofv3
     counter runs scale FETCH_SIZE / WRITE_SIZE by what this copy reads)."""
@@ -491,6 +526,32 @@ def parity_decode_ring(dr, n_seq=2):
             "decode_ring_sample_max_abs_dLSE": float(max(el))}
 
 
+def parity_decode_ring_quant(dr, n_seq=2):
+    """Oracle check of the first n_seq sequences: the dequantised ring cache
+    unwrapped by the ring rule, through the window oracle."""
+    import oracle
+    inp = dr["inp"]
+    w = inp.workload
+    wrap = w.capacity - w.sink
+    eo, el = [], []
+    for b, n in enumerate(np.asarray(inp.kv_len).tolist()[:n_seq]):
+        kd = oracle.dequantize(inp.k_codes[b], inp.k_scale)
+        vd = oracle.dequantize(inp.v_codes[b], inp.v_scale)
+        pos = np.arange(n)
+        keep = (pos < w.sink) | (pos >= n - wrap)
+        slot = np.where(pos < w.sink, pos, w.sink + (pos - w.sink) % wrap)
+        kl = np.zeros((n, w.H_kv, w.d), np.float32)
+        vl = np.zeros((n, w.H_kv, w.d), np.float32)
+        kl[keep] = kd[slot[keep]]
+        vl[keep] = vd[slot[keep]]
+        o, l = oracle.prefill_window(inp.q[b:b + 1], kl[None], vl[None], q_offset=n - w.T_q,
+                                     window=w.window, sink=w.sink)
+        eo.append(np.abs(dr["o_gpu"][b] - o[0]).max())
+        el.append(np.abs(dr["lse_gpu"][b] - l[0]).max())
+    return {"decode_ring_quant_sample_max_abs_dO": float(max(eo)),
+            "decode_ring_quant_sample_max_abs_dLSE": float(max(el))}
+
+
 def parity_decode_quant(dq, n_seq=1):
     """Oracle over the dequantised cache for the first n_seq sequences."""
     import oracle
@@ -530,11 +591,14 @@ def main():
                     help="quantised-cache decode workloads (reported under decode_quant)")
     ap.add_argument("--multi-workload", default="decode_t4_varlen_b16",
                     help="multi-token decode workload (reported under decode_multi)")
+    ap.add_argument("--ring-quant-workload", default="decode_ring_int4_b16",
+                    help="quantised ring-buffer decode workload (reported under decode_ring_quant)")
     ap.add_argument("--scale-workloads", default="decode_varlen_b16,decode_128k",
                     help="larger plain-decode workloads (reported under decode_at_scale)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", choices=["decode", "prefill", "decode_multi", "prefill_kvsplit",
-                                       "prefill_window", "decode_ring", "decode_quant"],
+                                       "prefill_window", "decode_ring", "decode_quant",
+                                       "decode_ring_quant"],
                     default=None,
                     help="run one path only (profiling runs); prints a partial line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -568,6 +632,11 @@ def main():
         dr = bench_decode_ring(args.ring_workload, min(args.steps, 200))
         log(f"[bench] decode_ring {dr['ms'] * 1e3:.1f} us/call "
             f"{dr['kv_bytes'] / (dr['ms'] * 1e-3) / 1e9:.1f} GB/s")
+        return
+    if args.only == "decode_ring_quant":
+        drq = bench_decode_ring_quant(args.ring_quant_workload, min(args.steps, 200))
+        log(f"[bench] decode_ring_quant {drq['ms'] * 1e3:.1f} us/call "
+            f"{drq['kv_bytes'] / (drq['ms'] * 1e-3) / 1e9:.1f} GB/s")
         return
     if args.only == "decode_quant":
         for name in args.quant_workloads.split(","):
@@ -613,6 +682,9 @@ def main():
     for name in args.quant_workloads.split(","):
         log(f"[bench] decode_quant {name}")
         dquant.append(bench_decode_quant(name, min(args.steps, 200)))
+
+    log(f"[bench] decode_ring_quant {args.ring_quant_workload}")
+    dringq = bench_decode_ring_quant(args.ring_quant_workload, min(args.steps, 200))
 
     dscale = []
     for name in filter(None, args.scale_workloads.split(",")):
@@ -713,6 +785,19 @@ def main():
                      "algorithmic_bytes_per_call": dring["kv_bytes"],
                      "note": "whole call (split + combine kernels); bytes = resident keys read"},
     }
+    qw = dringq["inp"].workload
+    gbs_rq = dringq["kv_bytes"] / (dringq["ms"] * 1e-3) / 1e9
+    result["decode_ring_quant"] = {
+        "workload": qw.name, "kv_bits": qw.kv_bits, "B": qw.B, "T_q": qw.T_q,
+        "capacity": qw.capacity, "window": qw.window, "sink": qw.sink,
+        "kv_len_range": list(qw.kv_len_range), "ms_per_call": dringq["ms"],
+        "value": round(gbs_rq, 2), "unit": "GB/s", "kv_copies_rotated": dringq["n_copies"],
+        "bf16_equivalent_GBps": round(gbs_rq * 16 / qw.kv_bits, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbs_rq, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs_rq / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes_per_call": dringq["kv_bytes"],
+                     "note": "whole call; bytes = codes of the resident keys read"},
+    }
     result["decode_at_scale"] = []
     for ds in dscale:
         sw = ds["inp"].workload
@@ -766,6 +851,8 @@ def main():
         for dq in dquant:
             log(f"[bench] oracle check ({dq['inp'].workload.name} sample)")
             result["parity"].update(parity_decode_quant(dq))
+        log("[bench] oracle check (decode_ring_quant sample)")
+        result["parity"].update(parity_decode_ring_quant(dringq))
         log("[bench] oracle check (decode_multi sample)")
         result["parity"].update(parity_decode_multi(mul))
     print(json.dumps(result), flush=True)

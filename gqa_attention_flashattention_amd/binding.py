@@ -70,6 +70,9 @@ def load_library():
     lib.gqa_attn_decode_ring.restype = i
     lib.gqa_attn_decode_ring.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, i, f, i, i,
                                          vp]
+    lib.gqa_attn_decode_ring_quant.restype = i
+    lib.gqa_attn_decode_ring_quant.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp,
+                                               i, i, i, f, i, vp]
     lib.gqa_attn_decode_multi.restype = i
     lib.gqa_attn_decode_multi.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, f, i, i, vp]
     lib.gqa_attn_decode_combine.restype = i
@@ -387,6 +390,46 @@ def decode_ring(q, k_cache, v_cache, kv_len, *, window: int, sink: int = 0,
         k_cache.shape[2], d, k_cache.shape[1], a.ctypes.data, int(window), int(sink),
         float(scale), int(num_splits), _dtype_code(q), _stream(q.device))
     _check(rc, "gqa_attn_decode_ring")
+    return out, lse
+
+
+def decode_ring_quant(q, k_codes, v_codes, k_scale, v_scale, kv_len, *, kv_bits: int,
+                      window: int, sink: int = 0, scale: float | None = None,
+                      num_splits: int = 0, out=None, lse=None, return_lse: bool = True):
+    """Decode over a quantised ring-buffer cache.  q [B,T_q,H_q,d] bf16;
+    k_codes/v_codes 1-byte tensors [B,capacity,H_kv,d] (int8, kv_bits=8) or
+    [B,capacity,H_kv,d/2] (two int4 codes per byte, kv_bits=4); k_scale/v_scale
+    fp32 [H_kv,d]; kv_len = tokens written per sequence.  Returns (o, lse)."""
+    import torch
+    _require(q, "q", 4)
+    _require(k_codes, "k_codes", 4)
+    _require(v_codes, "v_codes", 4)
+    B, T_q, H_q, d = q.shape
+    width = d if kv_bits == 8 else d // 2
+    if (k_codes.shape != v_codes.shape or k_codes.shape[0] != B
+            or k_codes.shape[3] != width):
+        raise GQAError(f"k/v codes must be [B, capacity, H_kv, {width}] bytes", 2)
+    if k_codes.element_size() != 1 or v_codes.element_size() != 1:
+        raise GQAError("k/v codes must be 1-byte tensors", 3)
+    if q.dtype != torch.bfloat16:
+        raise GQAError("q must be bf16", 3)
+    if k_codes.device != q.device or v_codes.device != q.device:
+        raise GQAError(f"k/v codes must be on {q.device}", 2)
+    H_kv = k_codes.shape[2]
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        _require(t, name, 2)
+        if t.dtype != torch.float32 or tuple(t.shape) != (H_kv, d) or t.device != q.device:
+            raise GQAError(f"{name} must be fp32 [{H_kv}, {d}] on {q.device}", 2)
+    a = _kv_len_array(kv_len, B)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = _out_like(out, q, (B, T_q, H_q, d))
+    lse = _lse_buf(lse, q, (B, T_q, H_q), return_lse)
+    rc = load_library().gqa_attn_decode_ring_quant(
+        _ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_scale), _ptr(v_scale), _ptr(out),
+        _ptr(lse), B, T_q, H_q, H_kv, d, k_codes.shape[1], a.ctypes.data, int(window),
+        int(sink), int(kv_bits), float(scale), int(num_splits), _stream(q.device))
+    _check(rc, "gqa_attn_decode_ring_quant")
     return out, lse
 
 

@@ -473,12 +473,15 @@ int gqa_attn_prefill_kvsplit_count(int B, int T_q, int S_kv, int H_q, int H_kv, 
     return prefill_splits(B, T_q, S_kv, H_q, H_kv, d, causal, causal ? q_offset : 0, num_splits);
 }
 
-int gqa_attn_decode_ring(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                         int T_q, int H_q, int H_kv, int d, int capacity, const int32_t* kv_len,
-                         int window, int sink, float scale, int num_splits, int dtype,
-                         void* stream) {
-    int rc = check_decode_args(q, k, v, B, H_q, H_kv, d, kv_len, scale, dtype);
-    if (rc) return rc;
+}  // extern "C"
+
+namespace {
+
+// Ring-buffer decode over a bf16 cache (bits = 16) or int8 / int4 codes.
+int decode_ring_impl(const void* q, const void* k, const void* v, const float* k_scale,
+                     const float* v_scale, int bits, void* o, float* lse, int B, int T_q,
+                     int H_q, int H_kv, int d, int capacity, const int32_t* kv_len, int window,
+                     int sink, float scale, int num_splits, void* stream) {
     if (!o) return GQA_ERR_NULL;
     if (T_q < 1 || T_q > kMaxDecodeTokens || capacity < 1) return GQA_ERR_SHAPE;
     // every key a new token may see must still be resident
@@ -499,7 +502,8 @@ int gqa_attn_decode_ring(const void* q, const void* k, const void* v, void* o, f
         walk[b] = (int32_t)(s_end + (n - w_lo));
     }
     HostPlan hp;
-    rc = hp.build(B, H_q, H_kv, walk, num_splits, T_q, gqa::DecodeKind::Ring);
+    int rc = hp.build(B, H_q, H_kv, walk, num_splits, T_q,
+                      bits == 16 ? gqa::DecodeKind::Ring : gqa::DecodeKind::Quant);
     if (rc) {
         free(walk);
         return rc;
@@ -515,8 +519,8 @@ int gqa_attn_decode_ring(const void* q, const void* k, const void* v, void* o, f
     const gqa::RingArgs ring{capacity, sink, window};
     (void)hipGetLastError();
     rc = for_each_chunk(B, walk, hp.splits, hp.lens, [&](const DecodePlanChunk& c) {
-        return gqa::launch_decode_ring_split_bf16(q, k, v, ws, c, T_q, H_q, H_kv, d, scale, ring,
-                                                  (hipStream_t)stream);
+        return gqa::launch_decode_ring_split(q, k, v, k_scale, v_scale, bits, ws, c, T_q, H_q,
+                                             H_kv, d, scale, ring, (hipStream_t)stream);
     }, capacity, kv_len);
     if (!rc)
         rc = for_each_chunk(B, walk, hp.splits, hp.lens, [&](const DecodePlanChunk& c) {
@@ -524,6 +528,33 @@ int gqa_attn_decode_ring(const void* q, const void* k, const void* v, void* o, f
         }, capacity, kv_len);
     free(walk);
     return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_attn_decode_ring(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                         int T_q, int H_q, int H_kv, int d, int capacity, const int32_t* kv_len,
+                         int window, int sink, float scale, int num_splits, int dtype,
+                         void* stream) {
+    const int rc = check_decode_args(q, k, v, B, H_q, H_kv, d, kv_len, scale, dtype);
+    if (rc) return rc;
+    return decode_ring_impl(q, k, v, nullptr, nullptr, 16, o, lse, B, T_q, H_q, H_kv, d, capacity,
+                            kv_len, window, sink, scale, num_splits, stream);
+}
+
+int gqa_attn_decode_ring_quant(const void* q, const void* k, const void* v, const float* k_scale,
+                               const float* v_scale, void* o, float* lse, int B, int T_q,
+                               int H_q, int H_kv, int d, int capacity, const int32_t* kv_len,
+                               int window, int sink, int kv_bits, float scale, int num_splits,
+                               void* stream) {
+    const int rc = check_decode_args(q, k, v, B, H_q, H_kv, d, kv_len, scale, GQA_BF16);
+    if (rc) return rc;
+    if (!k_scale || !v_scale) return GQA_ERR_NULL;
+    if (kv_bits != 8 && kv_bits != 4) return GQA_ERR_UNSUPPORTED;
+    return decode_ring_impl(q, k, v, k_scale, v_scale, kv_bits, o, lse, B, T_q, H_q, H_kv, d,
+                            capacity, kv_len, window, sink, scale, num_splits, stream);
 }
 
 int gqa_attn_decode_quant(const void* q, const void* k, const void* v, const float* k_scale,

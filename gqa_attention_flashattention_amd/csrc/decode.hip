@@ -978,11 +978,21 @@ hipError_t launch_decode_quant_split(const void* q, const void* k, const void* v
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode_ring_split_bf16(const void* q, const void* k, const void* v,
-                                         const DecodeWorkspace& ws, const DecodePlanChunk& plan,
-                                         int T_q, int H_q, int H_kv, int d, float scale,
-                                         const RingArgs& ring, hipStream_t stream) {
-    return split_dispatch<true>(q, k, v, ws, plan, T_q, H_q, H_kv, d, scale, ring, stream);
+hipError_t launch_decode_ring_split(const void* q, const void* k, const void* v,
+                                    const float* k_scale, const float* v_scale, int bits,
+                                    const DecodeWorkspace& ws, const DecodePlanChunk& plan,
+                                    int T_q, int H_q, int H_kv, int d, float scale,
+                                    const RingArgs& ring, hipStream_t stream) {
+    const KvScales sc{k_scale, v_scale};
+    if (bits == 16)
+        return split_dispatch<true>(q, k, v, ws, plan, T_q, H_q, H_kv, d, scale, ring, stream);
+    if (bits == 8)
+        return split_dispatch<true, kKvInt8>(q, k, v, ws, plan, T_q, H_q, H_kv, d, scale, ring,
+                                             stream, sc);
+    if (bits == 4)
+        return split_dispatch<true, kKvInt4>(q, k, v, ws, plan, T_q, H_q, H_kv, d, scale, ring,
+                                             stream, sc);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode_combine_bf16(const DecodeWorkspace& ws, const DecodePlanChunk& plan,

@@ -94,10 +94,13 @@ struct RingArgs {
     int sink;
     int window;
 };
-hipError_t launch_decode_ring_split_bf16(const void* q, const void* k, const void* v,
-                                         const DecodeWorkspace& ws, const DecodePlanChunk& plan,
-                                         int T_q, int H_q, int H_kv, int d, float scale,
-                                         const RingArgs& ring, hipStream_t stream);
+// bits = 16: bf16 cache; 8 / 4: quantised codes as launch_decode_quant_split
+// (k_scale, v_scale fp32 [H_kv, d]), [B, capacity, H_kv, d or d/2] bytes.
+hipError_t launch_decode_ring_split(const void* q, const void* k, const void* v,
+                                    const float* k_scale, const float* v_scale, int bits,
+                                    const DecodeWorkspace& ws, const DecodePlanChunk& plan,
+                                    int T_q, int H_q, int H_kv, int d, float scale,
+                                    const RingArgs& ring, hipStream_t stream);
 hipError_t launch_decode_combine_bf16(const DecodeWorkspace& ws, const DecodePlanChunk& plan,
                                       void* o, float* lse, int T_q, int H_q, int d,
                                       hipStream_t stream);

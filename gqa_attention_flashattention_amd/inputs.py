@@ -72,6 +72,9 @@ WORKLOADS = {
                  kv_len_range=(1024, 32768), kv_bits=4),
         Workload("decode_t4_varlen_b16", "decode", "bf16", B=16, H_q=64, H_kv=8, d=128,
                  T_q=4, kv_len_range=(1024, 32768)),
+        # the pccx base configuration: INT4 KV in an 8192-token hard-cap ring
+        Workload("decode_ring_int4_b16", "decode", "bf16", B=16, H_q=64, H_kv=8, d=128,
+                 kv_len_range=(1024, 32768), capacity=8192, window=8188, sink=4, kv_bits=4),
     ]
 }
 
@@ -177,7 +180,7 @@ class QuantInputs:
 
 
 def quant_case(*, B: int, H_q: int, H_kv: int, d: int, kv_len, kv_bits: int, T_q: int = 1,
-               seed: int = 0, name: str = "custom") -> QuantInputs:
+               seed: int = 0, name: str = "custom", capacity: int = 0) -> QuantInputs:
     """Seeded quantised-cache case.  Draw order: kv_len (if a range workload
     drew it), Q, K codes, V codes, K scales, V scales.  Codes are rounded
     normals clipped to the code range (sigma = 127/4 for int8, 7/3 for int4);
@@ -185,17 +188,20 @@ def quant_case(*, B: int, H_q: int, H_kv: int, d: int, kv_len, kv_bits: int, T_q
     so values are roughly standard normal."""
     rng = np.random.default_rng(seed)
     return _quant_draw(rng, Workload(name, "decode", "bf16", B=B, H_q=H_q, H_kv=H_kv, d=d,
-                                     T_q=T_q, kv_bits=kv_bits), np.asarray(kv_len, np.int32))
+                                     T_q=T_q, kv_bits=kv_bits, capacity=capacity),
+                       np.asarray(kv_len, np.int32))
 
 
 def _quant_draw(rng, w: Workload, kv_len: np.ndarray) -> QuantInputs:
     total = int(kv_len.astype(np.int64).sum())
+    # packed cache [sum kv_len, H_kv, d]; ring cache [B, capacity, H_kv, d]
+    rows = (w.B, w.capacity) if w.capacity > 0 else (total,)
     qs = (w.B, w.T_q, w.H_q, w.d)
     q = rng.standard_normal(qs, dtype=np.float32)
     lo, hi, sigma, unit = (-128, 127, 127 / 4, 4 / 127) if w.kv_bits == 8 else (-8, 7, 7 / 3, 3 / 7)
     codes = []
     for _ in range(2):
-        c = np.rint(rng.standard_normal((total, w.H_kv, w.d)) * sigma)
+        c = np.rint(rng.standard_normal(rows + (w.H_kv, w.d)) * sigma)
         codes.append(np.clip(c, lo, hi).astype(np.int8))
     scales = []
     for _ in range(2):

@@ -277,6 +277,29 @@ int gqa_attn_decode_ring(const void *q, const void *k, const void *v, void *o, f
                          int window, int sink, float scale, int num_splits, int dtype,
                          void *stream);
 
+/*
+ * Decode over a quantised hard-cap ring-buffer cache: the base configuration
+ * of the pccx page ("Gemma 3N E4B on pccx v002 -- Execution / Scheduling",
+ * section 6: INT4 KV cache with an 8192-token hard cap; section 4 items 2
+ * and 3).  The ring layout, kv_len, window, sink and their requirements are
+ * those of gqa_attn_decode_ring; the codes and scales those of
+ * gqa_attn_decode_quant:
+ *   k, v [B, capacity, H_kv, d] int8 codes (kv_bits = 8) or
+ *        [B, capacity, H_kv, d/2] bytes of two int4 codes (kv_bits = 4,
+ *        channel 2i in the low nibble of byte i);
+ *   k_scale, v_scale fp32 [H_kv, d] (device);
+ *   q, o [B, T_q, H_q, d] bf16; lse [B, T_q, H_q] fp32, may be NULL.
+ * The result is gqa_attn_decode_ring's over the dequantised cache (value =
+ * code * scale).  Library-owned workspace as gqa_attn_decode.
+ * Errors: GQA_ERR_NULL, GQA_ERR_SHAPE, GQA_ERR_UNSUPPORTED (kv_bits, d),
+ * GQA_ERR_RANGE (sink/window/capacity, scale), GQA_ERR_HIP.
+ */
+int gqa_attn_decode_ring_quant(const void *q, const void *k, const void *v, const float *k_scale,
+                               const float *v_scale, void *o, float *lse, int B, int T_q,
+                               int H_q, int H_kv, int d, int capacity, const int32_t *kv_len,
+                               int window, int sink, int kv_bits, float scale, int num_splits,
+                               void *stream);
+
 #ifdef __cplusplus
 }
 #endif

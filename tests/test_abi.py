@@ -26,7 +26,7 @@ def test_header_declares_the_boundary():
               "gqa_attn_decode_combine", "gqa_attn_decode_plan", "gqa_attn_decode_multi",
               "gqa_attn_prefill_kvsplit", "gqa_attn_prefill_kvsplit_count",
               "gqa_attn_prefill_window", "gqa_attn_decode_ring", "gqa_attn_decode_quant",
-              "gqa_attn_status_string", "gqa_attn_version"]:
+              "gqa_attn_decode_ring_quant", "gqa_attn_status_string", "gqa_attn_version"]:
         assert n in names
 
 
@@ -167,6 +167,23 @@ def test_quant_decode_rejects():
     assert call(q=None) == 1 and call(o=None) == 1 and call(ks=None) == 1 and call(vs=None) == 1
     assert call(bits=2) == 3 and call(bits=16) == 3 and call(d=32) == 3
     assert call(T=0) == 2 and call(kv=(1,), T=2) == 2 and call(kv=(0,)) == 2
+
+
+def test_ring_quant_decode_rejects():
+    lib = gq.load_library()
+
+    def call(kv=(10,), **kw):
+        a = dict(q=P, o=P, ks=P, vs=P, T=2, cap=16, window=10, sink=4, bits=4, d=128)
+        a.update(kw)
+        arr = np.asarray(kv, np.int32)
+        return lib.gqa_attn_decode_ring_quant(a["q"], P, P, a["ks"], a["vs"], a["o"], None,
+                                              len(kv), a["T"], 8, 2, a["d"], a["cap"],
+                                              arr.ctypes.data, a["window"], a["sink"], a["bits"],
+                                              0.1, 0, None)
+    assert call(q=None) == 1 and call(o=None) == 1 and call(ks=None) == 1 and call(vs=None) == 1
+    assert call(bits=2) == 3 and call(bits=16) == 3 and call(d=32) == 3
+    assert call(kv=(1,)) == 2 and call(T=0) == 2 and call(cap=0) == 2
+    assert call(sink=16) == 4 and call(window=0) == 4 and call(window=13) == 4
 
 
 def test_split_and_combine_reject_small_workspace():
