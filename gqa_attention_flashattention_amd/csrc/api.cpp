@@ -68,8 +68,8 @@ int device_cus();
 // splits of 2176 keys (528 work-groups) measured 196 us, 127 splits of 2304
 // keys (508) 190 us and 129 splits of 2240 keys (516) 222 us.  With the search
 // that batch runs 189 vs 196 us, four new tokens per sequence 211 vs 220 us
-// and the ring batch 84.9 vs 86.8 us.  Quantised caches, whose splits are
-// bound by code unpacking rather than by bytes, and batches above
+// and the ring batch 84.9 vs 86.8 us; int4 codes: the ragged batch 76 vs 84
+// us, the 8192-slot ring 39.4 vs 47.7 us.  int8 codes and batches above
 // kSearchMaxBatch take the length that gives about kTargetSplitWorkgroups
 // work-groups (the search picked 4864-key splits for the ragged int8 batch:
 // 116 vs 105 us).
@@ -503,7 +503,9 @@ int decode_ring_impl(const void* q, const void* k, const void* v, const float* k
     }
     HostPlan hp;
     int rc = hp.build(B, H_q, H_kv, walk, num_splits, T_q,
-                      bits == 16 ? gqa::DecodeKind::Ring : gqa::DecodeKind::Quant);
+                      bits == 16  ? gqa::DecodeKind::Ring
+                      : bits == 4 ? gqa::DecodeKind::QuantInt4
+                                  : gqa::DecodeKind::Quant);
     if (rc) {
         free(walk);
         return rc;
@@ -569,7 +571,8 @@ int gqa_attn_decode_quant(const void* q, const void* k, const void* v, const flo
     for (int b = 0; b < B; ++b)
         if (kv_len[b] < T_q) return GQA_ERR_SHAPE;
     HostPlan hp;
-    rc = hp.build(B, H_q, H_kv, kv_len, num_splits, T_q, gqa::DecodeKind::Quant);
+    rc = hp.build(B, H_q, H_kv, kv_len, num_splits, T_q,
+                  kv_bits == 4 ? gqa::DecodeKind::QuantInt4 : gqa::DecodeKind::Quant);
     if (rc) return rc;
     const int rows = T_q * H_q;
     void* base = nullptr;

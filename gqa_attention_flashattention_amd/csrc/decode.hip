@@ -862,7 +862,7 @@ int64_t decode_workgroups_per_split(DecodeKind kind, int T_q, int G, int H_kv, i
     } else {
         const int nh = decode_column_blocks_per_group(T_q, G);
         n_hg = (((int64_t)T_q * G + kCols - 1) / kCols + nh - 1) / nh;
-        pairs = kind != DecodeKind::Quant;
+        pairs = kind == DecodeKind::Bf16 || kind == DecodeKind::Ring;
     }
     const int hp = (pairs && H_kv % 2 == 0 && split_len >= kPairMinSplitLen) ? 2 : 1;
     return n_hg * (H_kv / hp);

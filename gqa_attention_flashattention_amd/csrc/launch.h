@@ -65,7 +65,7 @@ int decode_column_groups(int T_q, int G);
 // the kernel a decode entry point launches: packed bf16 cache (split or wide
 // kernel), quantised cache, or ring cache.  Two such work-groups are
 // resident per compute unit.
-enum class DecodeKind { Bf16, Quant, Ring };
+enum class DecodeKind { Bf16, Quant, QuantInt4, Ring };
 int64_t decode_workgroups_per_split(DecodeKind kind, int T_q, int G, int H_kv, int split_len);
 constexpr int kDecodeWorkgroupsPerCu = 2;
 

@@ -153,7 +153,8 @@ int gqa_attn_decode(const void *q, const void *k, const void *v, void *o, int B,
  *   num_splits > 0:  L_b = ceil(kv_len[b] / min(num_splits, kv_len[b])), so
  *                    n_b <= num_splits (fewer when the division rounds up);
  *   num_splits <= 0: L_b = L for all b, a multiple of 64 between 128 and
- *                    8192.  For B <= 256 (bf16 and ring caches) L is the
+ *                    8192.  For B <= 256 (bf16 and ring caches, and int4
+ *                    codes in gqa_attn_decode_quant / _ring_quant) L is the
  *                    multiple of 64 (up to 1024), of 128 (up to 2048) or of
  *                    256 (beyond) that minimises
  *                    ceil(W / R) * (L + 256) summed over the launches of 64
