@@ -281,6 +281,15 @@ int check_prefill_args(const void* q, const void* k, const void* v, const void* 
 }
 
 // Key splits per row block for the KV-parallel prefill (see gqa_attn_prefill_kvsplit).
+// One prefill work-group is resident per compute unit (128 KiB of LDS), so
+// W = blocks * n work-groups run in ceil(W / CUs) rounds, each about
+// tiles / n tiles plus a fixed cost per work-group (Q load, epilogue) of
+// kPrefillFixedTiles tiles; the automatic n minimises that product (ties to
+// the smaller n: fewer partials).  On the 256-token chunk over 64k keys (64
+// row blocks) that is n = 4, one round: 482 us, against 500 us for n = 8 (two
+// rounds, the previous "two work-groups per compute unit" rule) and 650 us
+// for n = 5.
+constexpr int kPrefillFixedTiles = 4;
 int prefill_splits(int B, int T_q, int S_kv, int H_q, int H_kv, int d, int causal, int q_offset,
                    int num_splits) {
     const int64_t blocks = gqa::prefill_row_blocks(T_q, H_q / H_kv) * B * H_kv;
@@ -291,10 +300,18 @@ int prefill_splits(int B, int T_q, int S_kv, int H_q, int H_kv, int d, int causa
     if (num_splits > 0) {
         ns = num_splits;
     } else {
-        const int64_t target = 2 * (int64_t)device_cus();
-        ns = blocks >= target ? 1 : (target + blocks - 1) / blocks;
-        const int64_t by_len = tiles / kMinPrefillSplitTiles;
-        if (ns > by_len) ns = by_len;
+        const int64_t cus = device_cus();
+        int64_t hi = tiles / kMinPrefillSplitTiles;
+        if (hi > kMaxPrefillSplits) hi = kMaxPrefillSplits;
+        ns = 1;
+        int64_t best = INT64_MAX;
+        for (int64_t n = 1; n <= (hi < 1 ? 1 : hi); ++n) {
+            const int64_t cost = (blocks * n + cus - 1) / cus * ((tiles + n - 1) / n + kPrefillFixedTiles);
+            if (cost < best) {
+                best = cost;
+                ns = n;
+            }
+        }
     }
     if (ns > tiles) ns = tiles;
     if (ns > kMaxPrefillSplits) ns = kMaxPrefillSplits;

@@ -91,9 +91,10 @@ int gqa_attn_prefill(const void *q, const void *k, const void *v, void *o, float
  * section 4 (the decode combine kernel) produces O and LSE.  This raises the
  * number of work-groups when B * H_kv * row blocks is small (short chunks over
  * long caches).  num_splits > 0 asks for that many ranges, num_splits <= 0 lets
- * the library choose (about two work-groups per compute unit, at least 256
- * keys per range); n is then clamped to [1, 64], to the number of 64-key tiles
- * and so that the partials fit in 4 GiB.  n == 1 runs gqa_attn_prefill's kernel.
+ * the library choose: with one work-group resident per compute unit, the n in
+ * [1, min(64, T / 4)] (T = 64-key tiles of the longest row block) minimising
+ * ceil(blocks * n / CUs) * (ceil(T / n) + 4), ties to the smaller n.  n is
+ * then clamped to [1, 64], to T and so that the partials fit in 4 GiB.  n == 1 runs gqa_attn_prefill's kernel.
  * Uses the library-owned workspace of gqa_attn_decode (same concurrency rule),
  * n * B * T_q * H_q * (d + 2) * 4 bytes.
  * Errors: as gqa_attn_prefill; GQA_ERR_UNSUPPORTED for dtype != GQA_BF16.

@@ -283,3 +283,29 @@ def test_auto_plan_on_the_benchmark_batches():
     assert (p["split_len"], p["total_splits"]) == (128, 64)
     p = gq.decode_plan(1, 64, 8, 128, [131072])
     assert (p["split_len"], p["total_splits"]) == (1024, 128)
+
+
+def _documented_kvsplit_count(B, T_q, S_kv, H_q, H_kv, causal, q_offset, cus=256):
+    """gqa_attn_prefill_kvsplit's automatic range count as its header states it
+    (d = 128: 256 query rows per row block, partials far below 4 GiB here)."""
+    G = H_q // H_kv
+    blocks = -(-(T_q * G) // 256) * B * H_kv
+    keys = q_offset + T_q if causal else S_kv
+    T = -(-keys // 64)
+    hi = max(1, min(64, T // 4))
+    best, best_n = None, 1
+    for n in range(1, hi + 1):
+        cost = -(-(blocks * n) // cus) * (-(-T // n) + 4)
+        if best is None or cost < best:
+            best, best_n = cost, n
+    return min(best_n, 64, T)
+
+
+@pytest.mark.parametrize("B,T_q,S_kv,causal,q_offset", [
+    (1, 256, 65792, True, 65536), (1, 2048, 67584, True, 65536), (1, 8192, 8192, True, 0),
+    (1, 64, 8192, True, 8128), (2, 32, 4096, False, 0), (1, 1, 100000, True, 99999),
+    (4, 512, 20000, True, 19488), (1, 128, 300, False, 0),
+])
+def test_kvsplit_count_follows_the_documented_rule(B, T_q, S_kv, causal, q_offset):
+    n = gq.prefill_kvsplit_count(B, T_q, S_kv, 64, 8, 128, causal=causal, q_offset=q_offset)
+    assert n == _documented_kvsplit_count(B, T_q, S_kv, 64, 8, causal, q_offset)
