@@ -605,7 +605,7 @@ def main():
                     help="first run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+        print(json.dumps({"error": "this library runs on one GPU only; --gpus must be 1 "
                                    "(multi-GPU sharding is a design note, not built)"}))
         sys.exit(2)
 
