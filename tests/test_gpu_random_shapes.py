@@ -76,3 +76,91 @@ def test_random_decode(i):
         off += n
     assert_close(to_f64(o), oref, to_f64(lse), lref,
                  name=f"random decode B={B} T_q={T_q} {Hq}/{Hkv} d={d} splits={num_splits}")
+
+
+def _quant_oracle(inp, ring=None):
+    """Per sequence against the dequantised cache; ring = (capacity, window,
+    sink) unwraps a ring cache into the logical sequence (zeros where evicted)."""
+    k = oracle.dequantize(inp.k_codes, inp.k_scale)
+    v = oracle.dequantize(inp.v_codes, inp.v_scale)
+    B, T_q, Hq, d = inp.q.shape
+    oref = np.empty((B, T_q, Hq, d))
+    lref = np.empty((B, T_q, Hq))
+    off = 0
+    for b, n in enumerate(np.asarray(inp.kv_len).tolist()):
+        if ring is None:
+            ob, lb = oracle.prefill(inp.q[b:b + 1], k[None, off:off + n], v[None, off:off + n],
+                                    causal=True, q_offset=n - T_q)
+            off += n
+        else:
+            cap, window, sink = ring
+            wrap = cap - sink
+            pos = np.arange(n)
+            keep = (pos < sink) | (pos >= n - wrap)
+            slot = np.where(pos < sink, pos, sink + (pos - sink) % wrap)
+            kl = np.zeros((n,) + k.shape[2:], np.float32)
+            vl = np.zeros((n,) + v.shape[2:], np.float32)
+            kl[keep] = k[b, slot[keep]]
+            vl[keep] = v[b, slot[keep]]
+            ob, lb = oracle.prefill_window(inp.q[b:b + 1], kl[None], vl[None], q_offset=n - T_q,
+                                           window=window, sink=sink)
+        oref[b], lref[b] = ob[0], lb[0]
+    return oref, lref
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_quant_decode(i):
+    """INT8 / INT4 caches with the automatic split plan over assorted batches
+    (the int4 plan searches split lengths against rounds of work-groups)."""
+    import gqa_attention_flashattention_amd as gq
+    import torch
+    rng = np.random.default_rng(5000 + i)
+    Hq, Hkv = HEADS[rng.integers(len(HEADS))]
+    d = int(rng.choice([64, 128]))
+    bits = int(rng.choice([8, 4]))
+    B = int(rng.integers(1, 24))
+    T_q = int(rng.choice([1, 1, 2, 4]))
+    kv_len = rng.integers(T_q, 12000, size=B).tolist()
+    inp = gin.quant_case(B=B, H_q=Hq, H_kv=Hkv, d=d, kv_len=kv_len, kv_bits=bits, T_q=T_q,
+                         seed=6000 + i)
+    pack = (lambda c: c) if bits == 8 else gin.pack_int4
+    o, lse = gq.decode_quant(to_gpu(inp.q_store, "bf16"),
+                             torch.from_numpy(pack(inp.k_codes)).cuda(),
+                             torch.from_numpy(pack(inp.v_codes)).cuda(),
+                             torch.from_numpy(inp.k_scale).cuda(),
+                             torch.from_numpy(inp.v_scale).cuda(), kv_len, kv_bits=bits)
+    torch.cuda.synchronize()
+    oref, lref = _quant_oracle(inp)
+    assert_close(to_f64(o), oref, to_f64(lse), lref,
+                 name=f"random int{bits} decode B={B} T_q={T_q} {Hq}/{Hkv} d={d}")
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_ring_quant_decode(i):
+    """Quantised ring caches: random capacities, windows, sinks and token counts
+    (wrapped and unwrapped), automatic split plan."""
+    import gqa_attention_flashattention_amd as gq
+    import torch
+    rng = np.random.default_rng(7000 + i)
+    Hq, Hkv = HEADS[rng.integers(len(HEADS))]
+    d = int(rng.choice([64, 128]))
+    bits = int(rng.choice([8, 4]))
+    B = int(rng.integers(1, 20))
+    T_q = int(rng.choice([1, 1, 2, 3]))
+    sink = int(rng.integers(0, 8))
+    cap = int(rng.integers(sink + T_q + 8, 3000))
+    window = int(rng.integers(1, cap - sink - T_q + 2))
+    kv_len = rng.integers(T_q, 3 * cap, size=B).tolist()
+    inp = gin.quant_case(B=B, H_q=Hq, H_kv=Hkv, d=d, kv_len=kv_len, kv_bits=bits, T_q=T_q,
+                         seed=8000 + i, capacity=cap)
+    pack = (lambda c: c) if bits == 8 else gin.pack_int4
+    o, lse = gq.decode_ring_quant(to_gpu(inp.q_store, "bf16"),
+                                  torch.from_numpy(pack(inp.k_codes)).cuda(),
+                                  torch.from_numpy(pack(inp.v_codes)).cuda(),
+                                  torch.from_numpy(inp.k_scale).cuda(),
+                                  torch.from_numpy(inp.v_scale).cuda(), kv_len, kv_bits=bits,
+                                  window=window, sink=sink)
+    torch.cuda.synchronize()
+    oref, lref = _quant_oracle(inp, ring=(cap, window, sink))
+    assert_close(to_f64(o), oref, to_f64(lse), lref,
+                 name=f"random ring int{bits} B={B} T_q={T_q} cap={cap} w={window} s={sink}")
