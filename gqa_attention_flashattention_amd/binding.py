@@ -62,6 +62,9 @@ def load_library():
                                              vp]
     lib.gqa_attn_prefill_window.restype = i
     lib.gqa_attn_prefill_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, i, vp]
+    lib.gqa_attn_prefill_window_kvsplit.restype = i
+    lib.gqa_attn_prefill_window_kvsplit.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i,
+                                                    i, i, i, vp]
     lib.gqa_attn_prefill_kvsplit_count.restype = i
     lib.gqa_attn_prefill_kvsplit_count.argtypes = [i] * 9
     lib.gqa_attn_decode_quant.restype = i
@@ -213,10 +216,12 @@ def prefill_kvsplit(q, k, v, *, causal: bool, q_offset: int = 0, scale: float | 
 
 
 def prefill_window(q, k, v, *, window: int, sink: int = 0, q_offset: int = 0,
-                   scale: float | None = None, out=None, lse=None, return_lse: bool = True):
+                   scale: float | None = None, out=None, lse=None, return_lse: bool = True,
+                   kv_split: bool = False, num_splits: int = 0):
     """Causal prefill with `sink` attention-sink keys and a local window of
     `window` keys (bf16): the query at position p sees key j iff j <= p and
-    (j < sink or j > p - window)."""
+    (j < sink or j > p - window).  kv_split=True runs the KV-parallel form
+    (gqa_attn_prefill_window_kvsplit; num_splits <= 0: automatic)."""
     import torch
     _require(q, "q", 4)
     _require(k, "k", 4)
@@ -230,6 +235,13 @@ def prefill_window(q, k, v, *, window: int, sink: int = 0, q_offset: int = 0,
         scale = 1.0 / math.sqrt(d)
     out = _out_like(out, q, (B, T_q, H_q, d))
     lse = _lse_buf(lse, q, (B, T_q, H_q), return_lse)
+    if kv_split:
+        rc = load_library().gqa_attn_prefill_window_kvsplit(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, T_q, S_kv, H_q, H_kv, d,
+            float(scale), int(q_offset), int(window), int(sink), int(num_splits),
+            _dtype_code(q), _stream(q.device))
+        _check(rc, "gqa_attn_prefill_window_kvsplit")
+        return out, lse
     rc = load_library().gqa_attn_prefill_window(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, T_q, S_kv, H_q, H_kv, d,
         float(scale), int(q_offset), int(window), int(sink), _dtype_code(q), _stream(q.device))

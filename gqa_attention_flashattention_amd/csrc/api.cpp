@@ -291,11 +291,16 @@ int check_prefill_args(const void* q, const void* k, const void* v, const void* 
 // for n = 5.
 constexpr int kPrefillFixedTiles = 4;
 int prefill_splits(int B, int T_q, int S_kv, int H_q, int H_kv, int d, int causal, int q_offset,
-                   int num_splits) {
+                   int num_splits, int window = 0, int sink = 0) {
     const int64_t blocks = gqa::prefill_row_blocks(T_q, H_q / H_kv) * B * H_kv;
     // the longest row block sees keys up to its last query
     const int64_t keys = causal ? (int64_t)q_offset + T_q : S_kv;
-    const int64_t tiles = (keys + 63) / 64;
+    int64_t tiles = (keys + 63) / 64;
+    if (window > 0) {   // a row block loads its sink tiles and the tiles of its window
+        const int64_t tokens = (256 + H_q / H_kv - 1) / (H_q / H_kv);   // per row block
+        const int64_t win = (sink + 63) / 64 + (window + tokens + 63) / 64 + 1;
+        if (win < tiles) tiles = win;
+    }
     int64_t ns;
     if (num_splits > 0) {
         ns = num_splits;
@@ -433,6 +438,45 @@ int gqa_attn_decode(const void* q, const void* k, const void* v, void* o, int B,
     });
 }
 
+}  // extern "C"
+
+namespace {
+
+// KV-parallel prefill for an already checked argument set (a.window > 0: sink
+// + local-window mask).
+int prefill_kvsplit_impl(const gqa::PrefillArgs& a, int num_splits, void* stream) {
+    const int ns = prefill_splits(a.B, a.T_q, a.S_kv, a.H_q, a.H_kv, a.d, a.causal, a.q_offset,
+                                  num_splits, a.window, a.sink);
+    (void)hipGetLastError();
+    if (ns == 1)
+        return gqa::launch_prefill_bf16(a, (hipStream_t)stream) == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+    const int64_t total = (int64_t)a.B * ns;             // partials per (t, h)
+    const int rows = a.T_q * a.H_q;
+    void* base = nullptr;
+    int rc = get_workspace(workspace_bytes_for(total, rows, a.d), &base);
+    if (rc) return rc;
+    DecodeWorkspace ws = carve(base, total, rows);
+    if (gqa::launch_prefill_split_bf16(a, ns, ws, (hipStream_t)stream) != hipSuccess)
+        return GQA_ERR_HIP;
+    for (int b0 = 0; b0 < a.B; b0 += gqa::kDecodeSeqPerLaunch) {
+        DecodePlanChunk c;
+        memset(&c, 0, sizeof(c));
+        c.nseq = a.B - b0 < gqa::kDecodeSeqPerLaunch ? a.B - b0 : gqa::kDecodeSeqPerLaunch;
+        c.seq0 = b0;
+        c.split_base = b0 * ns;
+        for (int i = 0; i <= c.nseq; ++i) c.unit_base[i] = i * ns;
+        c.units = c.nseq * ns;
+        if (gqa::launch_decode_combine_bf16(ws, c, a.o, a.lse, a.T_q, a.H_q, a.d,
+                                            (hipStream_t)stream) != hipSuccess)
+            return GQA_ERR_HIP;
+    }
+    return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int gqa_attn_prefill_kvsplit(const void* q, const void* k, const void* v, void* o, float* lse,
                              int B, int T_q, int S_kv, int H_q, int H_kv, int d, float scale,
                              int causal, int q_offset, int num_splits, int dtype, void* stream) {
@@ -442,31 +486,21 @@ int gqa_attn_prefill_kvsplit(const void* q, const void* k, const void* v, void* 
     if (!causal) q_offset = 0;
     gqa::PrefillArgs a{q, k, v, o, lse, B, T_q, S_kv, H_q, H_kv, d, scale, causal ? 1 : 0,
                        q_offset};
-    const int ns = prefill_splits(B, T_q, S_kv, H_q, H_kv, d, causal, q_offset, num_splits);
-    (void)hipGetLastError();
-    if (ns == 1)
-        return gqa::launch_prefill_bf16(a, (hipStream_t)stream) == hipSuccess ? GQA_OK : GQA_ERR_HIP;
-    const int64_t total = (int64_t)B * ns;               // partials per (t, h)
-    const int rows = T_q * H_q;
-    void* base = nullptr;
-    rc = get_workspace(workspace_bytes_for(total, rows, d), &base);
+    return prefill_kvsplit_impl(a, num_splits, stream);
+}
+
+int gqa_attn_prefill_window_kvsplit(const void* q, const void* k, const void* v, void* o,
+                                    float* lse, int B, int T_q, int S_kv, int H_q, int H_kv,
+                                    int d, float scale, int q_offset, int window, int sink,
+                                    int num_splits, int dtype, void* stream) {
+    int rc = check_prefill_args(q, k, v, o, B, T_q, S_kv, H_q, H_kv, d, scale, 1, q_offset);
     if (rc) return rc;
-    DecodeWorkspace ws = carve(base, total, rows);
-    if (gqa::launch_prefill_split_bf16(a, ns, ws, (hipStream_t)stream) != hipSuccess)
-        return GQA_ERR_HIP;
-    for (int b0 = 0; b0 < B; b0 += gqa::kDecodeSeqPerLaunch) {
-        DecodePlanChunk c;
-        memset(&c, 0, sizeof(c));
-        c.nseq = B - b0 < gqa::kDecodeSeqPerLaunch ? B - b0 : gqa::kDecodeSeqPerLaunch;
-        c.seq0 = b0;
-        c.split_base = b0 * ns;
-        for (int i = 0; i <= c.nseq; ++i) c.unit_base[i] = i * ns;
-        c.units = c.nseq * ns;
-        if (gqa::launch_decode_combine_bf16(ws, c, o, lse, T_q, H_q, d, (hipStream_t)stream) !=
-            hipSuccess)
-            return GQA_ERR_HIP;
-    }
-    return GQA_OK;
+    if (dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+    if (window < 1 || sink < 0) return GQA_ERR_RANGE;
+    gqa::PrefillArgs a{q, k, v, o, lse, B, T_q, S_kv, H_q, H_kv, d, scale, 1, q_offset};
+    a.window = window;
+    a.sink = sink < S_kv ? sink : S_kv;
+    return prefill_kvsplit_impl(a, num_splits, stream);
 }
 
 int gqa_attn_prefill_window(const void* q, const void* k, const void* v, void* o, float* lse,

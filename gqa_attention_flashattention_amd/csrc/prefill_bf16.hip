@@ -597,13 +597,9 @@ int64_t prefill_row_blocks(int T_q, int G) { return ((int64_t)T_q * G + kBlockM 
 template <bool SPLIT>
 static hipError_t dispatch(const PrefillArgs& a, int n_split, const DecodeWorkspace* ws,
                            hipStream_t stream) {
-    if constexpr (!SPLIT) {   // the window mask is built without the key split
-        if (a.window > 0)
-            return a.d == 128 ? launch_one<128, kMaskWindow, false>(a, 1, nullptr, stream)
-                              : launch_one<64, kMaskWindow, false>(a, 1, nullptr, stream);
-    } else {
-        if (a.window > 0) return hipErrorInvalidValue;
-    }
+    if (a.window > 0)
+        return a.d == 128 ? launch_one<128, kMaskWindow, SPLIT>(a, n_split, ws, stream)
+                          : launch_one<64, kMaskWindow, SPLIT>(a, n_split, ws, stream);
     if (a.d == 128)
         return a.causal ? launch_one<128, kMaskCausal, SPLIT>(a, n_split, ws, stream)
                         : launch_one<128, kMaskNone, SPLIT>(a, n_split, ws, stream);

@@ -121,6 +121,21 @@ int gqa_attn_prefill_window(const void *q, const void *k, const void *v, void *o
                             int q_offset, int window, int sink, int dtype, void *stream);
 
 /*
+ * KV-parallel form of gqa_attn_prefill_window (the two prefill variants
+ * above combined): the sink + window tiles each row block sees are cut into
+ * n contiguous ranges on separate work-groups and merged by the log-sum-exp
+ * combine, as gqa_attn_prefill_kvsplit; for short chunks under long windows.
+ * num_splits > 0 asks for that many ranges; num_splits <= 0 lets the library
+ * choose by gqa_attn_prefill_kvsplit's rule with T = the sink tiles plus the
+ * window tiles of a row block.  Arguments, layouts, requirements and errors
+ * as gqa_attn_prefill_window; workspace as gqa_attn_prefill_kvsplit.
+ */
+int gqa_attn_prefill_window_kvsplit(const void *q, const void *k, const void *v, void *o,
+                                    float *lse, int B, int T_q, int S_kv, int H_q, int H_kv,
+                                    int d, float scale, int q_offset, int window, int sink,
+                                    int num_splits, int dtype, void *stream);
+
+/*
  * Host only: the number of key ranges n that gqa_attn_prefill_kvsplit uses for
  * these arguments (>= 1), or minus a gqa_status code for invalid sizes.
  */

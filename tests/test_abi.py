@@ -26,7 +26,8 @@ def test_header_declares_the_boundary():
               "gqa_attn_decode_combine", "gqa_attn_decode_plan", "gqa_attn_decode_multi",
               "gqa_attn_prefill_kvsplit", "gqa_attn_prefill_kvsplit_count",
               "gqa_attn_prefill_window", "gqa_attn_decode_ring", "gqa_attn_decode_quant",
-              "gqa_attn_decode_ring_quant", "gqa_attn_status_string", "gqa_attn_version"]:
+              "gqa_attn_decode_ring_quant", "gqa_attn_prefill_window_kvsplit",
+              "gqa_attn_status_string", "gqa_attn_version"]:
         assert n in names
 
 
@@ -134,6 +135,13 @@ def test_window_prefill_rejects():
     assert lib.gqa_attn_prefill_window(*args(qoff=5)) == 4
     assert lib.gqa_attn_prefill_window(*args(window=0)) == 4
     assert lib.gqa_attn_prefill_window(*args(sink=-1)) == 4
+    sargs = lambda **kw: args(**kw)[:15] + [kw.get("ns", 0)] + args(**kw)[15:]
+    assert lib.gqa_attn_prefill_window_kvsplit(*sargs(q=None)) == 1
+    assert lib.gqa_attn_prefill_window_kvsplit(*sargs(d=96)) == 3
+    assert lib.gqa_attn_prefill_window_kvsplit(*sargs(dtype=1)) == 3
+    assert lib.gqa_attn_prefill_window_kvsplit(*sargs(qoff=5)) == 4
+    assert lib.gqa_attn_prefill_window_kvsplit(*sargs(window=0)) == 4
+    assert lib.gqa_attn_prefill_window_kvsplit(*sargs(sink=-1)) == 4
 
 
 def test_ring_decode_rejects():

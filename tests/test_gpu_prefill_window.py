@@ -78,3 +78,43 @@ def test_full_size_window_sampled():
                                        sink=w.sink, rows=rows)
     assert_close(og.reshape(-1, w.d)[rows], oref, lg.reshape(-1)[rows], lref,
                  name="prefill_8k_window1k")
+
+
+# ---- KV-parallel form (gqa_attn_prefill_window_kvsplit) ----
+
+def _run_split(inp, q_offset, window, sink, num_splits):
+    import gqa_attention_flashattention_amd as gq
+    import torch
+    q, k, v = (to_gpu(x, "bf16") for x in (inp.q_store, inp.k_store, inp.v_store))
+    o, lse = gq.prefill_window(q, k, v, q_offset=q_offset, window=window, sink=sink,
+                               kv_split=True, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return to_f64(o), to_f64(lse)
+
+
+@pytest.mark.parametrize("B,T,S,Hq,Hkv,d,q_offset,window,sink,num_splits", [
+    (1, 100, 1457, 16, 2, 128, 1357, 200, 3, 0),       # automatic range count
+    (1, 100, 1457, 16, 2, 128, 1357, 200, 3, 3),       # sink tile + window tiles in 3 ranges
+    (1, 64, 5000, 64, 8, 128, 4936, 3000, 4, 0),       # short chunk under a long window
+    (2, 77, 903, 12, 4, 64, 826, 129, 1, 5),           # G = 3, d = 64
+    (1, 300, 300, 16, 2, 128, 0, 64, 4, 2),            # ranges with rows that see none of them
+    (1, 200, 260, 8, 1, 64, 60, 5000, 0, 4),           # window wider than the sequence
+    (1, 129, 129, 8, 2, 128, 0, 1, 200, 3),            # every key a sink
+])
+def test_window_kvsplit_parity(B, T, S, Hq, Hkv, d, q_offset, window, sink, num_splits):
+    inp = gin.random_case("prefill", "bf16", B=B, H_q=Hq, H_kv=Hkv, d=d, T_q=T, S_kv=S,
+                          seed=T + S + window + sink + 7)
+    og, lg = _run_split(inp, q_offset, window, sink, num_splits)
+    oref, lref = oracle.prefill_window(inp.q, inp.k, inp.v, q_offset=q_offset, window=window,
+                                       sink=sink)
+    assert_close(og, oref, lg, lref,
+                 name=f"window kvsplit {B},{T},{S},{Hq},{Hkv},{d} w={window} s={sink} n={num_splits}")
+
+
+def test_window_kvsplit_one_range_equals_window_prefill():
+    """One range is the plain window kernel: bitwise equal outputs."""
+    inp = gin.random_case("prefill", "bf16", B=1, H_q=64, H_kv=8, d=128, T_q=256, S_kv=3000,
+                          seed=43)
+    o1, l1 = _run(inp, 2744, 1000, 4)
+    o2, l2 = _run_split(inp, 2744, 1000, 4, 1)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
