@@ -317,3 +317,19 @@ def _documented_kvsplit_count(B, T_q, S_kv, H_q, H_kv, causal, q_offset, cus=256
 def test_kvsplit_count_follows_the_documented_rule(B, T_q, S_kv, causal, q_offset):
     n = gq.prefill_kvsplit_count(B, T_q, S_kv, 64, 8, 128, causal=causal, q_offset=q_offset)
     assert n == _documented_kvsplit_count(B, T_q, S_kv, 64, 8, causal, q_offset)
+
+
+@pytest.mark.parametrize("argv,env", [(["--gpus", "2"], {}), (["--gpus", "8"], {}),
+                                      ([], {"WORLD_SIZE": "2"})])
+def test_bench_refuses_more_than_one_gpu(argv, env):
+    """bench.py runs on one GPU only: --gpus N > 1 (or a multi-rank launch)
+    exits with status 2 and a JSON message, before touching any device."""
+    import json
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py")] + argv,
+                       env={**os.environ, **env}, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU only" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
