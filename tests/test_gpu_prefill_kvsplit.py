@@ -98,3 +98,24 @@ def test_full_size_chunk_over_long_cache():
     oref, lref = oracle.prefill(inp.q, inp.k, inp.v, causal=True, q_offset=w.q_offset, rows=rows)
     assert_close(og.reshape(-1, w.d)[rows], oref, lg.reshape(-1)[rows], lref,
                  name="prefill_chunk_256_64k kvsplit")
+
+
+@pytest.mark.parametrize("window", [0, 90])
+def test_kvsplit_many_batch_entries(window):
+    """70 batch entries: the combine runs in two launches of at most 64
+    sequences; plain causal and sink + window, every element against the oracle."""
+    import gqa_attention_flashattention_amd as gq
+    import torch
+    inp = gin.random_case("prefill", "bf16", B=70, H_q=16, H_kv=2, d=64, T_q=9, S_kv=400,
+                          seed=77 + window)
+    q, k, v = (to_gpu(x, "bf16") for x in (inp.q_store, inp.k_store, inp.v_store))
+    if window:
+        o, lse = gq.prefill_window(q, k, v, q_offset=391, window=window, sink=3, kv_split=True,
+                                   num_splits=4)
+        oref, lref = oracle.prefill_window(inp.q, inp.k, inp.v, q_offset=391, window=window,
+                                           sink=3)
+    else:
+        o, lse = gq.prefill_kvsplit(q, k, v, causal=True, q_offset=391, num_splits=4)
+        oref, lref = oracle.prefill(inp.q, inp.k, inp.v, causal=True, q_offset=391)
+    torch.cuda.synchronize()
+    assert_close(to_f64(o), oref, to_f64(lse), lref, name=f"kvsplit B=70 window={window}")
