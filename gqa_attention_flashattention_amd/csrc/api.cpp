@@ -72,9 +72,14 @@ int device_cus();
 // us, the 8192-slot ring 39.4 vs 47.7 us.  int8 codes and batches above
 // kSearchMaxBatch take the length that gives about kTargetSplitWorkgroups
 // work-groups (the search picked 4864-key splits for the ragged int8 batch:
-// 116 vs 105 us).
+// 116 vs 105 us).  The combine then reads every split of a sequence, so each
+// split of the longest sequence adds kCombineKeysPerSplit keys: decode_8k
+// takes 32 splits of 256 keys (one work-group per compute unit), 12.95 us per
+// call, rather than 64 of 128 (two per compute unit), 13.33 us -- the split
+// kernel runs 9.9-10.0 us either way, the combine has half the partials.
 constexpr int kSearchMaxBatch = 256;
 constexpr int kSplitFixedKeys = 256;
+constexpr int kCombineKeysPerSplit = 8;
 int64_t auto_split_len(int B, const int32_t* kv_len, int T_q, int G, int H_kv,
                        gqa::DecodeKind kind, int64_t total_keys, int n_hg) {
     if (B > kSearchMaxBatch || kind == gqa::DecodeKind::Quant) {
@@ -92,13 +97,18 @@ int64_t auto_split_len(int B, const int32_t* kv_len, int T_q, int G, int H_kv,
     int64_t best = kMinSplitLen, best_cost = INT64_MAX;
     for (int64_t L = kMinSplitLen; L <= hi; L += L < 1024 ? 64 : L < 2048 ? 128 : 256) {
         const int64_t per_split = gqa::decode_workgroups_per_split(kind, T_q, G, H_kv, (int)L);
-        int64_t cost = 0;
+        int64_t cost = 0, max_n = 0;
         for (int b0 = 0; b0 < B; b0 += gqa::kDecodeSeqPerLaunch) {
             const int b1 = B - b0 < gqa::kDecodeSeqPerLaunch ? B : b0 + gqa::kDecodeSeqPerLaunch;
             int64_t n = 0;
-            for (int b = b0; b < b1; ++b) n += (kv_len[b] + L - 1) / L;
+            for (int b = b0; b < b1; ++b) {
+                const int64_t nb = (kv_len[b] + L - 1) / L;
+                n += nb;
+                max_n = nb > max_n ? nb : max_n;
+            }
             cost += (n * per_split + slots - 1) / slots * (L + kSplitFixedKeys);
         }
+        cost += kCombineKeysPerSplit * max_n;
         if (cost <= best_cost) {
             best_cost = cost;
             best = L;

@@ -174,9 +174,10 @@ int gqa_attn_decode(const void *q, const void *k, const void *v, void *o, int B,
  *                    multiple of 64 (up to 1024), of 128 (up to 2048) or of
  *                    256 (beyond) that minimises
  *                    ceil(W / R) * (L + 256) summed over the launches of 64
- *                    sequences, W being the split work-groups of a launch and
- *                    R the number resident at once (two per compute unit);
- *                    otherwise W is about four per compute unit.  The plan
+ *                    sequences, plus 8 * max_b n_b, W being the split
+ *                    work-groups of a launch and R the number resident at
+ *                    once (two per compute unit); otherwise W is about four
+ *                    per compute unit.  The plan
  *                    of the device current at the call.
  * Writes (every output pointer may be NULL):
  *   splits[b]        n_b (HOST array [B]),

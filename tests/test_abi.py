@@ -250,7 +250,8 @@ def _documented_auto_len(kv_len, H_kv, cus=256):
     """The automatic split length of gqa_attn_decode_plan as its header states
     it (bf16 cache, one new token, G <= 16): the candidate in [128, 8192]
     (multiples of 64 up to 1024, of 128 up to 2048, of 256 beyond)
-    minimising ceil(W / R) * (L + 256) summed over launches of 64 sequences,
+    minimising ceil(W / R) * (L + 256) summed over launches of 64 sequences
+    plus 8 x the largest split count of a sequence,
     W = split work-groups (H_kv / 2 per split from 512 keys on, else H_kv),
     R = 2 per compute unit; ties to the longer L."""
     slots = 2 * cus
@@ -264,6 +265,7 @@ def _documented_auto_len(kv_len, H_kv, cus=256):
         for b0 in range(0, len(kv_len), 64):
             n = sum(-(-x // L) for x in kv_len[b0:b0 + 64])
             cost += -(-(n * per) // slots) * (L + 256)
+        cost += 8 * max(-(-x // L) for x in kv_len)
         if best_cost is None or cost <= best_cost:
             best, best_cost = L, cost
     return best
@@ -282,13 +284,14 @@ def test_auto_plan_follows_the_documented_rule(seed, B):
 def test_auto_plan_on_the_benchmark_batches():
     """One full round of resident work-groups where that is cheapest: the
     16-sequence ragged batch takes 127 splits of 2304 keys (508 work-groups,
-    two KV heads each), decode_8k 64 splits of 128 keys (512)."""
+    two KV heads each), decode_8k 32 splits of 256 keys (256: half the
+    partials of 64 splits for the same round)."""
     from gqa_attention_flashattention_amd import inputs as gin
     kv_len = gin.kv_lengths(gin.WORKLOADS["decode_varlen_b16"], np.random.default_rng(0))
     p = gq.decode_plan(16, 64, 8, 128, kv_len)
     assert (p["split_len"], p["total_splits"]) == (2304, 127)
     p = gq.decode_plan(1, 64, 8, 128, [8192])
-    assert (p["split_len"], p["total_splits"]) == (128, 64)
+    assert (p["split_len"], p["total_splits"]) == (256, 32)
     p = gq.decode_plan(1, 64, 8, 128, [131072])
     assert (p["split_len"], p["total_splits"]) == (1024, 128)
 
