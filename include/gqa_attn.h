@@ -177,7 +177,10 @@ int gqa_attn_decode(const void *q, const void *k, const void *v, void *o, int B,
  *                    sequences, plus 8 * max_b n_b, W being the split
  *                    work-groups of a launch and R the number resident at
  *                    once (two per compute unit); otherwise W is about four
- *                    per compute unit.  The plan
+ *                    per compute unit.  A positive integer in the
+ *                    environment variable GQA_ATTN_SPLIT_LEN (read once per
+ *                    process) replaces the automatic L for every decode entry
+ *                    point (a tuning and measurement override).  The plan
  *                    of the device current at the call.
  * Writes (every output pointer may be NULL):
  *   splits[b]        n_b (HOST array [B]),
