@@ -150,7 +150,8 @@ int make_plan(int B, int T_q, int H_q, int H_kv, const int32_t* kv_len, int num_
         if (lens) lens[b] = (int32_t)L;
         p.total += n;
         if (n > p.max_splits) p.max_splits = (int)n;
-        if (L > p.max_len) p.max_len = (int)(L < len ? L : len);
+        const int64_t longest = L < len ? L : len;   // this sequence's longest split
+        if (longest > p.max_len) p.max_len = (int)longest;
     }
     if (p.total > (int64_t)1 << 30) return GQA_ERR_SHAPE;
     *out = p;

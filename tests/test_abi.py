@@ -246,6 +246,17 @@ def test_auto_plan_targets_occupancy():
     assert p["total_splits"] * 8 >= 256
 
 
+def test_plan_split_len_is_the_longest_split():
+    """*split_len is the longest split over the batch, max_b min(L_b, n_b),
+    also when a later sequence is shorter than the first (both shorter than
+    the automatic L = 128 here)."""
+    p = gq.decode_plan(2, 64, 8, 128, [100, 50])
+    assert p["splits"].tolist() == [1, 1]
+    assert p["split_len"] == 100
+    p = gq.decode_plan(3, 64, 8, 128, [50, 100, 70])
+    assert p["split_len"] == 100
+
+
 def _documented_auto_len(kv_len, H_kv, cus=256):
     """The automatic split length of gqa_attn_decode_plan as its header states
     it (bf16 cache, one new token, G <= 16): the candidate in [128, 8192]
