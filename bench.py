@@ -388,6 +388,23 @@ def traffic_record(kernel: str, grid: int):
     return rec["bytes_per_dispatch"]
 
 
+def mfma_record(kernel: str, grid: int):
+    """MFMA utilisation counters of `kernel` launched with `grid` threads
+    (busy and co-issue fractions, VALU instructions per MFMA, counted MFMA
+    flops and their rate against the peak at the clock the kernel ran at),
+    from profiles/mfma.json, or None when absent or measured on a different
+    kernel source."""
+    from gqa_attention_flashattention_amd import profile_summary as ps
+    path = ps.MFMA_JSON
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(f"{kernel}@{grid}")
+    if not rec or rec.get("source_sha256") != ps.source_sha(kernel):
+        return None
+    return {k: (round(v, 4) if isinstance(v, float) and v < 100 else v)
+            for k, v in rec.items() if k != "source_sha256"}
+
+
 # Launch geometry of the two headline kernels (threads per grid), to match
 # rocprofv3 records: the decode split kernel runs 256 threads per (split, KV
 # head) at G * T_q <= 16; the prefill kernel 512 threads per 256-row block.
@@ -734,6 +751,7 @@ def main():
                          "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": traffic_record(PREFILL_KERNEL, prefill_grid(pw)),
+                         "mfma_counters": mfma_record(PREFILL_KERNEL, prefill_grid(pw)),
                          "algorithmic_flops_per_launch": pre["flops"],
                          "avg_launch_us": round(pre["ms"] * 1e3, 3)},
         },

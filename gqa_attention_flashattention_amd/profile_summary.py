@@ -13,6 +13,13 @@
         "kernel@grid threads"), which bench.py reports as `roofline.traffic`
         while the kernel source it was measured on is unchanged (sha256
         recorded per kernel).
+    python -m gqa_attention_flashattention_amd.profile_summary mfma <dir> [<dir> ...] --cmd C ...
+        MFMA utilisation per dispatch from `rocprofv3 --pmc` runs that hold
+        GRBM_GUI_ACTIVE, SQ_VALU_MFMA_BUSY_CYCLES and, where collected,
+        SQ_VALU_MFMA_COEXEC_CYCLES, SQ_INSTS_VALU, SQ_INSTS_MFMA and
+        SQ_INSTS_VALU_MFMA_MOPS_BF16; writes a markdown table on stdout and
+        updates profiles/mfma.json (same keys and source guard as
+        traffic.json), which bench.py reports beside the prefill roofline.
 """
 from __future__ import annotations
 
@@ -30,6 +37,16 @@ import statistics
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+MFMA_JSON = os.path.join(ROOT, "profiles", "mfma.json")
+
+# MI355X: 8 XCDs (GRBM_GUI_ACTIVE is summed over one counter per XCD), 256
+# compute units of 4 SIMDs; one SIMD retires 1024 dense bf16 MFMA flops per
+# cycle (a 32x32x16 MFMA, 32768 flops, every 32 cycles); one unit of
+# SQ_INSTS_VALU_MFMA_MOPS_BF16 is 512 flops.
+XCDS = 8
+SIMDS = 256 * 4
+BF16_FLOPS_PER_SIMD_CYCLE = 1024
+FLOPS_PER_MOP = 512
 
 # kernel short name -> source file whose hash guards its traffic record
 KERNEL_SOURCES = {
@@ -87,6 +104,36 @@ def counters(run_dir: str) -> dict:
     return out
 
 
+def mfma_table(run_dirs: list[str]) -> dict:
+    """{"kernel@grid": {figure: median over dispatches}} for kernels that
+    issued MFMAs; counters of one kernel may come from several runs."""
+    merged = collections.defaultdict(dict)
+    for d in run_dirs:
+        for k, cs in counters(d).items():
+            merged[k].update({c: statistics.median(v) for c, v in cs.items()})
+            merged[k]["dispatches"] = max(merged[k].get("dispatches", 0),
+                                          max(len(v) for v in cs.values()))
+    out = {}
+    for k, c in merged.items():
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        grbm = c.get("GRBM_GUI_ACTIVE", 0.0)
+        if busy <= 0 or grbm <= 0:
+            continue
+        cycles = grbm / XCDS
+        rec = {"dispatches": int(c["dispatches"]), "cycles": cycles,
+               "mfma_busy": busy / (SIMDS * cycles)}
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in c:
+            rec["mfma_valu_coexec"] = c["SQ_VALU_MFMA_COEXEC_CYCLES"] / (SIMDS * cycles)
+        if c.get("SQ_INSTS_MFMA", 0) > 0 and "SQ_INSTS_VALU" in c:
+            rec["valu_insts_per_mfma"] = c["SQ_INSTS_VALU"] / c["SQ_INSTS_MFMA"]
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c:
+            flops = c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * FLOPS_PER_MOP
+            rec["counted_mfma_flops"] = flops
+            rec["mfma_rate_frac"] = flops / (BF16_FLOPS_PER_SIMD_CYCLE * SIMDS * cycles)
+        out[k] = rec
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -101,7 +148,44 @@ def main():
     tr.add_argument("--cmd-write", default="")
     tr.add_argument("--copy-mib", type=float, required=True)
     tr.add_argument("--title", default="HBM traffic per dispatch")
+    mf = sub.add_parser("mfma")
+    mf.add_argument("dirs", nargs="+")
+    mf.add_argument("--cmd", action="append", default=[])
+    mf.add_argument("--title", default="MFMA utilisation per dispatch")
     args = ap.parse_args()
+
+    if args.mode == "mfma":
+        table = mfma_table(args.dirs)
+        print(f"# {args.title}\n")
+        print("Commands:\n")
+        for c in args.cmd:
+            print(f"    {c}")
+        print("\nCycles = GRBM_GUI_ACTIVE / 8 (one counter per XCD, summed); MFMA busy = "
+              "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles); co-exec likewise with "
+              "SQ_VALU_MFMA_COEXEC_CYCLES; MFMA rate = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 flops / "
+              "(1024 flops per SIMD cycle x 1024 SIMDs x cycles), the fraction of the "
+              "bf16 MFMA peak at the clock the kernel ran at.\n")
+        print("| kernel | dispatches | cycles | MFMA busy | MFMA+VALU co-exec | VALU insts / MFMA "
+              "| counted MFMA flops | MFMA rate |")
+        print("|---|---|---|---|---|---|---|---|")
+        record = json.load(open(MFMA_JSON)) if os.path.exists(MFMA_JSON) else {}
+
+        def f(rec, key, fmt):
+            return format(rec[key], fmt) if key in rec else "-"
+
+        for k in sorted(table):
+            r = table[k]
+            shown = k if len(k) <= 90 else k[:87] + "..."
+            print(f"| `{shown}` | {r['dispatches']} | {r['cycles']:.4g} | {f(r, 'mfma_busy', '.1%')} "
+                  f"| {f(r, 'mfma_valu_coexec', '.1%')} | {f(r, 'valu_insts_per_mfma', '.2f')} "
+                  f"| {f(r, 'counted_mfma_flops', '.4g')} | {f(r, 'mfma_rate_frac', '.1%')} |")
+            sha = source_sha(k)
+            if sha:
+                record[k] = dict(r, source_sha256=sha)
+        os.makedirs(os.path.dirname(MFMA_JSON), exist_ok=True)
+        with open(MFMA_JSON, "w") as fh:
+            json.dump(record, fh, indent=1, sort_keys=True)
+        return
 
     if args.mode == "trace":
         print(f"# {args.title}\n")
