@@ -35,6 +35,16 @@
  *    concurrent gqa_attn_decode calls on different streams of one device
  *    must be serialised by the caller (or use gqa_attn_decode_split /
  *    gqa_attn_decode_combine with caller-owned workspaces).
+ *  - HIP graphs: every entry point enqueues only kernel launches (no
+ *    memset, copy or host synchronisation), so a call may be captured.  The
+ *    library-owned workspace (gqa_attn_decode, _multi, _quant, _ring,
+ *    _ring_quant and the KV-parallel prefills) grows on demand: a call that
+ *    needs more than it holds synchronises the device, frees it and
+ *    allocates a larger one, which capture forbids and which leaves a graph
+ *    captured earlier pointing at freed memory.  Make the largest such call
+ *    once before capturing and capture no call that needs more, or capture
+ *    gqa_attn_decode_split / gqa_attn_decode_combine with a caller-owned
+ *    workspace.
  */
 #ifndef GQA_ATTN_H
 #define GQA_ATTN_H
