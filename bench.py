@@ -849,6 +849,18 @@ def main():
                          "algorithmic_bytes_per_call": dq["kv_bytes"],
                          "note": "whole call; bytes = K and V codes read (scales negligible)"},
         })
+    log("[bench] measured ceilings (streaming read, MFMA loop)")
+    from gqa_attention_flashattention_amd import ceilings
+    read_gbs = ceilings.hbm_read_gbps()
+    mfma_tf = ceilings.mfma_bf16_tflops()
+    result["ceilings"] = {
+        "hbm_read_GBps": round(read_gbs, 1), "hbm_read_frac_of_peak": round(read_gbs / HBM_PEAK_GBS, 4),
+        "mfma_bf16_TFLOPs": round(mfma_tf, 1),
+        "mfma_bf16_frac_of_peak": round(mfma_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+        "note": "measured on this GPU: a 4 GiB read with 16-byte non-temporal loads, one "
+                "contiguous range per work-group; back-to-back 32x32x16 bf16 MFMAs on register "
+                "operands that change at every issue; the rooflines divide by the spec-sheet "
+                "peaks"}
     if not args.no_cpu:
         log("[bench] cpu oracle baseline (decode)")
         cb, o_ref, lse_ref = cpu_baseline_decode(dec["inp"], dec["kv_bytes"])

@@ -1,4 +1,6 @@
-"""Build libgqa_attn.so in-tree with hipcc for gfx950.
+"""Build libgqa_attn.so (the attention kernels and their C ABI) and
+libgqa_ceilings.so (the benchmark's measured HBM-read and MFMA ceilings)
+in-tree with hipcc for gfx950.
 
 Every call recompiles all sources (the build check must exercise the
 compiler).  Flags of note:
@@ -22,6 +24,8 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgqa_attn.so")
 
 SOURCES = ["prefill_bf16.hip", "prefill_f32.hip", "decode.hip", "api.cpp"]
+CEIL_LIB = os.path.join(PKG, "libgqa_ceilings.so")
+CEIL_SOURCES = ["ceilings.hip"]
 # The bf16 kernels never create NaNs (masked scores are -inf, never NaN); this
 # lets fmaxf lower to plain v_max_f32 / v_max3_f32 without quieting operands.
 # The prefill kernel also gets the scheduler that groups memory instructions
@@ -55,17 +59,23 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    workers = min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8")))
-    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs: list[str], lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + CEIL_SOURCES
+    workers = min(len(srcs), int(os.environ.get("MAX_JOBS", "8")))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in SOURCES], LIB, verbose)
+    _link([objs[s] for s in CEIL_SOURCES], CEIL_LIB, verbose)
     return LIB
 
 

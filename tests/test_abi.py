@@ -347,3 +347,15 @@ def test_bench_refuses_more_than_one_gpu(argv, env):
                        env={**os.environ, **env}, capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "one GPU only" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
+
+
+def test_ceilings_library_loads_and_rejects_bad_sizes():
+    """The benchmark's ceiling kernels (separate library) export their two
+    entry points and refuse invalid sizes before any launch."""
+    from gqa_attention_flashattention_amd import ceilings
+    lib = ceilings._load()
+    assert lib.gqa_ceiling_read(None, 1024, None, 4, None) == 2
+    assert lib.gqa_ceiling_read(8, 1000, 8, 4, None) == 2      # not a multiple of 16
+    assert lib.gqa_ceiling_read(8, 1024, 8, 0, None) == 2      # no work-groups
+    assert lib.gqa_ceiling_mfma(None, 4, 10, None) == 2
+    assert lib.gqa_ceiling_mfma(8, 4, 0, None) == 2
