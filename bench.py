@@ -92,6 +92,28 @@ def time_graph(fn_list, reps=1):
     return start.elapsed_time(end) / (reps * len(fn_list))
 
 
+def graph_samples(fn_list, n):
+    """Capture fn_list into one graph and time n replays separately; returns
+    the elapsed ms per call of each replay (for median and minimum)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for fn in fn_list:
+            fn()
+    warm(g.replay)
+    out = []
+    for _ in range(n):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        g.replay()
+        end.record()
+        torch.cuda.synchronize()
+        out.append(start.elapsed_time(end) / len(fn_list))
+    return out
+
+
 def decode_algorithmic_bytes(w, kv_len):
     return int(np.sum(kv_len, dtype=np.int64)) * w.H_kv * w.d * 2 * 2
 
@@ -151,10 +173,14 @@ def bench_decode(name, steps, warmup):
     ms_hot = time_graph([lambda: (gq.decode_split(q, k0, v0, inp.kv_len, ws),
                                   gq.decode_combine(ws, inp.kv_len, H_q=Hq, H_kv=w.H_kv, d=d,
                                                     out=out, lse=lse))] * min(steps, 200))
+    # after the K timed steps: 20 more replays of 100 calls each, for the
+    # median and the minimum of the per-call time
+    call_samples = graph_samples([call(i) for i in range(min(steps, 100))], 20)
     o_gpu = out.float().cpu().numpy().astype(np.float64)
     lse_gpu = lse.cpu().numpy().astype(np.float64)
     return dict(inp=inp, kv_bytes=kv_bytes, ms_call=ms_call, ms_split=ms_split, ms_hot=ms_hot,
-                n_copies=n_copies, plan=plan, o_gpu=o_gpu, lse_gpu=lse_gpu)
+                n_copies=n_copies, plan=plan, o_gpu=o_gpu, lse_gpu=lse_gpu,
+                call_samples=call_samples)
 
 
 def bench_decode_multi(name, steps, warmup):
@@ -208,13 +234,24 @@ def bench_prefill(name, steps, warmup):
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
+    # after the timed calls: each of `steps` more calls between its own events
+    # (median and minimum)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record()
+        gq.prefill(q, k, v, causal=w.causal, q_offset=w.q_offset, out=o, lse=lse)
+        e1.record()
+    torch.cuda.synchronize()
+    call_samples = [e0.elapsed_time(e1) for e0, e1 in evs]
     flops = prefill_algorithmic_flops(w)
     rng = np.random.default_rng(0)
     rows = np.unique(np.concatenate([[0, w.B * w.T_q * w.H_q - 1],
                                      rng.integers(0, w.B * w.T_q * w.H_q, 62)]))
     o_rows = o.float().cpu().numpy().reshape(-1, w.d)[rows].astype(np.float64)
     lse_rows = lse.cpu().numpy().reshape(-1)[rows].astype(np.float64)
-    return dict(inp=inp, ms=ms, flops=flops, rows=rows, o_rows=o_rows, lse_rows=lse_rows)
+    return dict(inp=inp, ms=ms, flops=flops, rows=rows, o_rows=o_rows, lse_rows=lse_rows,
+                call_samples=call_samples)
 
 
 def bench_prefill_kvsplit(name, steps):
@@ -733,6 +770,10 @@ def main():
                    "splits_per_seq": int(dec["plan"]["max_splits"]),
                    "kv_copies_rotated": dec["n_copies"], "timed_via": "hip graph replay"},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "call_ms_spread": {"median": round(float(np.median(dec["call_samples"])), 5),
+                           "min": round(float(np.min(dec["call_samples"])), 5),
+                           "samples": len(dec["call_samples"]),
+                           "how": "20 graph replays of 100 calls after the timed steps"},
         "hot_cache_GBps": round(dec["kv_bytes"] / (dec["ms_hot"] * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "kernel": decode_split_kernel_name(dec["plan"], dw),
                      "grid_threads": decode_split_grid(dec["plan"], dw),
@@ -745,6 +786,10 @@ def main():
         "prefill": {
             "workload": pw.name, "T_q": pw.T_q, "S_kv": pw.S_kv, "q_offset": pw.q_offset,
             "causal": pw.causal, "ms_per_call": pre["ms"], "value": round(tflops, 2),
+            "call_ms_spread": {"median": round(float(np.median(pre["call_samples"])), 5),
+                               "min": round(float(np.min(pre["call_samples"])), 5),
+                               "samples": len(pre["call_samples"]),
+                               "how": "each call between its own events, after the timed calls"},
             "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "kernel": PREFILL_KERNEL,
                          "grid_threads": prefill_grid(pw),
