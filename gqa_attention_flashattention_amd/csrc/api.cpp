@@ -235,7 +235,15 @@ struct HostPlan {
     }
 };
 
-// Per-device decode workspace owned by the library (gqa_attn_decode only).
+// Per-device workspace owned by the library (the one-call decode entry
+// points and the KV-parallel prefills).  A call holds the workspace lock from
+// the moment it takes the buffer until its last kernel is queued (the
+// WorkspaceLease lives to the end of the entry point), so a call that needs a
+// larger buffer can only replace it once every call that took the old one has
+// queued its kernels; hipDeviceSynchronize then drains those kernels before
+// the old buffer is freed.  Calls on one stream therefore never see a freed or
+// foreign buffer; calls on different streams of one device still share the
+// buffer's contents and must be serialised by the caller.
 constexpr int kMaxDevices = 64;
 struct CachedWorkspace {
     void* ptr = nullptr;
@@ -244,14 +252,19 @@ struct CachedWorkspace {
 std::mutex g_ws_mutex;
 CachedWorkspace g_ws[kMaxDevices];
 
-int get_workspace(size_t bytes, void** out) {
+struct WorkspaceLease {
+    std::unique_lock<std::mutex> lock;
+    void* ptr = nullptr;
+};
+
+int get_workspace(size_t bytes, WorkspaceLease* lease) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GQA_ERR_HIP;
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    std::unique_lock<std::mutex> lock(g_ws_mutex);
     CachedWorkspace& w = g_ws[dev];
     if (w.bytes < bytes) {
         if (w.ptr) {
-            // the old buffer may still be read by queued kernels
+            // kernels queued by earlier calls may still read the old buffer
             if (hipDeviceSynchronize() != hipSuccess) return GQA_ERR_HIP;
             (void)hipFree(w.ptr);
             w.ptr = nullptr;
@@ -264,7 +277,8 @@ int get_workspace(size_t bytes, void** out) {
         }
         w.bytes = want;
     }
-    *out = w.ptr;
+    lease->ptr = w.ptr;
+    lease->lock = std::move(lock);
     return GQA_OK;
 }
 
@@ -434,10 +448,10 @@ int gqa_attn_decode(const void* q, const void* k, const void* v, void* o, int B,
     rc = hp.build(B, H_q, H_kv, kv_len, num_splits);
     if (rc) return rc;
     const size_t need = workspace_bytes_for(hp.p.total, H_q, d);
-    void* base = nullptr;
-    rc = get_workspace(need, &base);
+    WorkspaceLease lease;
+    rc = get_workspace(need, &lease);
     if (rc) return rc;
-    DecodeWorkspace ws = carve(base, hp.p.total, H_q);
+    DecodeWorkspace ws = carve(lease.ptr, hp.p.total, H_q);
     (void)hipGetLastError();
     rc = for_each_chunk(B, kv_len, hp.splits, hp.lens, [&](const DecodePlanChunk& c) {
         return gqa::launch_decode_split_bf16(q, k, v, ws, c, 1, H_q, H_kv, d, scale,
@@ -463,10 +477,10 @@ int prefill_kvsplit_impl(const gqa::PrefillArgs& a, int num_splits, void* stream
         return gqa::launch_prefill_bf16(a, (hipStream_t)stream) == hipSuccess ? GQA_OK : GQA_ERR_HIP;
     const int64_t total = (int64_t)a.B * ns;             // partials per (t, h)
     const int rows = a.T_q * a.H_q;
-    void* base = nullptr;
-    int rc = get_workspace(workspace_bytes_for(total, rows, a.d), &base);
+    WorkspaceLease lease;
+    int rc = get_workspace(workspace_bytes_for(total, rows, a.d), &lease);
     if (rc) return rc;
-    DecodeWorkspace ws = carve(base, total, rows);
+    DecodeWorkspace ws = carve(lease.ptr, total, rows);
     if (gqa::launch_prefill_split_bf16(a, ns, ws, (hipStream_t)stream) != hipSuccess)
         return GQA_ERR_HIP;
     for (int b0 = 0; b0 < a.B; b0 += gqa::kDecodeSeqPerLaunch) {
@@ -573,13 +587,13 @@ int decode_ring_impl(const void* q, const void* k, const void* v, const float* k
         return rc;
     }
     const int rows = T_q * H_q;
-    void* base = nullptr;
-    rc = get_workspace(workspace_bytes_for(hp.p.total, rows, d), &base);
+    WorkspaceLease lease;
+    rc = get_workspace(workspace_bytes_for(hp.p.total, rows, d), &lease);
     if (rc) {
         free(walk);
         return rc;
     }
-    DecodeWorkspace ws = carve(base, hp.p.total, rows);
+    DecodeWorkspace ws = carve(lease.ptr, hp.p.total, rows);
     const gqa::RingArgs ring{capacity, sink, window};
     (void)hipGetLastError();
     rc = for_each_chunk(B, walk, hp.splits, hp.lens, [&](const DecodePlanChunk& c) {
@@ -637,10 +651,10 @@ int gqa_attn_decode_quant(const void* q, const void* k, const void* v, const flo
                   kv_bits == 4 ? gqa::DecodeKind::QuantInt4 : gqa::DecodeKind::Quant);
     if (rc) return rc;
     const int rows = T_q * H_q;
-    void* base = nullptr;
-    rc = get_workspace(workspace_bytes_for(hp.p.total, rows, d), &base);
+    WorkspaceLease lease;
+    rc = get_workspace(workspace_bytes_for(hp.p.total, rows, d), &lease);
     if (rc) return rc;
-    DecodeWorkspace ws = carve(base, hp.p.total, rows);
+    DecodeWorkspace ws = carve(lease.ptr, hp.p.total, rows);
     (void)hipGetLastError();
     rc = for_each_chunk(B, kv_len, hp.splits, hp.lens, [&](const DecodePlanChunk& c) {
         return gqa::launch_decode_quant_split(q, k, v, k_scale, v_scale, kv_bits, ws, c, T_q, H_q,
@@ -666,10 +680,10 @@ int gqa_attn_decode_multi(const void* q, const void* k, const void* v, void* o, 
     if (rc) return rc;
     const int rows = T_q * H_q;
     const size_t need = workspace_bytes_for(hp.p.total, rows, d);
-    void* base = nullptr;
-    rc = get_workspace(need, &base);
+    WorkspaceLease lease;
+    rc = get_workspace(need, &lease);
     if (rc) return rc;
-    DecodeWorkspace ws = carve(base, hp.p.total, rows);
+    DecodeWorkspace ws = carve(lease.ptr, hp.p.total, rows);
     (void)hipGetLastError();
     rc = for_each_chunk(B, kv_len, hp.splits, hp.lens, [&](const DecodePlanChunk& c) {
         return gqa::launch_decode_split_bf16(q, k, v, ws, c, T_q, H_q, H_kv, d, scale,

@@ -30,11 +30,20 @@
  *  - dtype: GQA_BF16 (storage bf16, fp32 accumulation and softmax state) or
  *    GQA_F32 (fp32 storage and arithmetic throughout, no reduced-precision
  *    matrix instructions).  Head dim d must be 64 or 128.
- *  - Calls are thread-safe with respect to each other except that
- *    gqa_attn_decode's internal workspace is per device and per process:
- *    concurrent gqa_attn_decode calls on different streams of one device
- *    must be serialised by the caller (or use gqa_attn_decode_split /
- *    gqa_attn_decode_combine with caller-owned workspaces).
+ *  - Threads.  Entry points that take only caller-owned buffers
+ *    (gqa_attn_prefill, gqa_attn_prefill_window, gqa_attn_decode_split,
+ *    gqa_attn_decode_combine and the host-only queries) may be called from
+ *    any number of host threads at once.  The others (gqa_attn_decode,
+ *    _multi, _quant, _ring, _ring_quant and the KV-parallel prefills) share
+ *    one library-owned workspace per device and process.  Each such call
+ *    holds a lock on it from the moment it takes the buffer until its last
+ *    kernel is queued, so calls from several host threads on ONE stream of
+ *    a device are safe: a call that has to grow the buffer first waits for
+ *    the kernels already queued against the old one.  Such calls on
+ *    DIFFERENT streams of one device may run their kernels at the same time
+ *    and overwrite each other's partials: serialise them (e.g. with events)
+ *    or use gqa_attn_decode_split / gqa_attn_decode_combine with a
+ *    caller-owned workspace per stream.
  *  - HIP graphs: every entry point enqueues only kernel launches (no
  *    memset, copy or host synchronisation), so a call may be captured.  The
  *    library-owned workspace (gqa_attn_decode, _multi, _quant, _ring,
@@ -283,9 +292,9 @@ int gqa_attn_decode_quant(const void *q, const void *k, const void *v, const flo
 /*
  * Decode over a hard-cap ring-buffer KV cache with attention sinks and a local
  * window (pccx page "Gemma 3N E4B on pccx v002 -- Execution / Scheduling":
- * KV ring buffer of max_tokens set at init, section 4: once the ring wraps,
- * the oldest entries are overwritten under an attention-sink + local-window
- * policy).  T_q >= 1 new tokens per sequence, already written to the cache.
+ * the KV ring buffer sized by max_tokens at init, and section 4, KV cache
+ * management, where a wrapped ring keeps the sink positions and a local
+ * window of the newest ones).  T_q >= 1 new tokens per sequence, already written to the cache.
  *   k, v [B, capacity, H_kv, d] (dtype): the first `sink` positions of
  *        sequence b stay in slots 0 .. sink-1; position j >= sink is in slot
  *        sink + (j - sink) mod (capacity - sink), so the ring keeps the

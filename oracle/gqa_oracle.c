@@ -36,12 +36,11 @@
  *   the end.
  *
  *   Sink + local-window mask (pccx page, "Gemma 3N E4B on pccx v002 --
- *   Execution / Scheduling", section 4, KV cache management, hard-cap ring
- *   buffer: once the ring wraps, the oldest entries are overwritten under an
- *   attention-sink + local-window policy).  Reading used here: a query at
- *   absolute position p sees key j iff j <= p and (j < sink or
- *   j > p - window), i.e. the first `sink` positions of the sequence plus
- *   the `window` most recent positions up to and including its own.
+ *   Execution / Scheduling", section 4, KV cache management of the
+ *   fixed-size ring cache).  Reading used here: key j is visible to the
+ *   query at absolute position p iff j <= p and (j < sink or j > p - window),
+ *   so a query keeps the leading `sink` positions plus the `window` newest
+ *   positions ending at its own.
  *   gqa_oracle_prefill_window computes exactly that over the logical
  *   (unwrapped) key sequence; where a ring buffer stores the keys is the
  *   kernel's business, not the oracle's.
