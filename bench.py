@@ -246,11 +246,16 @@ def bench_prefill(name, steps, warmup):
     call_samples = [e0.elapsed_time(e1) for e0, e1 in evs]
     flops = prefill_algorithmic_flops(w)
     rng = np.random.default_rng(0)
+    # rows: the CPU baseline's timing sample; wg_rows: one row of every
+    # work-group (parity)
     rows = np.unique(np.concatenate([[0, w.B * w.T_q * w.H_q - 1],
                                      rng.integers(0, w.B * w.T_q * w.H_q, 62)]))
-    o_rows = o.float().cpu().numpy().reshape(-1, w.d)[rows].astype(np.float64)
-    lse_rows = lse.cpu().numpy().reshape(-1)[rows].astype(np.float64)
-    return dict(inp=inp, ms=ms, flops=flops, rows=rows, o_rows=o_rows, lse_rows=lse_rows,
+    wg_rows = gin.rows_per_workgroup(w.B, w.T_q, w.H_q, w.H_kv, seed=1)
+    o_all = o.float().cpu().numpy().reshape(-1, w.d)
+    lse_all = lse.cpu().numpy().reshape(-1)
+    return dict(inp=inp, ms=ms, flops=flops, rows=rows, wg_rows=wg_rows,
+                o_rows=o_all[rows].astype(np.float64), lse_rows=lse_all[rows].astype(np.float64),
+                o_wg=o_all[wg_rows].astype(np.float64), lse_wg=lse_all[wg_rows].astype(np.float64),
                 call_samples=call_samples)
 
 
@@ -509,6 +514,20 @@ def cpu_baseline_prefill(inp, rows, min_seconds=10.0):
                        f"{el:.1f} s"), o, lse
 
 
+def parity_prefill_rows(pre, o_sample, lse_sample, tag):
+    """Prefill parity over the timing sample's rows (oracle outputs given)
+    and over one row of every work-group (oracle run here)."""
+    import oracle
+    inp = pre["inp"]
+    w = inp.workload
+    o, l = oracle.prefill(inp.q, inp.k, inp.v, causal=w.causal, q_offset=w.q_offset,
+                          rows=pre["wg_rows"])
+    do = max(np.abs(pre["o_rows"] - o_sample).max(), np.abs(pre["o_wg"] - o).max())
+    dl = max(np.abs(pre["lse_rows"] - lse_sample).max(), np.abs(pre["lse_wg"] - l).max())
+    return {f"{tag}_sample_max_abs_dO": float(do), f"{tag}_sample_max_abs_dLSE": float(dl),
+            f"{tag}_sample_rows": int(np.union1d(pre["rows"], pre["wg_rows"]).size)}
+
+
 def parity_decode_multi(mul, n_seq=2):
     """Oracle check of the first n_seq sequences of the multi-token decode
     result (every row of those sequences)."""
@@ -529,11 +548,13 @@ def parity_decode_multi(mul, n_seq=2):
 
 def parity_prefill_kvsplit(kvs, n_rows=64):
     import oracle
+    from gqa_attention_flashattention_amd import inputs as gin
     inp = kvs["inp"]
     w = inp.workload
     rng = np.random.default_rng(0)
     total = w.B * w.T_q * w.H_q
     rows = np.unique(np.concatenate([[0, total - 1], rng.integers(0, total, n_rows - 2)]))
+    rows = np.union1d(rows, gin.rows_per_workgroup(w.B, w.T_q, w.H_q, w.H_kv, seed=1))
     o, l = oracle.prefill(inp.q, inp.k, inp.v, causal=w.causal, q_offset=w.q_offset, rows=rows)
     og = kvs["o_gpu"].reshape(-1, w.d)[rows].astype(np.float64)
     lg = kvs["lse_gpu"].reshape(-1)[rows].astype(np.float64)
@@ -543,11 +564,13 @@ def parity_prefill_kvsplit(kvs, n_rows=64):
 
 def parity_prefill_window(pw_, n_rows=64):
     import oracle
+    from gqa_attention_flashattention_amd import inputs as gin
     inp = pw_["inp"]
     w = inp.workload
     rng = np.random.default_rng(0)
     total = w.B * w.T_q * w.H_q
     rows = np.unique(np.concatenate([[0, total - 1], rng.integers(0, total, n_rows - 2)]))
+    rows = np.union1d(rows, gin.rows_per_workgroup(w.B, w.T_q, w.H_q, w.H_kv, seed=1))
     o, l = oracle.prefill_window(inp.q, inp.k, inp.v, q_offset=w.q_offset, window=w.window,
                                  sink=w.sink, rows=rows)
     og = pw_["o_gpu"].reshape(-1, w.d)[rows].astype(np.float64)
@@ -635,6 +658,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--decode-workload", default="decode_8k")
     ap.add_argument("--prefill-workload", default="prefill_8k_causal")
+    ap.add_argument("--chunk-workload", default="prefill_chunk_64k",
+                    help="chunked causal prefill at an offset (reported under prefill_chunk)")
     ap.add_argument("--kvsplit-workload", default="prefill_chunk_256_64k",
                     help="KV-parallel prefill workload (reported under prefill_kvsplit)")
     ap.add_argument("--window-workload", default="prefill_8k_window1k",
@@ -650,7 +675,7 @@ def main():
     ap.add_argument("--scale-workloads", default="decode_varlen_b16,decode_128k",
                     help="larger plain-decode workloads (reported under decode_at_scale)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["decode", "prefill", "decode_multi", "prefill_kvsplit",
+    ap.add_argument("--only", choices=["decode", "prefill", "prefill_chunk", "decode_multi", "prefill_kvsplit",
                                        "prefill_window", "decode_ring", "decode_quant",
                                        "decode_ring_quant"],
                     default=None,
@@ -703,9 +728,10 @@ def main():
         log(f"[bench] prefill_kvsplit {kvs['ms'] * 1e3:.1f} us/call (plain "
             f"{kvs['ms_plain'] * 1e3:.1f} us), {kvs['n_split']} ranges")
         return
-    if args.only == "prefill":
-        pre = bench_prefill(args.prefill_workload, args.prefill_steps, 2)
-        log(f"[bench] prefill {pre['ms']:.3f} ms/call "
+    if args.only in ("prefill", "prefill_chunk"):
+        name = args.prefill_workload if args.only == "prefill" else args.chunk_workload
+        pre = bench_prefill(name, args.prefill_steps, 2)
+        log(f"[bench] {args.only} {pre['ms']:.3f} ms/call "
             f"{pre['flops'] / (pre['ms'] * 1e-3) / 1e12:.1f} TFLOP/s")
         return
     log(f"[bench] decode {args.decode_workload}: warmup {args.warmup}, steps {args.steps}")
@@ -718,6 +744,10 @@ def main():
     log(f"[bench] prefill {args.prefill_workload}: steps {args.prefill_steps}")
     pre = bench_prefill(args.prefill_workload, args.prefill_steps, 2)
     log(f"[bench] prefill {pre['ms']:.3f} ms/call")
+
+    log(f"[bench] prefill_chunk {args.chunk_workload}: steps {max(args.prefill_steps // 4, 3)}")
+    chk = bench_prefill(args.chunk_workload, max(args.prefill_steps // 4, 3), 1)
+    log(f"[bench] prefill_chunk {chk['ms']:.3f} ms/call")
 
     log(f"[bench] decode_multi {args.multi_workload}")
     mul = bench_decode_multi(args.multi_workload, min(args.steps, 200), args.warmup)
@@ -800,6 +830,26 @@ def main():
                          "algorithmic_flops_per_launch": pre["flops"],
                          "avg_launch_us": round(pre["ms"] * 1e3, 3)},
         },
+    }
+    cw = chk["inp"].workload
+    tf_chunk = chk["flops"] / (chk["ms"] * 1e-3) / 1e12
+    result["prefill_chunk"] = {
+        "workload": cw.name, "T_q": cw.T_q, "S_kv": cw.S_kv, "q_offset": cw.q_offset,
+        "causal": cw.causal, "ms_per_call": chk["ms"], "value": round(tf_chunk, 2),
+        "call_ms_spread": {"median": round(float(np.median(chk["call_samples"])), 5),
+                           "min": round(float(np.min(chk["call_samples"])), 5),
+                           "samples": len(chk["call_samples"]),
+                           "how": "each call between its own events, after the timed calls"},
+        "unit": "TFLOP/s",
+        "roofline": {"bound": "mfma", "kernel": PREFILL_KERNEL,
+                     "grid_threads": prefill_grid(cw),
+                     "achieved": round(tf_chunk, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf_chunk / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic_record(PREFILL_KERNEL, prefill_grid(cw)),
+                     "mfma_counters": mfma_record(PREFILL_KERNEL, prefill_grid(cw)),
+                     "algorithmic_flops_per_launch": chk["flops"],
+                     "avg_launch_us": round(chk["ms"] * 1e3, 3),
+                     "note": "one prefill kernel launch per call"},
     }
     mw = mul["inp"].workload
     gbs_multi = mul["kv_bytes"] / (mul["ms"] * 1e-3) / 1e9
@@ -915,8 +965,11 @@ def main():
         log("[bench] cpu oracle baseline (prefill sample)")
         cbp, op, lp = cpu_baseline_prefill(pre["inp"], pre["rows"])
         result["prefill"]["cpu_baseline"] = cbp
-        result["parity"]["prefill_sample_max_abs_dO"] = float(np.abs(pre["o_rows"] - op).max())
-        result["parity"]["prefill_sample_max_abs_dLSE"] = float(np.abs(pre["lse_rows"] - lp).max())
+        result["parity"].update(parity_prefill_rows(pre, op, lp, "prefill"))
+        log("[bench] cpu oracle baseline (prefill_chunk sample)")
+        cbc, oc, lc = cpu_baseline_prefill(chk["inp"], chk["rows"])
+        result["prefill_chunk"]["cpu_baseline"] = cbc
+        result["parity"].update(parity_prefill_rows(chk, oc, lc, "prefill_chunk"))
         log("[bench] oracle check (prefill_kvsplit sample)")
         result["parity"].update(parity_prefill_kvsplit(kvs))
         log("[bench] oracle check (prefill_window sample)")

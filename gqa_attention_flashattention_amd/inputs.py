@@ -223,3 +223,26 @@ def pack_int4(codes: np.ndarray) -> np.ndarray:
     the low nibble of byte i (two's complement nibbles)."""
     u = codes.astype(np.uint8) & np.uint8(0x0F)
     return (u[..., 0::2] | (u[..., 1::2] << np.uint8(4))).astype(np.uint8)
+
+
+def rows_per_workgroup(B: int, T_q: int, H_q: int, H_kv: int, seed: int = 0,
+                       block_rows: int = 256) -> np.ndarray:
+    """Flat output-row indices ((b * T_q + t) * H_q + h) for sampled parity
+    checks of a full-size prefill: one random row from every (batch entry, KV
+    head, block of `block_rows` folded rows), where the G query heads of a KV
+    head are folded t-major (folded row t * G + g, query head kv * G + g), so
+    every prefill work-group contributes a row, plus the first and last rows."""
+    G = H_q // H_kv
+    rng = np.random.default_rng(seed)
+    n_fold = T_q * G
+    n_blk = -(-n_fold // block_rows)
+    out = [0, B * T_q * H_q - 1]
+    for b in range(B):
+        for kv in range(H_kv):
+            lo = np.arange(n_blk, dtype=np.int64) * block_rows
+            hi = np.minimum(lo + block_rows, n_fold)
+            i = lo + (rng.random(n_blk) * (hi - lo)).astype(np.int64)
+            t, g = i // G, i % G
+            out.extend(((b * T_q + t) * H_q + kv * G + g).tolist())
+    return np.unique(np.asarray(out, np.int64))
+

@@ -118,11 +118,13 @@ def _sampled_rows(B, T, Hq, n, seed):
 @pytest.mark.parametrize("name", ["prefill_8k_causal", "prefill_chunk_64k"])
 def test_full_size_sampled(name):
     """Full-size workloads in the benchmark's launch configuration; the oracle
-    computes a sample of rows (first, last, head boundaries, random)."""
+    computes a sample of rows (first, last, head boundaries, random, and one
+    row of every work-group's 256-row block)."""
     inp = gin.make(name)
     w = inp.workload
     og, lg = _run(inp, w.causal, w.q_offset)
-    rows = _sampled_rows(w.B, w.T_q, w.H_q, 384, 7)
+    rows = np.union1d(_sampled_rows(w.B, w.T_q, w.H_q, 384, 7),
+                      gin.rows_per_workgroup(w.B, w.T_q, w.H_q, w.H_kv, seed=8))
     oref, lref = oracle.prefill(inp.q, inp.k, inp.v, causal=w.causal, q_offset=w.q_offset,
                                 rows=rows)
     assert_close(og.reshape(-1, w.d)[rows], oref, lg.reshape(-1)[rows], lref, name=name)

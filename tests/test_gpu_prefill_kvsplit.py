@@ -95,6 +95,7 @@ def test_full_size_chunk_over_long_cache():
     total = w.B * w.T_q * w.H_q
     rows = np.unique(np.concatenate([[0, 1, w.H_q - 1, total // 2, total - 1],
                                      rng.integers(0, total, 250)]))
+    rows = np.union1d(rows, gin.rows_per_workgroup(w.B, w.T_q, w.H_q, w.H_kv, seed=8))
     oref, lref = oracle.prefill(inp.q, inp.k, inp.v, causal=True, q_offset=w.q_offset, rows=rows)
     assert_close(og.reshape(-1, w.d)[rows], oref, lg.reshape(-1)[rows], lref,
                  name="prefill_chunk_256_64k kvsplit")

@@ -74,6 +74,7 @@ def test_full_size_window_sampled():
     total = w.B * w.T_q * w.H_q
     rows = np.unique(np.concatenate([[0, 1, w.H_q - 1, 1030 * w.H_q, total // 2, total - 1],
                                      rng.integers(0, total, 250)]))
+    rows = np.union1d(rows, gin.rows_per_workgroup(w.B, w.T_q, w.H_q, w.H_kv, seed=8))
     oref, lref = oracle.prefill_window(inp.q, inp.k, inp.v, q_offset=w.q_offset, window=w.window,
                                        sink=w.sink, rows=rows)
     assert_close(og.reshape(-1, w.d)[rows], oref, lg.reshape(-1)[rows], lref,
