@@ -53,6 +53,8 @@ def load_library():
     lib.gqa_attn_prefill.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp]
     lib.gqa_attn_decode.restype = i
     lib.gqa_attn_decode.argtypes = [vp, vp, vp, vp, i, i, i, i, vp, f, i, i, vp]
+    lib.gqa_attn_decode_noalloc.restype = i
+    lib.gqa_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, vp, f, i, i, vp]
     lib.gqa_attn_decode_plan.restype = i
     lib.gqa_attn_decode_plan.argtypes = [i, i, i, i, vp, i, vp, vp, vp, vp, vp]
     lib.gqa_attn_decode_split.restype = i
@@ -306,6 +308,24 @@ def decode(q, k, v, kv_len, *, scale: float | None = None, num_splits: int = 0, 
                                         a.ctypes.data, float(scale), int(num_splits),
                                         _dtype_code(q), _stream(q.device))
     _check(rc, "gqa_attn_decode")
+    return out
+
+
+def decode_noalloc(q, k, v, kv_len, *, scale: float | None = None, num_splits: int = 0,
+                   out=None):
+    """gqa_attn_decode_noalloc: decode whose partials live in the library's
+    fixed per-device scratch (no device allocation by the library; pass
+    ``out`` to avoid torch's).  Raises GQAError (status 4) when the split
+    plan's partials exceed the scratch."""
+    B, H_q, H_kv, d, a = _decode_shapes(q, k, v, kv_len)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = _out_like(out, q, (B, H_q, d))
+    rc = load_library().gqa_attn_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H_q,
+                                                H_kv, d, a.ctypes.data, float(scale),
+                                                int(num_splits), _dtype_code(q),
+                                                _stream(q.device))
+    _check(rc, "gqa_attn_decode_noalloc")
     return out
 
 

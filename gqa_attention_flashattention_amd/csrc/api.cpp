@@ -467,6 +467,68 @@ int gqa_attn_decode(const void* q, const void* k, const void* v, void* o, int B,
 
 namespace {
 
+// Scratch of gqa_attn_decode_noalloc: the split partials live in this fixed
+// device array instead of an allocated workspace.  Each device that the
+// library runs on holds its own copy for the life of the process.  Host code
+// never uses the array's name as an address (on the host it is only a
+// stand-in for the symbol): the first call on a device, with that device
+// current, looks the device address up with hipGetSymbolAddress and keeps
+// it per device; kernels receive that pointer.  Every partial the combine
+// reads is written by the split kernel of the same call, so nothing in it
+// has to start at zero.
+static __device__ __align__(256) unsigned char scratch[GQA_ATTN_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_address(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GQA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return GQA_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_attn_decode_noalloc(const void* q, const void* k, const void* v, void* o, int B, int H_q,
+                            int H_kv, int d, const int32_t* kv_len, float scale, int num_splits,
+                            int dtype, void* stream) {
+    int rc = check_decode_args(q, k, v, B, H_q, H_kv, d, kv_len, scale, dtype);
+    if (rc) return rc;
+    if (!o) return GQA_ERR_NULL;
+    HostPlan hp;
+    rc = hp.build(B, H_q, H_kv, kv_len, num_splits);
+    if (rc) return rc;
+    if (workspace_bytes_for(hp.p.total, H_q, d) > (size_t)GQA_ATTN_NOALLOC_SCRATCH_BYTES)
+        return GQA_ERR_RANGE;
+    void* base = nullptr;
+    rc = scratch_address(&base);
+    if (rc) return rc;
+    DecodeWorkspace ws = carve(base, hp.p.total, H_q);
+    (void)hipGetLastError();
+    rc = for_each_chunk(B, kv_len, hp.splits, hp.lens, [&](const DecodePlanChunk& c) {
+        return gqa::launch_decode_split_bf16(q, k, v, ws, c, 1, H_q, H_kv, d, scale,
+                                             (hipStream_t)stream);
+    });
+    if (rc) return rc;
+    return for_each_chunk(B, kv_len, hp.splits, hp.lens, [&](const DecodePlanChunk& c) {
+        return gqa::launch_decode_combine_bf16(ws, c, o, nullptr, 1, H_q, d, (hipStream_t)stream);
+    });
+}
+
+}  // extern "C"
+
+namespace {
+
 // KV-parallel prefill for an already checked argument set (a.window > 0: sink
 // + local-window mask).
 int prefill_kvsplit_impl(const gqa::PrefillArgs& a, int num_splits, void* stream) {

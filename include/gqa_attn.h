@@ -182,6 +182,31 @@ int gqa_attn_decode(const void *q, const void *k, const void *v, void *o, int B,
                     int dtype, void *stream);
 
 /*
+ * Decode that allocates nothing, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same operation, arguments, layouts, split plan and
+ * result as gqa_attn_decode (the same kernels; results are bitwise those of
+ * gqa_attn_decode with the same arguments), but the split partials go to a
+ * fixed scratch array inside the library, GQA_ATTN_NOALLOC_SCRATCH_BYTES per
+ * device, held by every device the library runs on until the process ends.
+ * The call makes no hipMalloc / hipFree and no allocating library call; the
+ * first call on a device looks up that device's scratch address
+ * (hipGetSymbolAddress), so make one call per device before capturing.
+ * The plan's partials, total_splits * H_q * (d + 2) * 4 bytes (see
+ * gqa_attn_decode_plan), must fit in the scratch: larger requests return
+ * GQA_ERR_RANGE before anything is enqueued (e.g. 64 query heads at d = 128
+ * allow 504 splits in total; pass num_splits to stay below).
+ * Every call on a device shares that device's scratch: calls whose kernels
+ * may overlap (different streams, or several host threads without ordering
+ * between their streams) race on it and must be serialised by the caller.
+ * Errors: as gqa_attn_decode, plus GQA_ERR_RANGE (scratch too small).
+ */
+#define GQA_ATTN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int gqa_attn_decode_noalloc(const void *q, const void *k, const void *v, void *o, int B,
+                            int H_q, int H_kv, int d, const int32_t *kv_len, float scale,
+                            int num_splits, int dtype, void *stream);
+
+/*
  * Split plan (host only, no device access).  Sequence b is cut into
  * n_b = ceil(kv_len[b] / L_b) splits of L_b keys (the last may be shorter),
  * split s covering keys [s*L_b, min((s+1)*L_b, kv_len[b])):

@@ -27,6 +27,7 @@ def test_header_declares_the_boundary():
               "gqa_attn_prefill_kvsplit", "gqa_attn_prefill_kvsplit_count",
               "gqa_attn_prefill_window", "gqa_attn_decode_ring", "gqa_attn_decode_quant",
               "gqa_attn_decode_ring_quant", "gqa_attn_prefill_window_kvsplit",
+              "gqa_attn_decode_noalloc",
               "gqa_attn_status_string", "gqa_attn_version"]:
         assert n in names
 
@@ -84,6 +85,26 @@ def _decode(kv_len, **kw):
 ])
 def test_decode_rejects(kv_len, kw, code):
     assert _decode(kv_len, **kw) == code
+
+
+def _decode_noalloc(kv_len, **kw):
+    a = dict(q=P, k=P, v=P, o=P, B=len(kv_len), Hq=8, Hkv=2, d=128, scale=0.1, ns=0, dtype=0)
+    a.update(kw)
+    arr = np.asarray(kv_len, np.int32)
+    return gq.load_library().gqa_attn_decode_noalloc(
+        a["q"], a["k"], a["v"], a["o"], a["B"], a["Hq"], a["Hkv"], a["d"],
+        arr.ctypes.data if kv_len else None, a["scale"], a["ns"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kv_len,kw,code", [
+    ([4], dict(q=None), 1), ([4], dict(o=None), 1), ([], dict(B=1), 1),
+    ([4, 0], {}, 2), ([4], dict(Hq=9), 2), ([4], dict(d=32), 3), ([4], dict(dtype=1), 3),
+    ([4], dict(scale=0.0), 4),
+    # 2 x 4096 one-key splits of 64 query heads: 8192 * 64 * 130 * 4 bytes > 16 MiB
+    ([4096, 4096], dict(Hq=64, Hkv=8, ns=4096), 4),
+])
+def test_decode_noalloc_rejects(kv_len, kw, code):
+    assert _decode_noalloc(kv_len, **kw) == code
 
 
 def _decode_multi(kv_len, **kw):
