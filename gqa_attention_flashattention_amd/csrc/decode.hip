@@ -311,14 +311,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const uint8_t* kseq = k + plan.key_off[sq] * row_bytes + (int64_t)kv * WT::ROW_BYTES;
     const uint8_t* vseq = v + plan.key_off[sq] * row_bytes + (int64_t)kv * WT::ROW_BYTES;
     const int n_tiles = (kend - kbeg + kTile - 1) / kTile;
-    // the first tile's K/V loads go out before anything else
-    WT wt;
-    int tt = wave / HP;
-    auto load = [&](int key0) {
-        if (RING) wt.load(kseq, vseq, row_bytes, key0, kend, lane, rmap);
-        else wt.load(kseq, vseq, row_bytes, key0, kend, lane, Identity{});
+    // NB register tiles per wave.  With two (one column block per wave, where
+    // the registers allow it) a wave's first two tiles are requested together
+    // right after its Q, and from then on the loads of tile i + 2 go out as
+    // soon as tile i's registers are free, so two tiles are always in flight:
+    // a split of two tiles per wave waits for memory once, not twice.  The
+    // loads are unconditional: a tile past the wave's last one clamps every
+    // key to the split's last key (a few cache lines, no HBM stream), which
+    // keeps the load count per iteration fixed and the compiler's wait for a
+    // tile exact (it does not also wait for the tile behind it).
+    constexpr int NB = NH == 1 ? 2 : 1;
+    WT wt[NB];
+    const int tt = wave / HP;
+    auto load = [&](WT& w, int tile) __attribute__((always_inline)) {
+        const int key0 = kbeg + tile * kTile;
+        if (RING) w.load(kseq, vseq, row_bytes, key0, kend, lane, rmap);
+        else w.load(kseq, vseq, row_bytes, key0, kend, lane, Identity{});
     };
-    if (tt < n_tiles) load(kbeg + tt * kTile);
 
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
@@ -392,8 +401,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         lb[h] = 0.f;
     }
 
-    for (; tt < n_tiles; tt += TSTRIDE) {
-        const int key0 = kbeg + tt * kTile;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) load(wt[i], tt + i * TSTRIDE);
+
+    // one tile: S^T = K Q^T, V into the wave's LDS tile (then, if `reload`,
+    // the loads of tile `next` into the same registers), mask, online
+    // softmax, O += P V
+    auto process = [&](WT& tl, int tile, int next, bool reload) __attribute__((always_inline)) {
+        const int key0 = kbeg + tile * kTile;
         // S^T for two 16-key blocks; element i of s[h][blk] is key key0 + g4 + 16 blk + 4 i
         f32x4 s[NH][2];
 #pragma unroll
@@ -403,7 +418,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 s[h][blk] = f32x4{};
 #pragma unroll
                 for (int ks = 0; ks < KSTEPS; ++ks) {
-                    const bf16x8 ka = wt.k_operand(blk, ks);
+                    const bf16x8 ka = tl.k_operand(blk, ks);
                     s[h][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[h][ks], s[h][blk],
                                                                          0, 0, 0);
                     if constexpr (QUANT)
@@ -413,9 +428,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 if constexpr (OFFSET) s[h][blk] -= kc[h];
             }
         wave_lds_fence();                    // previous tile's V reads are done
-        wt.store_v(vt, lane);
-        const int nt = tt + TSTRIDE;
-        if (nt < n_tiles) load(kbeg + nt * kTile);
+        tl.store_v(vt, lane);
+        if (reload) load(tl, next);
         if (key0 + kTile > mask_from || (RING && key0 + kTile > s_end && key0 < wbeg_max)) {
 #pragma unroll
             for (int h = 0; h < NH; ++h)
@@ -472,7 +486,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                     __builtin_bit_cast(bf16x8, a8), pb[h], oacc[h][db], 0, 0, 0);
             }
         }
+    };
+
+    int t = tt;
+    for (; t + NB * TSTRIDE < n_tiles; t += NB * TSTRIDE) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) process(wt[i], t + i * TSTRIDE, t + (i + NB) * TSTRIDE, true);
     }
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+        if (t + i * TSTRIDE < n_tiles) process(wt[i], t + i * TSTRIDE, 0, false);
 
     // ---- merge the wave partials of each KV head through LDS, one column block at a time ----
     const int64_t pidx = (int64_t)plan.split_base + unit;
@@ -525,6 +548,261 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             *(f32x4*)(ws_o + hrow * D + x) = acc;
             if (x == 0) {
                 ws_m[hrow] = mx * c;             // base-2 units
+                ws_l[hrow] = lsum;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Short splits of a bf16 packed cache (at most R = 1 or 2 32-key tiles per
+// wave, one KV head per work-group, at most 16 query rows per KV head), e.g.
+// decode of one 8k sequence in 256-key splits.  There the whole split is in
+// flight at once and the call is bound by how fast the bytes arrive and by
+// the work after the last of them, so this kernel:
+//  * requests every tile of the wave at the start: K and V rows go from HBM
+//    straight into the wave's LDS slots with buffer_load ... lds, four whole
+//    256-byte rows per wave instruction (the register path of the split
+//    kernel fetches K as half cache lines of 16 rows per instruction, which
+//    streams measurably slower);
+//  * reads the K A-operands back with ds_read_b128 and V^T with
+//    ds_read_b64_tr_b16; the 16-byte chunks of each row are XOR-swizzled by
+//    the row (chunk c of row r at c ^ (r mod CPR)) so both reads are free of
+//    bank conflicts;
+//  * merges the four wave partials with one exchange of the running maxima
+//    and one summation pass through LDS;
+//  * finds its sequence's plan entries with one round of kernel-argument
+//    loads when the launch holds one sequence.
+// Per wave R slots of one K and one V tile (16 KiB each at d = 128).
+constexpr int kShortMaxKeys = 2 * kWaves * kTile;   // 256: two tiles per wave
+
+template <int D, int R>
+struct ShortSmem {
+    static constexpr int TILE_ELEMS = kTile * D;              // one K or V tile
+    static constexpr int SLOT_ELEMS = 2 * TILE_ELEMS;         // K then V
+};
+
+template <int D>
+__device__ __forceinline__ int short_swz(int r) { return r & (D / 8 - 1); }
+
+template <int D, int R>
+__global__ __launch_bounds__(kThreads) void decode_short_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, float* __restrict__ ws_m, float* __restrict__ ws_l,
+    float* __restrict__ ws_o, const DecodePlanChunk plan, int T_q, int H_q, int H_kv, int G,
+    float c) {
+    using SM = ShortSmem<D, R>;
+    constexpr int KSTEPS = D / 32;
+    constexpr int DBLK = D / 16;
+    constexpr int CPR = D / 8;                     // 16-byte chunks per row
+    constexpr int ROWS_PER_LOAD = 64 / CPR;        // rows per wave DMA instruction
+    constexpr int LOADS = kTile / ROWS_PER_LOAD;   // DMA instructions per K or V tile
+    typedef __attribute__((address_space(3))) void lds_void_t;
+    // one array per slot (all waves' tiles of that slot): with distinct
+    // arrays the compiler waits for the DMA loads of the slot being read,
+    // not for every DMA load in flight
+    __shared__ __attribute__((aligned(1024))) uint16_t slot0[kWaves * SM::SLOT_ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t slot1[R > 1 ? kWaves * SM::SLOT_ELEMS : 8];
+    __shared__ float mx_lds[kWaves * kCols];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int col = lane & 15;
+    const int g4 = lane >> 4;
+
+    const int kv = blockIdx.x % H_kv;
+    const int unit = blockIdx.x / H_kv;
+    // plan entries: index 0 is loaded with the launch's other arguments; a
+    // launch of several sequences looks its own up
+    int sq = 0;
+    int len = plan.len[0], L = plan.split_len[0], ub = plan.unit_base[0];
+    int64_t key_off = plan.key_off[0];
+    if (plan.nseq > 1) {
+        while (sq + 1 < plan.nseq && plan.unit_base[sq + 1] <= unit) ++sq;
+        len = plan.len[sq];
+        L = plan.split_len[sq];
+        ub = plan.unit_base[sq];
+        key_off = plan.key_off[sq];
+    }
+    const int split = unit - ub;
+    const int kbeg = split * L;
+    const int kend = min(len, kbeg + L);
+    const int b = plan.seq0 + sq;
+    const int ncols = T_q * G;
+    const int pos0 = len - T_q;                    // position of new token 0
+
+    // Q^T operand (column = query row): loaded first, so that the wait for the
+    // first tile covers it
+    const int fc = min(col, ncols - 1);            // columns past the end read a valid row
+    const int tq = fc / G;
+    const int hq = kv * G + fc % G;
+    const int vis_end = min(kend, pos0 + tq + 1);
+    bf16x8 qf[KSTEPS];
+    {
+        const uint16_t* qrow = q + (((int64_t)b * T_q + tq) * H_q + hq) * D + g4 * 8;
+#pragma unroll
+        for (int st = 0; st < KSTEPS; ++st)
+            qf[st] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + st * 32));
+    }
+
+    // the wave's tiles: tile w, w + 4, ... of the split (at most R of them);
+    // every slot is requested, keys past the split end clamp to its last key
+    const int64_t row_elems = (int64_t)H_kv * D;
+    const uint16_t* kseq = k + key_off * row_elems + (int64_t)kv * D;
+    const uint16_t* vseq = v + key_off * row_elems + (int64_t)kv * D;
+    auto wslot = [&](int sl) { return (sl == 0 ? slot0 : slot1) + wave * SM::SLOT_ELEMS; };
+    const int n_tiles = (kend - kbeg + kTile - 1) / kTile;
+#pragma unroll
+    for (int sl = 0; sl < R; ++sl) {
+        const int key0 = kbeg + (wave + kWaves * sl) * kTile;
+        // keys of this tile inside the split: rows past them re-read the last key
+        const int last = kend - 1;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint16_t* src = h == 0 ? kseq : vseq;
+            uint16_t* dst = wslot(sl) + h * SM::TILE_ELEMS;
+            const int kfirst = min(key0, last);
+            __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(src + (int64_t)kfirst * row_elems), (short)0,
+                (int)(kTile * row_elems * 2), 0x00020000);
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                const int r = i * ROWS_PER_LOAD + lane / CPR;
+                const int cc = (lane % CPR) ^ short_swz<D>(r);
+                const int key = min(key0 + r, last);
+                const int off = (int)(((int64_t)(key - kfirst) * row_elems + cc * 8) * 2);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + i * ROWS_PER_LOAD * D),
+                                                         16, off, 0, 0, 2);
+            }
+        }
+    }
+
+    // per-lane LDS read offsets (elements within a tile)
+    int koff[2][KSTEPS];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        const int r = tile_key(col, blk);
+#pragma unroll
+        for (int st = 0; st < KSTEPS; ++st) koff[blk][st] = r * D + (((st * 4 + g4) ^ short_swz<D>(r)) << 3);
+    }
+    // V^T: lane L of group g4 reads key row g4 + 4 (L / 4) (+ 16), dims 4 (L % 4) of each 16-dim block
+    int voff[2][DBLK];
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+        const int r = g4 + 4 * ((lane & 15) >> 2) + 16 * hi;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+            const int x = db * 16 + 4 * (lane & 3);
+            voff[hi][db] = r * D + (((x >> 3) ^ short_swz<D>(r)) << 3) + (x & 7);
+        }
+    }
+
+    f32x4 oacc[DBLK];
+#pragma unroll
+    for (int i = 0; i < DBLK; ++i) oacc[i] = f32x4{};
+    float m_run = -INFINITY, l_run = 0.f;
+    const int mask_from = min(kend, pos0 + 1);     // keys before it are visible to every token
+
+#pragma unroll
+    for (int sl = 0; sl < R; ++sl) {
+        // this slot's DMA writes (and Q's load) have landed: R - 1 - sl slots behind it
+        if (sl == R - 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * LOADS) : "memory");
+        const int tile = wave + kWaves * sl;
+        if (tile >= n_tiles) break;                // wave-uniform
+        const int key0 = kbeg + tile * kTile;
+        const uint16_t* kt = wslot(sl);
+        const uint16_t* vt = kt + SM::TILE_ELEMS;
+        f32x4 s[2];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            s[blk] = f32x4{};
+#pragma unroll
+            for (int st = 0; st < KSTEPS; ++st) {
+                const bf16x8 ka = *(const bf16x8*)(kt + koff[blk][st]);
+                s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[st], s[blk], 0, 0, 0);
+            }
+        }
+        if (key0 + kTile > mask_from) {
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (key0 + g4 + 16 * blk + 4 * i >= vis_end) s[blk][i] = -INFINITY;
+        }
+        float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+        mt = fmaxf(mt, xor16(mt));
+        mt = fmaxf(mt, xor32(mt));
+        const float m_new = fmaxf(m_run, mt);
+        const float mc = (m_new == -INFINITY) ? 0.f : m_new * c;
+        const float corr = fast_exp2(m_run * c - mc);
+        float p[8];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p[blk * 4 + i] = fast_exp2(__builtin_fmaf(s[blk][i], c, -mc));
+        l_run = l_run * corr + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+        m_run = m_new;
+        const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                          pack_bf16x2(p[6], p[7])};
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+            const s16x4 lo = lds_read_tr16(vt + voff[0][db]);
+            const s16x4 hi = lds_read_tr16(vt + voff[1][db]);
+            const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            oacc[db] *= corr;
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a8), pb,
+                                                              oacc[db], 0, 0, 0);
+        }
+    }
+
+    // ---- merge the four wave partials: common max, rescale, sum through LDS ----
+    float lr = l_run;
+    lr += xor16(lr);
+    lr += xor32(lr);
+    if (g4 == 0) mx_lds[wave * kCols + col] = m_run;
+    // the merge area overlays the tile slots: no DMA write of this wave may
+    // still be pending (a wave with fewer than R tiles skipped the last wait)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();                               // every wave is also done with its tiles
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, mx_lds[w * kCols + col]);
+    const float sc = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - mx) * c);
+    // wave area: O [16][CS] (columns padded by 4 floats against bank
+    // conflicts) then l [16], overlaying the tile slots
+    float* mrg = (float*)slot0;
+    constexpr int CS = D + 4;
+    constexpr int WSTRIDE = kCols * CS + kCols;
+    static_assert(kWaves * WSTRIDE * 4 <= kWaves * SM::SLOT_ELEMS * 2, "merge area fits slot 0");
+    float* mw = mrg + wave * WSTRIDE;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) *(f32x4*)(mw + col * CS + db * 16 + g4 * 4) = oacc[db] * sc;
+    if (g4 == 0) mw[kCols * CS + col] = lr * sc;
+    __syncthreads();
+    const int64_t pidx = (int64_t)plan.split_base + unit;
+    constexpr int PER = kCols * D / 4 / kThreads;  // f32x4 outputs per thread
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int e = tid + u * kThreads;
+        const int cc = e / (D / 4), x = (e % (D / 4)) * 4;
+        f32x4 acc = *(const f32x4*)(mrg + cc * CS + x);
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) acc += *(const f32x4*)(mrg + w * WSTRIDE + cc * CS + x);
+        if (cc < ncols) {
+            const int64_t hrow = (pidx * T_q + cc / G) * H_q + (int64_t)kv * G + cc % G;
+            *(f32x4*)(ws_o + hrow * D + x) = acc;
+            if (x == 0) {
+                float lsum = 0.f, mcc = -INFINITY;
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) {
+                    lsum += mrg[w * WSTRIDE + kCols * CS + cc];
+                    mcc = fmaxf(mcc, mx_lds[w * kCols + cc]);
+                }
+                ws_m[hrow] = mcc * c;                  // base-2 units
                 ws_l[hrow] = lsum;
             }
         }
@@ -865,7 +1143,11 @@ int64_t decode_workgroups_per_split(DecodeKind kind, int T_q, int G, int H_kv, i
         pairs = kind == DecodeKind::Bf16 || kind == DecodeKind::Ring;
     }
     const int hp = (pairs && H_kv % 2 == 0 && split_len >= kPairMinSplitLen) ? 2 : 1;
-    return n_hg * (H_kv / hp);
+    // a short-split work-group with two tiles per wave holds the LDS of two
+    // (decode_short_kernel), so it counts twice against the resident slots
+    const int occ = (kind == DecodeKind::Bf16 && T_q * G <= kCols && hp == 1 &&
+                     split_len > kShortMaxKeys / 2 && split_len <= kShortMaxKeys) ? 2 : 1;
+    return n_hg * (H_kv / hp) * occ;
 }
 
 int decode_column_groups(int T_q, int G) {
@@ -933,6 +1215,33 @@ static hipError_t split_dispatch(const void* q, const void* k, const void* v,
     const int hp = (KVF == kKvBf16 && H_kv % 2 == 0 && min_len >= kPairMinSplitLen) ? 2 : 1;
     const float c = scale * kLog2e;
     const int64_t uh = (int64_t)plan.units * n_hg;
+    if (KVF == kKvBf16 && !RING && T_q * G <= kCols && hp == 1) {
+        // short splits: every tile of a wave requested at once (see decode_short_kernel)
+        int max_len = 0;
+        for (int i = 0; i < plan.nseq; ++i)
+            max_len = std::max(max_len, std::min((int)plan.split_len[i], (int)plan.len[i]));
+        if (max_len <= kShortMaxKeys) {
+            const dim3 sgrid((unsigned)(plan.units * H_kv));
+            const bool two = max_len > kShortMaxKeys / 2;
+            if (d == 128 && two)
+                hipLaunchKernelGGL((decode_short_kernel<128, 2>), sgrid, dim3(kThreads), 0, stream,
+                                   (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                   ws.m, ws.l, ws.o, plan, T_q, H_q, H_kv, G, c);
+            else if (d == 128)
+                hipLaunchKernelGGL((decode_short_kernel<128, 1>), sgrid, dim3(kThreads), 0, stream,
+                                   (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                   ws.m, ws.l, ws.o, plan, T_q, H_q, H_kv, G, c);
+            else if (two)
+                hipLaunchKernelGGL((decode_short_kernel<64, 2>), sgrid, dim3(kThreads), 0, stream,
+                                   (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                   ws.m, ws.l, ws.o, plan, T_q, H_q, H_kv, G, c);
+            else
+                hipLaunchKernelGGL((decode_short_kernel<64, 1>), sgrid, dim3(kThreads), 0, stream,
+                                   (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                   ws.m, ws.l, ws.o, plan, T_q, H_q, H_kv, G, c);
+            return hipGetLastError();
+        }
+    }
     if (d == 128 && nh == 1)
         launch_split<128, 1, RING, KVF>(hp, uh, q, k, v, ws, plan, T_q, H_q, H_kv, G, n_hg, c, ring, sc, stream);
     else if (d == 128)

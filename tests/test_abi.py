@@ -284,8 +284,9 @@ def _documented_auto_len(kv_len, H_kv, cus=256):
     (multiples of 64 up to 1024, of 128 up to 2048, of 256 beyond)
     minimising ceil(W / R) * (L + 256) summed over launches of 64 sequences
     plus 8 x the largest split count of a sequence,
-    W = split work-groups (H_kv / 2 per split from 512 keys on, else H_kv),
-    R = 2 per compute unit; ties to the longer L."""
+    W = split work-groups (H_kv / 2 per split from 512 keys on, else H_kv;
+    those of 129-256 keys count twice), R = 2 per compute unit; ties to the
+    longer L."""
     slots = 2 * cus
     hi = min(8192, max(128, -(-max(kv_len) // 64) * 64))
     best, best_cost = None, None
@@ -293,6 +294,8 @@ def _documented_auto_len(kv_len, H_kv, cus=256):
              if L <= 1024 or (L <= 2048 and L % 128 == 0) or L % 256 == 0]
     for L in cands:
         per = H_kv // 2 if (H_kv % 2 == 0 and L >= 512) else H_kv
+        if 128 < L <= 256:
+            per *= 2
         cost = 0
         for b0 in range(0, len(kv_len), 64):
             n = sum(-(-x // L) for x in kv_len[b0:b0 + 64])
