@@ -586,7 +586,7 @@ template <int D>
 __device__ __forceinline__ int short_swz(int r) { return r & (D / 8 - 1); }
 
 template <int D, int R>
-__global__ __launch_bounds__(kThreads) void decode_short_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R == 1 ? 2 : 1))) void decode_short_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ ws_m, float* __restrict__ ws_l,
     float* __restrict__ ws_o, const DecodePlanChunk plan, int T_q, int H_q, int H_kv, int G,
@@ -603,7 +603,6 @@ __global__ __launch_bounds__(kThreads) void decode_short_kernel(
     // not for every DMA load in flight
     __shared__ __attribute__((aligned(1024))) uint16_t slot0[kWaves * SM::SLOT_ELEMS];
     __shared__ __attribute__((aligned(1024))) uint16_t slot1[R > 1 ? kWaves * SM::SLOT_ELEMS : 8];
-    __shared__ float mx_lds[kWaves * kCols];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -735,16 +734,27 @@ __global__ __launch_bounds__(kThreads) void decode_short_kernel(
                          fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
         mt = fmaxf(mt, xor16(mt));
         mt = fmaxf(mt, xor32(mt));
-        const float m_new = fmaxf(m_run, mt);
-        const float mc = (m_new == -INFINITY) ? 0.f : m_new * c;
-        const float corr = fast_exp2(m_run * c - mc);
+        // Lazy rescale: the reference max moves only when a column's tile max
+        // exceeds it by more than 2^8 in the exponentials (then O and l are
+        // rescaled); otherwise P <= 2^8 against the old reference, which the
+        // fp32 sums carry exactly as well.  The first tile sets it.
+        if (sl == 0) {
+            m_run = mt;
+        } else if (__builtin_amdgcn_ballot_w64(mt * c > m_run * c + 8.f) != 0) {
+            const float m_new = fmaxf(m_run, mt);
+            const float corr = (m_new == -INFINITY) ? 1.f : fast_exp2((m_run - m_new) * c);
+            l_run *= corr;
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db) oacc[db] *= corr;
+            m_run = m_new;
+        }
+        const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
         float p[8];
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
             for (int i = 0; i < 4; ++i) p[blk * 4 + i] = fast_exp2(__builtin_fmaf(s[blk][i], c, -mc));
-        l_run = l_run * corr + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
-        m_run = m_new;
+        l_run += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                           pack_bf16x2(p[6], p[7])};
         const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
@@ -753,58 +763,62 @@ __global__ __launch_bounds__(kThreads) void decode_short_kernel(
             const s16x4 lo = lds_read_tr16(vt + voff[0][db]);
             const s16x4 hi = lds_read_tr16(vt + voff[1][db]);
             const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            oacc[db] *= corr;
             oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a8), pb,
                                                               oacc[db], 0, 0, 0);
         }
     }
 
-    // ---- merge the four wave partials: common max, rescale, sum through LDS ----
+    // ---- merge the four wave partials ----
+    // Each wave puts its unnormalised partial (m, l, O) into its own slot-0
+    // area, which no other wave reads before the barrier; after it, every
+    // thread merges four waves' values for its outputs.
     float lr = l_run;
     lr += xor16(lr);
     lr += xor32(lr);
-    if (g4 == 0) mx_lds[wave * kCols + col] = m_run;
-    // the merge area overlays the tile slots: no DMA write of this wave may
-    // still be pending (a wave with fewer than R tiles skipped the last wait)
+    // no DMA write into this wave's slots may still be pending (a wave with
+    // fewer than R tiles skipped the last wait)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();                               // every wave is also done with its tiles
-    float mx = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, mx_lds[w * kCols + col]);
-    const float sc = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - mx) * c);
     // wave area: O [16][CS] (columns padded by 4 floats against bank
-    // conflicts) then l [16], overlaying the tile slots
-    float* mrg = (float*)slot0;
+    // conflicts), then l [16], then m [16]
     constexpr int CS = D + 4;
-    constexpr int WSTRIDE = kCols * CS + kCols;
-    static_assert(kWaves * WSTRIDE * 4 <= kWaves * SM::SLOT_ELEMS * 2, "merge area fits slot 0");
-    float* mw = mrg + wave * WSTRIDE;
+    constexpr int AREA = kCols * CS + 2 * kCols;             // floats
+    static_assert(AREA * 4 <= SM::SLOT_ELEMS * 2, "a wave's merge area fits its slot");
+    constexpr int AREA_STRIDE = SM::SLOT_ELEMS / 2;          // floats between waves' areas
+    float* mw = (float*)(slot0 + wave * SM::SLOT_ELEMS);
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) *(f32x4*)(mw + col * CS + db * 16 + g4 * 4) = oacc[db] * sc;
-    if (g4 == 0) mw[kCols * CS + col] = lr * sc;
+    for (int db = 0; db < DBLK; ++db) *(f32x4*)(mw + col * CS + db * 16 + g4 * 4) = oacc[db];
+    if (g4 == 0) {
+        mw[kCols * CS + col] = lr;
+        mw[kCols * CS + kCols + col] = m_run;
+    }
     __syncthreads();
+    const float* mrg = (const float*)slot0;
     const int64_t pidx = (int64_t)plan.split_base + unit;
     constexpr int PER = kCols * D / 4 / kThreads;  // f32x4 outputs per thread
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
         const int e = tid + u * kThreads;
         const int cc = e / (D / 4), x = (e % (D / 4)) * 4;
-        f32x4 acc = *(const f32x4*)(mrg + cc * CS + x);
+        if (cc >= ncols) continue;
+        float mwv[kWaves], mx = -INFINITY;
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) acc += *(const f32x4*)(mrg + w * WSTRIDE + cc * CS + x);
-        if (cc < ncols) {
-            const int64_t hrow = (pidx * T_q + cc / G) * H_q + (int64_t)kv * G + cc % G;
-            *(f32x4*)(ws_o + hrow * D + x) = acc;
-            if (x == 0) {
-                float lsum = 0.f, mcc = -INFINITY;
+        for (int w = 0; w < kWaves; ++w) {
+            mwv[w] = mrg[w * AREA_STRIDE + kCols * CS + kCols + cc];
+            mx = fmaxf(mx, mwv[w]);
+        }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        float lsum = 0.f;
 #pragma unroll
-                for (int w = 0; w < kWaves; ++w) {
-                    lsum += mrg[w * WSTRIDE + kCols * CS + cc];
-                    mcc = fmaxf(mcc, mx_lds[w * kCols + cc]);
-                }
-                ws_m[hrow] = mcc * c;                  // base-2 units
-                ws_l[hrow] = lsum;
-            }
+        for (int w = 0; w < kWaves; ++w) {
+            const float sc = (mwv[w] == -INFINITY) ? 0.f : fast_exp2((mwv[w] - mx) * c);
+            acc += sc * *(const f32x4*)(mrg + w * AREA_STRIDE + cc * CS + x);
+            lsum += sc * mrg[w * AREA_STRIDE + kCols * CS + cc];
+        }
+        const int64_t hrow = (pidx * T_q + cc / G) * H_q + (int64_t)kv * G + cc % G;
+        *(f32x4*)(ws_o + hrow * D + x) = acc;
+        if (x == 0) {
+            ws_m[hrow] = mx * c;                   // base-2 units
+            ws_l[hrow] = lsum;
         }
     }
 }
