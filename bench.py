@@ -183,6 +183,41 @@ def bench_decode(name, steps, warmup):
                 call_samples=call_samples)
 
 
+def bench_gqa_reuse(groups, steps, S=32768, H_kv=8, d=128):
+    """Decode of one S-key sequence with H_kv = 8 and H_q = G * H_kv for each
+    G in `groups`: the same K/V bytes serve G query heads per KV head.  Under
+    rocprofv3 --pmc FETCH_SIZE the split kernel's fetched bytes show whether
+    K/V are read once for all G heads (the count must not grow with G)."""
+    import torch
+    import gqa_attention_flashattention_amd as gq
+    from gqa_attention_flashattention_amd import inputs as gin
+    out = []
+    n_copies = 4
+    kv_len = np.array([S], np.int32)
+    kv_bytes = S * H_kv * d * 2 * 2
+    for G in groups:
+        inp = gin.random_case("decode", "bf16", B=1, H_q=G * H_kv, H_kv=H_kv, d=d, kv_len=[S],
+                              seed=G)
+        q = dev_tensor(inp.q_store)
+        k0, v0 = dev_tensor(inp.k_store), dev_tensor(inp.v_store)
+        ks = [k0] + [k0.clone() for _ in range(n_copies - 1)]
+        vs = [v0] + [v0.clone() for _ in range(n_copies - 1)]
+        plan = gq.decode_plan(1, G * H_kv, H_kv, d, kv_len)
+        ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device="cuda")
+        fns = [lambda i=i: gq.decode_split(q, ks[i % n_copies], vs[i % n_copies], kv_len, ws)
+               for i in range(steps)]
+        for f in fns[:3]:
+            f()
+        torch.cuda.synchronize()
+        ms = time_graph(fns)
+        out.append({"G": G, "H_q": G * H_kv, "H_kv": H_kv, "S_kv": S, "kv_bytes": kv_bytes,
+                    "splits": int(plan["total_splits"]), "split_us": round(ms * 1e3, 3),
+                    "GBps": round(kv_bytes / (ms * 1e-3) / 1e9, 1)})
+        del ks, vs, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_decode_multi(name, steps, warmup):
     """Multi-token decode (T_q new tokens per sequence) through the one-call
     entry point, timed by graph replay over rotated K/V copies."""
@@ -460,7 +495,20 @@ def decode_heads_per_wg(plan, w):
     return 2 if (w.H_kv % 2 == 0 and int(plan["split_len"]) >= DECODE_PAIR_MIN_SPLIT_LEN) else 1
 
 
+# splits of at most this many keys (one KV head per work-group, G * T_q <= 16)
+# run the short-split kernel, with two LDS slots per wave above half of it
+DECODE_SHORT_MAX_KEYS = 256
+
+
+def decode_is_short(plan, w):
+    return (decode_heads_per_wg(plan, w) == 1 and w.G * w.T_q <= 16
+            and int(plan["split_len"]) <= DECODE_SHORT_MAX_KEYS)
+
+
 def decode_split_kernel_name(plan, w):
+    if decode_is_short(plan, w):
+        r = 2 if int(plan["split_len"]) > DECODE_SHORT_MAX_KEYS // 2 else 1
+        return f"decode_short_kernel<{w.d},{r}>"
     return f"decode_split_kernel<{w.d},1,false,0,{decode_heads_per_wg(plan, w)}>"
 
 
@@ -675,11 +723,15 @@ def main():
     ap.add_argument("--scale-workloads", default="decode_varlen_b16,decode_128k",
                     help="larger plain-decode workloads (reported under decode_at_scale)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["decode", "prefill", "prefill_chunk", "decode_multi", "prefill_kvsplit",
+    ap.add_argument("--only", choices=["decode", "prefill", "prefill_chunk", "gqa_reuse", "decode_multi", "prefill_kvsplit",
                                        "prefill_window", "decode_ring", "decode_quant",
                                        "decode_ring_quant"],
                     default=None,
                     help="run one path only (profiling runs); prints a partial line")
+    ap.add_argument("--gqa-groups", default="1,2,4,8",
+                    help="--only gqa_reuse: query heads per KV head to run (H_kv = 8)")
+    ap.add_argument("--gqa-keys", type=int, default=32768,
+                    help="--only gqa_reuse: keys of the one sequence")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -697,6 +749,11 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
 
+    if args.only == "gqa_reuse":
+        groups = [int(g) for g in args.gqa_groups.split(",")]
+        print(json.dumps({"gqa_reuse": bench_gqa_reuse(groups, min(args.steps, 100),
+                                                       S=args.gqa_keys)}), flush=True)
+        return
     if args.only == "decode_multi":
         mul = bench_decode_multi(args.multi_workload, min(args.steps, 200), args.warmup)
         log(f"[bench] decode_multi {mul['ms'] * 1e3:.2f} us/call "

@@ -13,6 +13,12 @@
         "kernel@grid threads"), which bench.py reports as `roofline.traffic`
         while the kernel source it was measured on is unchanged (sha256
         recorded per kernel).
+    python -m gqa_attention_flashattention_amd.profile_summary gqa --run G=<dir> [...] \
+            --kernel K --kv-bytes N --copy-mib M --cmd C
+        FETCH_SIZE per dispatch of kernel K in one `rocprofv3 --pmc FETCH_SIZE`
+        run per G (query heads per KV head), scaled by that run's copy
+        calibration, against the N bytes of K and V the launch must read:
+        the GQA reuse check (the fetched bytes must not grow with G).
     python -m gqa_attention_flashattention_amd.profile_summary mfma <dir> [<dir> ...] --cmd C ...
         MFMA utilisation per dispatch from `rocprofv3 --pmc` runs that hold
         GRBM_GUI_ACTIVE, SQ_VALU_MFMA_BUSY_CYCLES and, where collected,
@@ -51,6 +57,8 @@ FLOPS_PER_MOP = 512
 # kernel short name -> source file whose hash guards its traffic record
 KERNEL_SOURCES = {
     "decode_split_kernel": "csrc/decode.hip",
+    "decode_short_kernel": "csrc/decode.hip",
+    "decode_wide_kernel": "csrc/decode.hip",
     "decode_combine_kernel": "csrc/decode.hip",
     "prefill_bf16_kernel": "csrc/prefill_bf16.hip",
     "prefill_f32_kernel": "csrc/prefill_f32.hip",
@@ -148,11 +156,49 @@ def main():
     tr.add_argument("--cmd-write", default="")
     tr.add_argument("--copy-mib", type=float, required=True)
     tr.add_argument("--title", default="HBM traffic per dispatch")
+    gq_ = sub.add_parser("gqa")
+    gq_.add_argument("--run", action="append", required=True, help="G=<rocprofv3 output dir>")
+    gq_.add_argument("--kernel", required=True, help="kernel short-name prefix")
+    gq_.add_argument("--kv-bytes", type=float, required=True)
+    gq_.add_argument("--copy-mib", type=float, required=True)
+    gq_.add_argument("--cmd", default="")
+    gq_.add_argument("--title", default="GQA reuse: HBM fetch of the decode split kernel against G")
     mf = sub.add_parser("mfma")
     mf.add_argument("dirs", nargs="+")
     mf.add_argument("--cmd", action="append", default=[])
     mf.add_argument("--title", default="MFMA utilisation per dispatch")
     args = ap.parse_args()
+
+    if args.mode == "gqa":
+        copy_kib = args.copy_mib * 1024.0
+        print(f"# {args.title}\n")
+        if args.cmd:
+            print(f"Command (one run per G):\n\n    {args.cmd}\n")
+        print(f"FETCH_SIZE of each run is scaled by what it reads for a plain device copy of "
+              f"{args.copy_mib:g} MiB run first in the same process. K/V bytes per launch: "
+              f"{args.kv_bytes:.6g}.\n")
+        print("| G (query heads per KV head) | kernel@grid | dispatches | FETCH KiB (median) "
+              "| calibration | fetched bytes | fetched / K+V bytes |")
+        print("|---|---|---|---|---|---|---|")
+        for spec in args.run:
+            g, d = spec.split("=", 1)
+            table = counters(d)
+            cal = None
+            for k, cs in table.items():
+                if "copy" in k.lower() or "elementwise" in k.lower():
+                    big = [v for v in cs.get("FETCH_SIZE", []) if v > 0.5 * copy_kib]
+                    if big:
+                        cal = copy_kib / statistics.median(big)
+            if cal is None:
+                raise RuntimeError(f"{d}: no calibration copy")
+            for k, cs in sorted(table.items()):
+                if not k.startswith(args.kernel):
+                    continue
+                fm = statistics.median(cs["FETCH_SIZE"])
+                b = fm * cal * 1024.0
+                print(f"| {g} | `{k}` | {len(cs['FETCH_SIZE'])} | {fm:.0f} | x{cal:.4f} | {b:.6g} "
+                      f"| {b / args.kv_bytes:.4f} |")
+        return
 
     if args.mode == "mfma":
         table = mfma_table(args.dirs)
