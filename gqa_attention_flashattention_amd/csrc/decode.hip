@@ -311,17 +311,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const uint8_t* kseq = k + plan.key_off[sq] * row_bytes + (int64_t)kv * WT::ROW_BYTES;
     const uint8_t* vseq = v + plan.key_off[sq] * row_bytes + (int64_t)kv * WT::ROW_BYTES;
     const int n_tiles = (kend - kbeg + kTile - 1) / kTile;
-    // NB register tiles per wave.  With two (one column block per wave, where
-    // the registers allow it) a wave's first two tiles are requested together
-    // right after its Q, and from then on the loads of tile i + 2 go out as
-    // soon as tile i's registers are free, so two tiles are always in flight:
-    // a split of two tiles per wave waits for memory once, not twice.  The
-    // loads are unconditional: a tile past the wave's last one clamps every
-    // key to the split's last key (a few cache lines, no HBM stream), which
-    // keeps the load count per iteration fixed and the compiler's wait for a
-    // tile exact (it does not also wait for the tile behind it).
-    constexpr int NB = NH == 1 ? 2 : 1;
-    WT wt[NB];
+    // One register tile per wave: the loads of the wave's next tile go out as
+    // soon as the current tile's K has fed the MFMAs and its V is in LDS.
+    // (Two tiles in flight per wave measured 1-4% slower on the long and the
+    // quantised batches; short splits use decode_short_kernel instead.)
+    WT wt;
     const int tt = wave / HP;
     auto load = [&](WT& w, int tile) __attribute__((always_inline)) {
         const int key0 = kbeg + tile * kTile;
@@ -401,8 +395,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         lb[h] = 0.f;
     }
 
-#pragma unroll
-    for (int i = 0; i < NB; ++i) load(wt[i], tt + i * TSTRIDE);
+    load(wt, tt);
 
     // one tile: S^T = K Q^T, V into the wave's LDS tile (then, if `reload`,
     // the loads of tile `next` into the same registers), mask, online
@@ -489,13 +482,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     };
 
     int t = tt;
-    for (; t + NB * TSTRIDE < n_tiles; t += NB * TSTRIDE) {
-#pragma unroll
-        for (int i = 0; i < NB; ++i) process(wt[i], t + i * TSTRIDE, t + (i + NB) * TSTRIDE, true);
-    }
-#pragma unroll
-    for (int i = 0; i < NB; ++i)
-        if (t + i * TSTRIDE < n_tiles) process(wt[i], t + i * TSTRIDE, 0, false);
+    for (; t + TSTRIDE < n_tiles; t += TSTRIDE) process(wt, t, t + TSTRIDE, true);
+    if (t < n_tiles) process(wt, t, 0, false);
 
     // ---- merge the wave partials of each KV head through LDS, one column block at a time ----
     const int64_t pidx = (int64_t)plan.split_base + unit;
