@@ -495,25 +495,25 @@ def decode_heads_per_wg(plan, w):
     return 2 if (w.H_kv % 2 == 0 and int(plan["split_len"]) >= DECODE_PAIR_MIN_SPLIT_LEN) else 1
 
 
-# splits of at most this many keys (one KV head per work-group, G * T_q <= 16)
-# run the short-split kernel, with two LDS slots per wave above half of it
-DECODE_SHORT_MAX_KEYS = 256
+# bf16 caches with at most 16 query rows per KV head stream K/V into LDS, one
+# KV head per work-group, with two LDS slots per wave above this many keys
+DECODE_STREAM_ONE_SLOT_KEYS = 128
 
 
-def decode_is_short(plan, w):
-    return (decode_heads_per_wg(plan, w) == 1 and w.G * w.T_q <= 16
-            and int(plan["split_len"]) <= DECODE_SHORT_MAX_KEYS)
+def decode_is_stream(w):
+    return w.G * w.T_q <= 16
 
 
 def decode_split_kernel_name(plan, w):
-    if decode_is_short(plan, w):
-        r = 2 if int(plan["split_len"]) > DECODE_SHORT_MAX_KEYS // 2 else 1
-        return f"decode_short_kernel<{w.d},{r}>"
+    if decode_is_stream(w):
+        r = 2 if int(plan["split_len"]) > DECODE_STREAM_ONE_SLOT_KEYS else 1
+        return f"decode_stream_kernel<{w.d},{r},false>"
     return f"decode_split_kernel<{w.d},1,false,0,{decode_heads_per_wg(plan, w)}>"
 
 
 def decode_split_grid(plan, w):
-    return int(plan["total_splits"]) * (w.H_kv // decode_heads_per_wg(plan, w)) * 256
+    hp = 1 if decode_is_stream(w) else decode_heads_per_wg(plan, w)
+    return int(plan["total_splits"]) * (w.H_kv // hp) * 256
 
 
 def prefill_grid(w):

@@ -314,7 +314,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // One register tile per wave: the loads of the wave's next tile go out as
     // soon as the current tile's K has fed the MFMAs and its V is in LDS.
     // (Two tiles in flight per wave measured 1-4% slower on the long and the
-    // quantised batches; short splits use decode_short_kernel instead.)
+    // quantised batches; bf16 caches with one column block use
+    // decode_stream_kernel instead.)
     WT wt;
     const int tt = wave / HP;
     auto load = [&](WT& w, int tile) __attribute__((always_inline)) {
@@ -543,54 +544,77 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 }
 
 // ---------------------------------------------------------------------------
-// Short splits of a bf16 packed cache (at most R = 1 or 2 32-key tiles per
-// wave, one KV head per work-group, at most 16 query rows per KV head), e.g.
-// decode of one 8k sequence in 256-key splits.  There the whole split is in
-// flight at once and the call is bound by how fast the bytes arrive and by
-// the work after the last of them, so this kernel:
-//  * requests every tile of the wave at the start: K and V rows go from HBM
-//    straight into the wave's LDS slots with buffer_load ... lds, four whole
-//    256-byte rows per wave instruction (the register path of the split
-//    kernel fetches K as half cache lines of 16 rows per instruction, which
-//    streams measurably slower);
-//  * reads the K A-operands back with ds_read_b128 and V^T with
+// bf16 caches (packed or ring) with at most 16 query rows per KV head (one new
+// token of up to 16 query heads per KV head, or a few new tokens of fewer),
+// one KV head per work-group: the split kernel's job with the K/V bytes
+// streamed into LDS instead of registers.
+//  * Every wave walks its 32-key tiles (tile w, w + 4, ... of the split)
+//    through a ring of R LDS slots of its own: K and V rows go from HBM
+//    straight into a slot with buffer_load ... lds, four whole 256-byte rows
+//    per wave instruction (the register path fetches K as half cache lines of
+//    16 rows per instruction, which streams measurably slower).  A slot is
+//    refilled with the wave's tile i + R as soon as tile i is read, so R
+//    tiles stay in flight per wave and no barrier is needed.
+//  * K A-operands are read back with ds_read_b128, V^T with
 //    ds_read_b64_tr_b16; the 16-byte chunks of each row are XOR-swizzled by
-//    the row (chunk c of row r at c ^ (r mod CPR)) so both reads are free of
-//    bank conflicts;
-//  * merges the four wave partials with one exchange of the running maxima
-//    and one summation pass through LDS;
-//  * finds its sequence's plan entries with one round of kernel-argument
-//    loads when the launch holds one sequence.
-// Per wave R slots of one K and one V tile (16 KiB each at d = 128).
-constexpr int kShortMaxKeys = 2 * kWaves * kTile;   // 256: two tiles per wave
+//    the row (chunk c of row r at c ^ (r mod CPR)), which keeps both reads
+//    free of bank conflicts.
+//  * One LDS array per slot: the compiler then waits for the DMA loads of the
+//    slot being read, not for every DMA load in flight.
+//  * The four wave partials meet once at the end: each wave leaves its
+//    unnormalised partial in its own slot, one barrier, then every thread
+//    merges four waves' values for its outputs.
+//  * A launch of one sequence finds its plan entries with one round of
+//    kernel-argument loads.
+// With R = 2 a work-group holds 128 KiB of LDS (one per compute unit); with
+// R = 1 (splits of at most 128 keys, one tile per wave) 64 KiB.
+constexpr int kStreamOneSlotKeys = kWaves * kTile;   // 128: one tile per wave
 
-template <int D, int R>
-struct ShortSmem {
+// One wave-wide 16-byte-per-lane load from a buffer straight into LDS
+// (lane l's 16 bytes at lds_byte + 16 l).  Written as inline assembly so that
+// the compiler does not track it: it would otherwise wait for every LDS load
+// in flight before any LDS read it cannot attribute to a particular one; the
+// kernels that use it wait for these loads themselves (s_waitcnt vmcnt) and
+// issue no other vector-memory loads.
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, int range) {
+    const uint64_t a = (uint64_t)base;
+    return i32x4{(int)(uint32_t)a, (int)(uint32_t)((a >> 32) & 0xffff), range, 0x00020000};
+}
+__device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t lds_byte, int voffset) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                 :: "s"(lds_byte), "v"(voffset), "s"(rsrc) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+template <int D>
+struct StreamSmem {
     static constexpr int TILE_ELEMS = kTile * D;              // one K or V tile
     static constexpr int SLOT_ELEMS = 2 * TILE_ELEMS;         // K then V
 };
 
 template <int D>
-__device__ __forceinline__ int short_swz(int r) { return r & (D / 8 - 1); }
+__device__ __forceinline__ int stream_swz(int r) { return r & (D / 8 - 1); }
 
-template <int D, int R>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R == 1 ? 2 : 1))) void decode_short_kernel(
+template <int D, int R, bool RING>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R == 1 ? 2 : 1))) void decode_stream_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ ws_m, float* __restrict__ ws_l,
     float* __restrict__ ws_o, const DecodePlanChunk plan, int T_q, int H_q, int H_kv, int G,
-    float c) {
-    using SM = ShortSmem<D, R>;
+    float c, RingArgs ring) {
+    using SM = StreamSmem<D>;
     constexpr int KSTEPS = D / 32;
     constexpr int DBLK = D / 16;
     constexpr int CPR = D / 8;                     // 16-byte chunks per row
     constexpr int ROWS_PER_LOAD = 64 / CPR;        // rows per wave DMA instruction
     constexpr int LOADS = kTile / ROWS_PER_LOAD;   // DMA instructions per K or V tile
-    typedef __attribute__((address_space(3))) void lds_void_t;
-    // one array per slot (all waves' tiles of that slot): with distinct
-    // arrays the compiler waits for the DMA loads of the slot being read,
-    // not for every DMA load in flight
+    constexpr int LPT = 2 * LOADS;                 // per tile (K and V)
+    static_assert(R == 1 || R == 2, "one or two slots per wave");
     __shared__ __attribute__((aligned(1024))) uint16_t slot0[kWaves * SM::SLOT_ELEMS];
     __shared__ __attribute__((aligned(1024))) uint16_t slot1[R > 1 ? kWaves * SM::SLOT_ELEMS : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t qlds[kWaves * kCols * D];   // per wave
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -604,12 +628,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R =
     // launch of several sequences looks its own up
     int sq = 0;
     int len = plan.len[0], L = plan.split_len[0], ub = plan.unit_base[0];
+    int ntok = plan.ntok[0];
     int64_t key_off = plan.key_off[0];
     if (plan.nseq > 1) {
         while (sq + 1 < plan.nseq && plan.unit_base[sq + 1] <= unit) ++sq;
         len = plan.len[sq];
         L = plan.split_len[sq];
         ub = plan.unit_base[sq];
+        ntok = plan.ntok[sq];
         key_off = plan.key_off[sq];
     }
     const int split = unit - ub;
@@ -617,53 +643,89 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R =
     const int kend = min(len, kbeg + L);
     const int b = plan.seq0 + sq;
     const int ncols = T_q * G;
-    const int pos0 = len - T_q;                    // position of new token 0
+    // walk index <-> position: [0, s_end) are positions 0.., then w_lo.. (ring);
+    // a packed cache is the identity (s_end = w_lo = 0)
+    int s_end = 0, w_lo = 0, pos0 = len - T_q;    // pos0: position of new token 0
+    RowMap rmap{0, 0, 0, 1};
+    if (RING) {
+        pos0 = ntok - T_q;
+        s_end = min(ring.sink, ntok);
+        w_lo = max(s_end, pos0 - ring.window + 1);
+        const int wrap = ring.capacity - ring.sink;
+        rmap = RowMap{s_end, ring.sink, w_lo >= ring.sink ? (w_lo - ring.sink) % wrap : 0, wrap};
+    }
 
-    // Q^T operand (column = query row): loaded first, so that the wait for the
-    // first tile covers it
+    // Q^T operand (column = query row)
     const int fc = min(col, ncols - 1);            // columns past the end read a valid row
     const int tq = fc / G;
     const int hq = kv * G + fc % G;
-    const int vis_end = min(kend, pos0 + tq + 1);
-    bf16x8 qf[KSTEPS];
-    {
-        const uint16_t* qrow = q + (((int64_t)b * T_q + tq) * H_q + hq) * D + g4 * 8;
-#pragma unroll
-        for (int st = 0; st < KSTEPS; ++st)
-            qf[st] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + st * 32));
+    const int pos = pos0 + tq;
+    int vis_end, wbeg = 0;
+    if (RING) {
+        vis_end = min(kend, pos < s_end ? pos + 1 : s_end + (pos - w_lo + 1));
+        wbeg = s_end + max(0, pos - ring.window + 1 - w_lo);
+    } else {
+        vis_end = min(kend, pos + 1);
     }
+    // Q rows of the 16 columns go into the wave's own Q area first (row c =
+    // column c, chunks swizzled as the K rows), so that the wait for the
+    // first tile covers them
+    uint16_t* qw = qlds + wave * kCols * D;
+    {
+        // based at the KV head's first query head of token 0; T_q * H_q * d * 2
+        // bytes stay far below 2^31 (T_q <= 256)
+        const i32x4 rs = buffer_rsrc(q + ((int64_t)b * T_q * H_q + (int64_t)kv * G) * D, 0x7ffffff0);
+#pragma unroll
+        for (int j = 0; j < kCols / ROWS_PER_LOAD; ++j) {
+            const int r = j * ROWS_PER_LOAD + lane / CPR;           // column
+            const int rc = min(r, ncols - 1);
+            const int cc = (lane % CPR) ^ stream_swz<D>(r);
+            dma16(rs, lds_addr(qw + j * ROWS_PER_LOAD * D),
+                  (((rc / G) * H_q + rc % G) * D + cc * 8) * 2);
+        }
+    }
+    bf16x8 qf[KSTEPS];                             // read once its loads have landed
+    // walk indices before mask_from are visible to all tokens (apart from the
+    // ring window starts, all below wbeg_max)
+    const int mask_from = RING ? min(kend, pos0 < s_end ? pos0 + 1 : s_end + (pos0 - w_lo + 1))
+                               : min(kend, pos0 + 1);
+    const int wbeg_max = RING ? s_end + max(0, pos0 + T_q - 1 - ring.window + 1 - w_lo) : 0;
 
-    // the wave's tiles: tile w, w + 4, ... of the split (at most R of them);
-    // every slot is requested, keys past the split end clamp to its last key
     const int64_t row_elems = (int64_t)H_kv * D;
     const uint16_t* kseq = k + key_off * row_elems + (int64_t)kv * D;
     const uint16_t* vseq = v + key_off * row_elems + (int64_t)kv * D;
     auto wslot = [&](int sl) { return (sl == 0 ? slot0 : slot1) + wave * SM::SLOT_ELEMS; };
     const int n_tiles = (kend - kbeg + kTile - 1) / kTile;
-#pragma unroll
-    for (int sl = 0; sl < R; ++sl) {
-        const int key0 = kbeg + (wave + kWaves * sl) * kTile;
-        // keys of this tile inside the split: rows past them re-read the last key
+    const int n_w = n_tiles > wave ? (n_tiles - wave + kWaves - 1) / kWaves : 0;   // this wave's tiles
+
+    // DMA of the wave's tile i into slot sl; rows past the split end re-read
+    // its last key
+    auto issue = [&](int i, int sl) __attribute__((always_inline)) {
+        const int key0 = kbeg + (wave + kWaves * i) * kTile;
         const int last = kend - 1;
+        const int kfirst = RING ? 0 : min(key0, last);
+        const int range = 0x7ffffff0;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const uint16_t* src = h == 0 ? kseq : vseq;
             uint16_t* dst = wslot(sl) + h * SM::TILE_ELEMS;
-            const int kfirst = min(key0, last);
-            __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                (void*)(src + (int64_t)kfirst * row_elems), (short)0,
-                (int)(kTile * row_elems * 2), 0x00020000);
+            // packed: based at the tile's first row; ring: at the sequence's
+            // first slot (the host keeps capacity * row bytes below 2^31)
+            const i32x4 rs = buffer_rsrc(src + (int64_t)kfirst * row_elems, range);
 #pragma unroll
-            for (int i = 0; i < LOADS; ++i) {
-                const int r = i * ROWS_PER_LOAD + lane / CPR;
-                const int cc = (lane % CPR) ^ short_swz<D>(r);
+            for (int j = 0; j < LOADS; ++j) {
+                const int r = j * ROWS_PER_LOAD + lane / CPR;
+                const int cc = (lane % CPR) ^ stream_swz<D>(r);
                 const int key = min(key0 + r, last);
-                const int off = (int)(((int64_t)(key - kfirst) * row_elems + cc * 8) * 2);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + i * ROWS_PER_LOAD * D),
-                                                         16, off, 0, 0, 2);
+                const int row = RING ? rmap(key) : key - kfirst;
+                const int off = (int)(((int64_t)row * row_elems + cc * 8) * 2);
+                dma16(rs, lds_addr(dst + j * ROWS_PER_LOAD * D), off);
             }
         }
-    }
+    };
+#pragma unroll
+    for (int sl = 0; sl < R; ++sl)
+        if (sl < n_w) issue(sl, sl);
 
     // per-lane LDS read offsets (elements within a tile)
     int koff[2][KSTEPS];
@@ -671,7 +733,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R =
     for (int blk = 0; blk < 2; ++blk) {
         const int r = tile_key(col, blk);
 #pragma unroll
-        for (int st = 0; st < KSTEPS; ++st) koff[blk][st] = r * D + (((st * 4 + g4) ^ short_swz<D>(r)) << 3);
+        for (int st = 0; st < KSTEPS; ++st) koff[blk][st] = r * D + (((st * 4 + g4) ^ stream_swz<D>(r)) << 3);
     }
     // V^T: lane L of group g4 reads key row g4 + 4 (L / 4) (+ 16), dims 4 (L % 4) of each 16-dim block
     int voff[2][DBLK];
@@ -681,24 +743,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R =
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) {
             const int x = db * 16 + 4 * (lane & 3);
-            voff[hi][db] = r * D + (((x >> 3) ^ short_swz<D>(r)) << 3) + (x & 7);
+            voff[hi][db] = r * D + (((x >> 3) ^ stream_swz<D>(r)) << 3) + (x & 7);
         }
     }
 
     f32x4 oacc[DBLK];
 #pragma unroll
-    for (int i = 0; i < DBLK; ++i) oacc[i] = f32x4{};
+    for (int j = 0; j < DBLK; ++j) oacc[j] = f32x4{};
     float m_run = -INFINITY, l_run = 0.f;
-    const int mask_from = min(kend, pos0 + 1);     // keys before it are visible to every token
 
-#pragma unroll
-    for (int sl = 0; sl < R; ++sl) {
-        // this slot's DMA writes (and Q's load) have landed: R - 1 - sl slots behind it
-        if (sl == R - 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * LOADS) : "memory");
-        const int tile = wave + kWaves * sl;
-        if (tile >= n_tiles) break;                // wave-uniform
-        const int key0 = kbeg + tile * kTile;
+    // one tile from slot sl: S^T = K Q^T, mask, online softmax, O += P V
+    auto process = [&](int i, int sl) __attribute__((always_inline)) {
+        const int key0 = kbeg + (wave + kWaves * i) * kTile;
         const uint16_t* kt = wslot(sl);
         const uint16_t* vt = kt + SM::TILE_ELEMS;
         f32x4 s[2];
@@ -711,12 +767,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R =
                 s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[st], s[blk], 0, 0, 0);
             }
         }
-        if (key0 + kTile > mask_from) {
+        if (key0 + kTile > mask_from || (RING && key0 + kTile > s_end && key0 < wbeg_max)) {
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (key0 + g4 + 16 * blk + 4 * i >= vis_end) s[blk][i] = -INFINITY;
+                for (int e = 0; e < 4; ++e) {
+                    const int key = key0 + g4 + 16 * blk + 4 * e;
+                    bool hide = key >= vis_end;
+                    if (RING) hide = hide || (key >= s_end && key < wbeg);
+                    if (hide) s[blk][e] = -INFINITY;
+                }
         }
         float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                          fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
@@ -725,8 +785,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R =
         // Lazy rescale: the reference max moves only when a column's tile max
         // exceeds it by more than 2^8 in the exponentials (then O and l are
         // rescaled); otherwise P <= 2^8 against the old reference, which the
-        // fp32 sums carry exactly as well.  The first tile sets it.
-        if (sl == 0) {
+        // fp32 sums carry exactly as well.  The wave's first tile sets it.
+        if (i == 0) {
             m_run = mt;
         } else if (__builtin_amdgcn_ballot_w64(mt * c > m_run * c + 8.f) != 0) {
             const float m_new = fmaxf(m_run, mt);
@@ -741,7 +801,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R =
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) p[blk * 4 + i] = fast_exp2(__builtin_fmaf(s[blk][i], c, -mc));
+            for (int e = 0; e < 4; ++e) p[blk * 4 + e] = fast_exp2(__builtin_fmaf(s[blk][e], c, -mc));
         l_run += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                           pack_bf16x2(p[6], p[7])};
@@ -754,6 +814,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R =
             oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a8), pb,
                                                               oacc[db], 0, 0, 0);
         }
+    };
+
+    // Q from the wave's Q area (its loads are older than every tile's)
+    if (R == 2 && n_w >= 2) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * LPT) : "memory");
+    else if (n_w >= 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LPT) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int st = 0; st < KSTEPS; ++st)
+        qf[st] = *(const bf16x8*)(qw + col * D + (((st * 4 + g4) ^ stream_swz<D>(col)) << 3));
+
+    // Tile j sits in slot j mod R; when it is processed the loads in flight
+    // are those of the wave's tiles j .. min(j + R, n_w) - 1, oldest first, so
+    // the wait leaves the later tiles' loads outstanding.
+    for (int i = 0; i < n_w; i += R) {
+#pragma unroll
+        for (int sl = 0; sl < R; ++sl) {
+            const int j = i + sl;
+            if (j >= n_w) break;                   // wave-uniform
+            if (R == 2 && j + 1 < n_w) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LPT) : "memory");
+            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            process(j, sl);
+            if (j + R < n_w) {
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the slot's LDS reads are done
+                issue(j + R, sl);
+            }
+        }
     }
 
     // ---- merge the four wave partials ----
@@ -763,8 +849,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R =
     float lr = l_run;
     lr += xor16(lr);
     lr += xor32(lr);
-    // no DMA write into this wave's slots may still be pending (a wave with
-    // fewer than R tiles skipped the last wait)
+    // no DMA write into this wave's slots may still be pending
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     // wave area: O [16][CS] (columns padded by 4 floats against bank
     // conflicts), then l [16], then m [16]
@@ -1144,11 +1229,15 @@ int64_t decode_workgroups_per_split(DecodeKind kind, int T_q, int G, int H_kv, i
         n_hg = (((int64_t)T_q * G + kCols - 1) / kCols + nh - 1) / nh;
         pairs = kind == DecodeKind::Bf16 || kind == DecodeKind::Ring;
     }
-    const int hp = (pairs && H_kv % 2 == 0 && split_len >= kPairMinSplitLen) ? 2 : 1;
-    // a short-split work-group with two tiles per wave holds the LDS of two
-    // (decode_short_kernel), so it counts twice against the resident slots
-    const int occ = (kind == DecodeKind::Bf16 && T_q * G <= kCols && hp == 1 &&
-                     split_len > kShortMaxKeys / 2 && split_len <= kShortMaxKeys) ? 2 : 1;
+    int hp = (pairs && H_kv % 2 == 0 && split_len >= kPairMinSplitLen) ? 2 : 1;
+    // bf16 caches with one column block stream K/V into LDS one KV head per
+    // work-group (decode_stream_kernel); with two slots per wave a
+    // work-group holds the LDS of two, so it counts twice
+    int occ = 1;
+    if ((kind == DecodeKind::Bf16 || kind == DecodeKind::Ring) && T_q * G <= kCols) {
+        hp = 1;
+        occ = split_len > kStreamOneSlotKeys ? 2 : 1;
+    }
     return n_hg * (H_kv / hp) * occ;
 }
 
@@ -1217,32 +1306,27 @@ static hipError_t split_dispatch(const void* q, const void* k, const void* v,
     const int hp = (KVF == kKvBf16 && H_kv % 2 == 0 && min_len >= kPairMinSplitLen) ? 2 : 1;
     const float c = scale * kLog2e;
     const int64_t uh = (int64_t)plan.units * n_hg;
-    if (KVF == kKvBf16 && !RING && T_q * G <= kCols && hp == 1) {
-        // short splits: every tile of a wave requested at once (see decode_short_kernel)
+    if (KVF == kKvBf16 && T_q * G <= kCols &&
+        (!RING || (int64_t)ring.capacity * H_kv * d * 2 < 0x7fff0000)) {
+        // one KV head per work-group, K/V streamed into LDS (decode_stream_kernel)
         int max_len = 0;
         for (int i = 0; i < plan.nseq; ++i)
             max_len = std::max(max_len, std::min((int)plan.split_len[i], (int)plan.len[i]));
-        if (max_len <= kShortMaxKeys) {
-            const dim3 sgrid((unsigned)(plan.units * H_kv));
-            const bool two = max_len > kShortMaxKeys / 2;
-            if (d == 128 && two)
-                hipLaunchKernelGGL((decode_short_kernel<128, 2>), sgrid, dim3(kThreads), 0, stream,
-                                   (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                                   ws.m, ws.l, ws.o, plan, T_q, H_q, H_kv, G, c);
-            else if (d == 128)
-                hipLaunchKernelGGL((decode_short_kernel<128, 1>), sgrid, dim3(kThreads), 0, stream,
-                                   (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                                   ws.m, ws.l, ws.o, plan, T_q, H_q, H_kv, G, c);
-            else if (two)
-                hipLaunchKernelGGL((decode_short_kernel<64, 2>), sgrid, dim3(kThreads), 0, stream,
-                                   (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                                   ws.m, ws.l, ws.o, plan, T_q, H_q, H_kv, G, c);
-            else
-                hipLaunchKernelGGL((decode_short_kernel<64, 1>), sgrid, dim3(kThreads), 0, stream,
-                                   (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                                   ws.m, ws.l, ws.o, plan, T_q, H_q, H_kv, G, c);
-            return hipGetLastError();
+        const dim3 sgrid((unsigned)(plan.units * H_kv));
+        const bool two = max_len > kStreamOneSlotKeys;
+        auto go = [&](auto kernel) {
+            hipLaunchKernelGGL(kernel, sgrid, dim3(kThreads), 0, stream, (const uint16_t*)q,
+                               (const uint16_t*)k, (const uint16_t*)v, ws.m, ws.l, ws.o, plan, T_q,
+                               H_q, H_kv, G, c, ring);
+        };
+        if (d == 128) {
+            if (two) go(decode_stream_kernel<128, 2, RING>);
+            else go(decode_stream_kernel<128, 1, RING>);
+        } else {
+            if (two) go(decode_stream_kernel<64, 2, RING>);
+            else go(decode_stream_kernel<64, 1, RING>);
         }
+        return hipGetLastError();
     }
     if (d == 128 && nh == 1)
         launch_split<128, 1, RING, KVF>(hp, uh, q, k, v, ws, plan, T_q, H_q, H_kv, G, n_hg, c, ring, sc, stream);

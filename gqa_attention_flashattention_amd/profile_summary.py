@@ -57,7 +57,7 @@ FLOPS_PER_MOP = 512
 # kernel short name -> source file whose hash guards its traffic record
 KERNEL_SOURCES = {
     "decode_split_kernel": "csrc/decode.hip",
-    "decode_short_kernel": "csrc/decode.hip",
+    "decode_stream_kernel": "csrc/decode.hip",
     "decode_wide_kernel": "csrc/decode.hip",
     "decode_combine_kernel": "csrc/decode.hip",
     "prefill_bf16_kernel": "csrc/prefill_bf16.hip",

@@ -219,11 +219,13 @@ int gqa_attn_decode_noalloc(const void *q, const void *k, const void *v, void *o
  *                    256 (beyond) that minimises
  *                    ceil(W / R) * (L + 256) summed over the launches of 64
  *                    sequences, plus 8 * max_b n_b, W being the split
- *                    work-groups of a launch (a bf16 split of 129 to 256
- *                    keys with G <= 16 counts twice: its work-group holds
- *                    the LDS of two) and R the number resident at
- *                    once (two per compute unit); otherwise W is about four
- *                    per compute unit.  A positive integer in the
+ *                    work-groups of a launch and R the number resident at
+ *                    once (two per compute unit).  A bf16 or ring cache
+ *                    with at most 16 query rows per KV head (G * T_q <= 16)
+ *                    takes one work-group per (split, KV head), which counts
+ *                    twice above 128 keys (it holds the LDS of two); other
+ *                    cases pair KV heads from 512 keys on.  Otherwise W is
+ *                    about four per compute unit.  A positive integer in the
  *                    environment variable GQA_ATTN_SPLIT_LEN (read once per
  *                    process) replaces the automatic L for every decode entry
  *                    point (a tuning and measurement override).  The plan

@@ -284,18 +284,15 @@ def _documented_auto_len(kv_len, H_kv, cus=256):
     (multiples of 64 up to 1024, of 128 up to 2048, of 256 beyond)
     minimising ceil(W / R) * (L + 256) summed over launches of 64 sequences
     plus 8 x the largest split count of a sequence,
-    W = split work-groups (H_kv / 2 per split from 512 keys on, else H_kv;
-    those of 129-256 keys count twice), R = 2 per compute unit; ties to the
-    longer L."""
+    W = split work-groups (H_kv per split, each counting twice above 128
+    keys), R = 2 per compute unit; ties to the longer L."""
     slots = 2 * cus
     hi = min(8192, max(128, -(-max(kv_len) // 64) * 64))
     best, best_cost = None, None
     cands = [L for L in range(128, hi + 1, 64)
              if L <= 1024 or (L <= 2048 and L % 128 == 0) or L % 256 == 0]
     for L in cands:
-        per = H_kv // 2 if (H_kv % 2 == 0 and L >= 512) else H_kv
-        if 128 < L <= 256:
-            per *= 2
+        per = H_kv * (2 if L > 128 else 1)
         cost = 0
         for b0 in range(0, len(kv_len), 64):
             n = sum(-(-x // L) for x in kv_len[b0:b0 + 64])
@@ -317,18 +314,19 @@ def test_auto_plan_follows_the_documented_rule(seed, B):
 
 
 def test_auto_plan_on_the_benchmark_batches():
-    """One full round of resident work-groups where that is cheapest: the
-    16-sequence ragged batch takes 127 splits of 2304 keys (508 work-groups,
-    two KV heads each), decode_8k 32 splits of 256 keys (256: half the
-    partials of 64 splits for the same round)."""
+    """Whole rounds of resident work-groups where that is cheapest: the
+    16-sequence ragged batch takes 64 splits of 4864 keys (512 work-groups of
+    one KV head, two rounds of one per compute unit), decode_8k 32 splits of
+    256 keys (256 work-groups: one round), the 128k sequence 32 splits of
+    4096 (one round)."""
     from gqa_attention_flashattention_amd import inputs as gin
     kv_len = gin.kv_lengths(gin.WORKLOADS["decode_varlen_b16"], np.random.default_rng(0))
     p = gq.decode_plan(16, 64, 8, 128, kv_len)
-    assert (p["split_len"], p["total_splits"]) == (2304, 127)
+    assert (p["split_len"], p["total_splits"]) == (4864, 64)
     p = gq.decode_plan(1, 64, 8, 128, [8192])
     assert (p["split_len"], p["total_splits"]) == (256, 32)
     p = gq.decode_plan(1, 64, 8, 128, [131072])
-    assert (p["split_len"], p["total_splits"]) == (1024, 128)
+    assert (p["split_len"], p["total_splits"]) == (4096, 32)
 
 
 def _documented_kvsplit_count(B, T_q, S_kv, H_q, H_kv, causal, q_offset, cus=256):
