@@ -309,7 +309,13 @@ int gqa_attn_decode_multi(const void *q, const void *k, const void *v, void *o, 
  *   q, o [B, T_q, H_q, d] bf16; lse [B, T_q, H_q] fp32, may be NULL.
  * T_q new tokens per sequence with the causal rule of gqa_attn_decode_multi
  * (T_q = 1: plain decode).  The result is attention over the dequantised
- * K and V; fp32 accumulation as gqa_attn_decode.  Library-owned workspace.
+ * K and V; fp32 accumulation as gqa_attn_decode.  Scale precision: each
+ * k_scale multiplies the query in fp32 and enters the MFMA as a bf16 high
+ * plus low pair (about 16 significant bits); v_scale multiplies the fp32
+ * partial output exactly.  Scales are arbitrary finite fp32 values; parity
+ * against the fp64 oracle is tested both with bf16-valued scales (where code
+ * * scale is exact) and with scales that are not bf16 values.
+ * Library-owned workspace.
  * Errors: GQA_ERR_NULL, GQA_ERR_SHAPE, GQA_ERR_UNSUPPORTED (kv_bits, d),
  * GQA_ERR_RANGE, GQA_ERR_HIP.
  */

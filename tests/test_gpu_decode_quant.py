@@ -128,3 +128,30 @@ def test_quant_many_sequences_two_launches():
     og, lg = _gpu(inp)
     oref, lref = _oracle(inp)
     assert_close(og, oref, lg, lref, name="int4 B=70")
+
+
+def _full_fp32_scales(inp, seed):
+    """Replace the bf16-representable scales with fp32 values that use low
+    mantissa bits (none of them is a bf16 value): the generator's scales are
+    bf16 values so that code * scale is exact, which leaves any other scale
+    untested without this case."""
+    rng = np.random.default_rng(seed)
+    for name in ("k_scale", "v_scale"):
+        s = getattr(inp, name).astype(np.float64)
+        s = (s * (1.0 + rng.uniform(2.0**-8, 2.0**-7, size=s.shape))).astype(np.float32)
+        assert not np.any(gin.bf16_bits_to_f32(gin.bf16_round_bits(s)) == s)
+        setattr(inp, name, s)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("T_q,kv_len", [(1, [1, 40, 2000]), (4, [9, 700])])
+def test_quant_fp32_scales(bits, T_q, kv_len):
+    """Scales that bf16 cannot hold: K's is folded into Q as a bf16 high and
+    low pair and V's multiplies the fp32 partial, so both stay within the
+    bf16 parity gate of the fp64 oracle on the exact fp32 scales."""
+    inp = gin.quant_case(B=len(kv_len), H_q=64, H_kv=8, d=128, kv_len=kv_len, kv_bits=bits,
+                         T_q=T_q, seed=500 + bits + T_q)
+    _full_fp32_scales(inp, 501 + bits)
+    og, lg = _gpu(inp)
+    oref, lref = _oracle(inp)
+    assert_close(og, oref, lg, lref, name=f"int{bits} fp32 scales T_q={T_q}")
