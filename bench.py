@@ -244,9 +244,17 @@ def bench_decode_multi(name, steps, warmup):
         call(i)()
     torch.cuda.synchronize()
     ms = time_graph([call(i) for i in range(steps)])
-    return dict(inp=inp, kv_bytes=kv_bytes, ms=ms, n_copies=n_copies,
-                o_gpu=out.float().cpu().numpy().astype(np.float64),
-                lse_gpu=lse.cpu().numpy().astype(np.float64))
+    # score/value flops of the visible (token, key) pairs: token t of a
+    # sequence of n keys sees n - T_q + t + 1 keys
+    pairs = sum(w.T_q * (n - w.T_q) + w.T_q * (w.T_q + 1) // 2
+                for n in np.asarray(inp.kv_len, np.int64).tolist())
+    flops = 4.0 * w.d * w.H_q * pairs
+    res = dict(inp=inp, kv_bytes=kv_bytes, flops=flops, ms=ms, n_copies=n_copies,
+               o_gpu=out.float().cpu().numpy().astype(np.float64),
+               lse_gpu=lse.cpu().numpy().astype(np.float64))
+    del ks, vs, k0, v0
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_prefill(name, steps, warmup):
@@ -576,22 +584,24 @@ def parity_prefill_rows(pre, o_sample, lse_sample, tag):
             f"{tag}_sample_rows": int(np.union1d(pre["rows"], pre["wg_rows"]).size)}
 
 
-def parity_decode_multi(mul, n_seq=2):
-    """Oracle check of the first n_seq sequences of the multi-token decode
-    result (every row of those sequences)."""
+def parity_decode_multi(mul, seqs=(0, 1), tag="decode_multi"):
+    """Oracle check of sequences `seqs` of a multi-token decode result (every
+    row of those sequences)."""
     import oracle
     inp = mul["inp"]
     w = inp.workload
     errs_o, errs_l = [], []
-    off = 0
-    for b, n in enumerate(np.asarray(inp.kv_len).tolist()[:n_seq]):
-        o, l = oracle.prefill(inp.q[b:b + 1], inp.k[None, off:off + n], inp.v[None, off:off + n],
+    kv_len = np.asarray(inp.kv_len, np.int64)
+    off = np.concatenate([[0], np.cumsum(kv_len)])
+    for b in seqs:
+        n = int(kv_len[b])
+        kb, ke = int(off[b]), int(off[b + 1])
+        o, l = oracle.prefill(inp.q[b:b + 1], inp.k[None, kb:ke], inp.v[None, kb:ke],
                               causal=True, q_offset=n - w.T_q)
         errs_o.append(np.abs(mul["o_gpu"][b] - o[0]).max())
         errs_l.append(np.abs(mul["lse_gpu"][b] - l[0]).max())
-        off += n
-    return {"decode_multi_sample_max_abs_dO": float(max(errs_o)),
-            "decode_multi_sample_max_abs_dLSE": float(max(errs_l))}
+    return {f"{tag}_sample_max_abs_dO": float(max(errs_o)),
+            f"{tag}_sample_max_abs_dLSE": float(max(errs_l))}
 
 
 def parity_prefill_kvsplit(kvs, n_rows=64):
@@ -718,6 +728,9 @@ def main():
                     help="quantised-cache decode workloads (reported under decode_quant)")
     ap.add_argument("--multi-workload", default="decode_t4_varlen_b16",
                     help="multi-token decode workload (reported under decode_multi)")
+    ap.add_argument("--multi-wide-workloads", default="decode_t16_varlen_b16,decode_t32_varlen_b16",
+                    help="multi-token decode workloads with 128 / 256 query rows per KV head "
+                         "(reported under decode_multi_wide)")
     ap.add_argument("--ring-quant-workload", default="decode_ring_int4_b16",
                     help="quantised ring-buffer decode workload (reported under decode_ring_quant)")
     ap.add_argument("--scale-workloads", default="decode_varlen_b16,decode_128k",
@@ -755,9 +768,11 @@ def main():
                                                        S=args.gqa_keys)}), flush=True)
         return
     if args.only == "decode_multi":
-        mul = bench_decode_multi(args.multi_workload, min(args.steps, 200), args.warmup)
-        log(f"[bench] decode_multi {mul['ms'] * 1e3:.2f} us/call "
-            f"{mul['kv_bytes'] / (mul['ms'] * 1e-3) / 1e9:.1f} GB/s")
+        for name in [args.multi_workload] + args.multi_wide_workloads.split(","):
+            mul = bench_decode_multi(name, min(args.steps, 200), args.warmup)
+            log(f"[bench] decode_multi {name} {mul['ms'] * 1e3:.2f} us/call "
+                f"{mul['kv_bytes'] / (mul['ms'] * 1e-3) / 1e9:.1f} GB/s "
+                f"{mul['flops'] / (mul['ms'] * 1e-3) / 1e12:.1f} TFLOP/s")
         return
     if args.only == "prefill_window":
         pw_ = bench_prefill_window(args.window_workload, args.prefill_steps)
@@ -809,6 +824,11 @@ def main():
     log(f"[bench] decode_multi {args.multi_workload}")
     mul = bench_decode_multi(args.multi_workload, min(args.steps, 200), args.warmup)
     log(f"[bench] decode_multi {mul['ms'] * 1e3:.2f} us/call")
+    mulw = []
+    for name in [n for n in args.multi_wide_workloads.split(",") if n]:
+        log(f"[bench] decode_multi_wide {name}")
+        mulw.append(bench_decode_multi(name, min(args.steps, 100), args.warmup))
+        log(f"[bench] decode_multi_wide {mulw[-1]['ms'] * 1e3:.2f} us/call")
 
     log(f"[bench] prefill_kvsplit {args.kvsplit_workload}")
     kvs = bench_prefill_kvsplit(args.kvsplit_workload, args.prefill_steps)
@@ -919,6 +939,25 @@ def main():
                      "algorithmic_bytes_per_call": mul["kv_bytes"],
                      "note": "whole call (split + combine kernels)"},
     }
+    result["decode_multi_wide"] = []
+    for m in mulw:
+        mw = m["inp"].workload
+        gbs = m["kv_bytes"] / (m["ms"] * 1e-3) / 1e9
+        tfs = m["flops"] / (m["ms"] * 1e-3) / 1e12
+        result["decode_multi_wide"].append({
+            "workload": mw.name, "B": mw.B, "T_q": mw.T_q, "H_q": mw.H_q, "H_kv": mw.H_kv,
+            "d": mw.d, "rows_per_kv_head": mw.T_q * mw.H_q // mw.H_kv,
+            "kv_len_range": list(mw.kv_len_range) if mw.kv_len_range else None,
+            "ms_per_call": m["ms"], "value": round(gbs, 2), "unit": "GB/s",
+            "TFLOPs": round(tfs, 2), "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_call": m["kv_bytes"],
+                         "algorithmic_flops_per_call": m["flops"],
+                         "note": "whole call (prefill-loop split kernel + combine); at 256 "
+                                 "rows per KV head the bf16 MFMA work per byte is near the "
+                                 "ridge, so mfma_frac is given beside the HBM fraction"},
+        })
     kw = kvs["inp"].workload
     tf_split = kvs["flops"] / (kvs["ms"] * 1e-3) / 1e12
     result["prefill_kvsplit"] = {
@@ -1040,6 +1079,12 @@ def main():
         result["parity"].update(parity_decode_ring_quant(dringq))
         log("[bench] oracle check (decode_multi sample)")
         result["parity"].update(parity_decode_multi(mul))
+        for m in mulw:
+            log(f"[bench] oracle check ({m['inp'].workload.name} sample)")
+            # the shortest sequence of the batch, every row
+            b = int(np.argmin(np.asarray(m["inp"].kv_len)))
+            result["parity"].update(parity_decode_multi(m, seqs=(b,),
+                                                        tag=m["inp"].workload.name))
     print(json.dumps(result), flush=True)
 
 

@@ -972,6 +972,69 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
         lse[(int64_t)b * R + r] = (m + fast_log2(l)) * kLn2;
 }
 
+// Row-per-wave variant for launches of many rows with few splits each
+// (multi-token decode: T_q * H_q rows per sequence): each wave merges one
+// whole row.  Its lanes form SG = 256 / D split groups of D / 4 lanes, lane
+// (sg, dq) owning dims 4 dq .. 4 dq + 3 and splits sg, sg + SG, ...; the
+// groups then merge with a fixed butterfly as above (same merge order for
+// every NB).  Four waves (four rows) per work-group.
+constexpr int kCombineRowWaves = 4;
+// launches with at least this many (sequence, row) pairs and at most four
+// splits per lane group take the row-per-wave kernel
+constexpr int64_t kCombineRowsMin = 4096;
+
+template <int D, int NB>
+__global__ __launch_bounds__(64 * kCombineRowWaves) void decode_combine_rows_kernel(
+    const float* __restrict__ ws_m, const float* __restrict__ ws_l,
+    const float* __restrict__ ws_o, uint16_t* __restrict__ o, float* __restrict__ lse,
+    const DecodePlanChunk plan, int T_q, int H_q) {
+    constexpr int LPG = D / 4;          // lanes per split group
+    constexpr int SG = 64 / LPG;        // split groups per wave
+    const int R = T_q * H_q;            // rows per sequence
+    const int lane = threadIdx.x & 63;
+    const int sh = blockIdx.x * kCombineRowWaves + (threadIdx.x >> 6);   // (sequence, row)
+    if (sh >= plan.nseq * R) return;    // whole wave
+    const int sq = sh / R, r = sh % R;  // r = t * H_q + h
+    const int n = plan.unit_base[sq + 1] - plan.unit_base[sq];
+    const int64_t p0 = (int64_t)plan.split_base + plan.unit_base[sq];
+    const int sg = lane / LPG, dim = (lane % LPG) * 4;
+    float m = -INFINITY, l = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = sg; s0 < n; s0 += SG * NB) {
+        float mv[NB], lv[NB];
+        f32x4 ov[NB];
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int s = s0 + SG * u;
+            const int64_t hrow = (p0 + (s < n ? s : 0)) * R + r;
+            mv[u] = s < n ? ws_m[hrow] : -INFINITY;
+            lv[u] = s < n ? ws_l[hrow] : 0.f;
+            ov[u] = *(const f32x4*)(ws_o + hrow * D + dim);
+            if (s >= n) ov[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < NB; ++u) merge_lse(m, l, acc, mv[u], lv[u], ov[u]);
+    }
+#pragma unroll
+    for (int step = (SG == 2 ? 1 : 0); step < 2; ++step) {   // partners l ^ 16 (SG 4), l ^ 32
+        auto other = [step](float x) { return step == 0 ? xor16(x) : xor32(x); };
+        const float m2 = other(m);
+        const float l2 = other(l);
+        f32x4 o2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o2[i] = other(acc[i]);
+        merge_lse(m, l, acc, m2, l2, o2);
+    }
+    const float inv = 1.f / l;
+    const int b = plan.seq0 + sq;
+    if (sg == 0) {
+        u32x2 w = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+        *(u32x2*)(o + ((int64_t)b * R + r) * D + dim) = w;
+    }
+    if (lse != nullptr && lane == 0)
+        lse[(int64_t)b * R + r] = (m + fast_log2(l)) * kLn2;
+}
+
 // ---------------------------------------------------------------------------
 // Wide variant for many query rows per KV head (G * T_q > 32, e.g. multi-token
 // decode): the four waves of a work-group split the column blocks instead of
@@ -1210,8 +1273,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
 int decode_column_blocks_per_group(int T_q, int G) { return T_q * G > kCols ? 2 : 1; }
 
-// more than two 16-row column blocks: the wide kernel (bf16, packed cache)
-static bool decode_use_wide(int T_q, int G) { return T_q * G > 2 * kCols; }
+// from kDecodeRowsMin rows: the prefill tile loop (launch_decode_rows_bf16);
+// more than two 16-row column blocks below that: the wide kernel (bf16,
+// packed cache)
+static bool decode_use_rows(int T_q, int G) { return T_q * G >= kDecodeRowsMin; }
+static bool decode_use_wide(int T_q, int G) { return T_q * G > 2 * kCols && !decode_use_rows(T_q, G); }
 static int decode_wide_nhw(int T_q, int G) { return T_q * G > kWideWaves * kCols ? 2 : 1; }
 
 // bf16 splits of at least this many keys take two KV heads per work-group
@@ -1222,6 +1288,10 @@ constexpr int kPairMinSplitLen = 512;
 int64_t decode_workgroups_per_split(DecodeKind kind, int T_q, int G, int H_kv, int split_len) {
     int64_t n_hg;
     bool pairs = false;
+    if (kind == DecodeKind::Bf16 && decode_use_rows(T_q, G)) {
+        // 512 threads and 128 KiB of LDS: one work-group per compute unit
+        return prefill_row_blocks(T_q, G) * H_kv * kDecodeWorkgroupsPerCu;
+    }
     if (kind == DecodeKind::Bf16 && decode_use_wide(T_q, G)) {
         n_hg = decode_column_groups(T_q, G);
     } else {
@@ -1242,6 +1312,7 @@ int64_t decode_workgroups_per_split(DecodeKind kind, int T_q, int G, int H_kv, i
 }
 
 int decode_column_groups(int T_q, int G) {
+    if (decode_use_rows(T_q, G)) return (int)prefill_row_blocks(T_q, G);
     const int blocks = (T_q * G + kCols - 1) / kCols;
     const int per = decode_use_wide(T_q, G) ? kWideWaves * decode_wide_nhw(T_q, G)
                                             : decode_column_blocks_per_group(T_q, G);
@@ -1344,6 +1415,8 @@ hipError_t launch_decode_split_bf16(const void* q, const void* k, const void* v,
                                     int T_q, int H_q, int H_kv, int d, float scale,
                                     hipStream_t stream) {
     const int G = H_q / H_kv;
+    if (decode_use_rows(T_q, G))
+        return launch_decode_rows_bf16(q, k, v, ws, plan, T_q, H_q, H_kv, d, scale, stream);
     if (decode_use_wide(T_q, G)) {
         const float c = scale * kLog2e;
         const bool two = decode_wide_nhw(T_q, G) == 2;
@@ -1398,6 +1471,27 @@ hipError_t launch_decode_combine_bf16(const DecodeWorkspace& ws, const DecodePla
     int max_n = 1;
     for (int i = 0; i < plan.nseq; ++i)
         max_n = std::max(max_n, (int)(plan.unit_base[i + 1] - plan.unit_base[i]));
+    const int64_t rows = (int64_t)plan.nseq * T_q * H_q;
+    const int sg = 256 / d;   // split groups of the row-per-wave kernel
+    if (rows >= kCombineRowsMin && max_n <= 4 * sg) {
+        const int per = (max_n + sg - 1) / sg;
+        const int nb = per <= 1 ? 1 : per <= 2 ? 2 : 4;
+        const dim3 rgrid((unsigned)((rows + kCombineRowWaves - 1) / kCombineRowWaves));
+        auto go = [&](auto kernel) {
+            hipLaunchKernelGGL(kernel, rgrid, dim3(64 * kCombineRowWaves), 0, stream, ws.m, ws.l,
+                               ws.o, (uint16_t*)o, lse, plan, T_q, H_q);
+        };
+        if (d == 128) {
+            if (nb == 1) go(decode_combine_rows_kernel<128, 1>);
+            else if (nb == 2) go(decode_combine_rows_kernel<128, 2>);
+            else go(decode_combine_rows_kernel<128, 4>);
+        } else {
+            if (nb == 1) go(decode_combine_rows_kernel<64, 1>);
+            else if (nb == 2) go(decode_combine_rows_kernel<64, 2>);
+            else go(decode_combine_rows_kernel<64, 4>);
+        }
+        return hipGetLastError();
+    }
     const int per_lane = (max_n + 7) / 8;   // splits of one lane group
     const int nb = per_lane <= 1 ? 1 : per_lane <= 2 ? 2 : per_lane <= 4 ? 4 : 8;
     auto go = [&](auto kernel) {

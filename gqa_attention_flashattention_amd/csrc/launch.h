@@ -101,6 +101,16 @@ hipError_t launch_decode_ring_split(const void* q, const void* k, const void* v,
                                     const DecodeWorkspace& ws, const DecodePlanChunk& plan,
                                     int T_q, int H_q, int H_kv, int d, float scale,
                                     const RingArgs& ring, hipStream_t stream);
+// Multi-token decode with at least kDecodeRowsMin query rows per KV head
+// (T_q * G) over a packed bf16 cache: each (split, row block of 256 rows, KV
+// head) runs the prefill kernel's tile loop (32x32 MFMAs, 64-key tiles) on
+// the split's key range and writes partials like launch_decode_split_bf16.
+constexpr int kDecodeRowsMin = 128;
+hipError_t launch_decode_rows_bf16(const void* q, const void* k, const void* v,
+                                   const DecodeWorkspace& ws, const DecodePlanChunk& plan,
+                                   int T_q, int H_q, int H_kv, int d, float scale,
+                                   hipStream_t stream);
+
 hipError_t launch_decode_combine_bf16(const DecodeWorkspace& ws, const DecodePlanChunk& plan,
                                       void* o, float* lse, int T_q, int H_q, int d,
                                       hipStream_t stream);

@@ -50,6 +50,8 @@
 //    when some row's tile max exceeds it by more than 8 (log2 units), so most
 //    tiles skip the O rescale; exact, since O and l always share the same
 //    reference max and P stays below 2^8.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -164,14 +166,27 @@ struct LaneOffsets {
 // never loaded.
 constexpr int kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2;
 
-template <int D, int MASK, bool SPLIT>
+// PLAN: multi-token decode over a packed varlen cache.  The work-group's key
+// range is one split of a decode plan (sequence sq, keys [kb, kb + L) of
+// plan.len[sq]); the kernel sees that range as its own sequence of S keys
+// with token 0 at position kv_len - T_q - kb (the causal rule of decode with
+// T_q new tokens, shifted to the range), and writes partials as SPLIT does,
+// at the plan's split index.  Blocks: KV head fastest, then row block, then
+// plan unit.
+struct NoPlan {};
+template <bool PLAN>
+using PlanArg = typename std::conditional<PLAN, DecodePlanChunk, NoPlan>::type;
+
+template <int D, int MASK, bool SPLIT, bool PLAN = false>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int B,
     int T_q, int S_kv, int H_q, int H_kv, int G, float c, int q_offset, int n_mblk,
     int n_split, float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
-    int window, int sink) {
+    int window, int sink, const PlanArg<PLAN> plan) {
+    static_assert(!PLAN || (MASK == kMaskCausal && !SPLIT), "plan ranges are causal partials");
     constexpr bool CAUSAL = MASK != kMaskNone;
+    constexpr bool PARTIAL = SPLIT || PLAN;   // writes (m, l, O) partials
     constexpr bool WINDOW = MASK == kMaskWindow;
     using T = Tile<D>;
     constexpr int KSTEPS = D / 16;   // MFMA k-steps over the head dim
@@ -191,14 +206,35 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     int bid = blockIdx.x;
     const int kv = bid % H_kv;
     bid /= H_kv;
-    int split = 0;
-    if (SPLIT) {
-        split = bid % n_split;
-        bid /= n_split;
+    int split = 0, b, mb;
+    int64_t prow;   // partial (split) index of the work-group's rows
+    // K/V row 0 of the keys this work-group walks (their count is S_kv, and
+    // q_offset the position of query token 0 relative to that row)
+    int64_t key_row0;
+    if constexpr (PLAN) {
+        mb = bid % n_mblk;
+        const int unit = bid / n_mblk;
+        int sq = 0;
+        while (sq + 1 < plan.nseq && plan.unit_base[sq + 1] <= unit) ++sq;
+        const int L = plan.split_len[sq];
+        const int len = plan.len[sq];
+        const int kb = (unit - plan.unit_base[sq]) * L;
+        b = plan.seq0 + sq;
+        S_kv = min(L, len - kb);
+        q_offset = len - T_q - kb;
+        key_row0 = plan.key_off[sq] + kb;
+        prow = (int64_t)plan.split_base + unit;
+    } else {
+        if (SPLIT) {
+            split = bid % n_split;
+            bid /= n_split;
+        }
+        b = bid % B;
+        mb = bid / B;
+        if (CAUSAL) mb = n_mblk - 1 - mb;
+        key_row0 = (int64_t)b * S_kv;
+        prow = (int64_t)b * n_split + split;
     }
-    const int b = bid % B;
-    int mb = bid / B;
-    if (CAUSAL) mb = n_mblk - 1 - mb;
 
     const int rows_total = T_q * G;
     const int r0 = mb * kBlockM;
@@ -216,7 +252,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     // (wave- and block-uniform values are pinned to scalar registers so the
     // branches on them are scalar branches)
     const int t_hi = min(T_q - 1, (r0 + kBlockM - 1) / G);
-    const int kend = CAUSAL ? min(S_kv, q_offset + t_hi + 1) : S_kv;
+    // (a plan range can start after every key the block's tokens see)
+    const int kend = CAUSAL ? max(0, min(S_kv, q_offset + t_hi + 1)) : S_kv;
     int wg_tiles = (kend + kBlockN - 1) / kBlockN;
     // window: tiles [0, sink_tiles) then [sink_tiles + gap, ...); the work-group
     // counts tiles in that compacted order (tile index = j + (j >= sink_tiles) * gap)
@@ -258,8 +295,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const int wave_win_all = __builtin_amdgcn_readfirstlane(WINDOW ? q_offset + wt_hi - window + 1 : 0);
 
     const int64_t row_stride = (int64_t)H_kv * D;
-    const uint16_t* kbase = k + ((int64_t)b * S_kv * H_kv + kv) * D;
-    const uint16_t* vbase = v + ((int64_t)b * S_kv * H_kv + kv) * D;
+    const uint16_t* kbase = k + (key_row0 * H_kv + kv) * D;
+    const uint16_t* vbase = v + (key_row0 * H_kv + kv) * D;
 
     // global tile of the work-group's compacted tile index j
     auto tile_of = [&](int j) { return WINDOW ? j + (j >= sink_tiles ? gap : 0) : j; };
@@ -417,7 +454,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         }
         // a window or a split can start past the keys a row sees: its m stays
         // -inf and P = 0
-        const float mc = ((SPLIT || WINDOW) && m_run == -INFINITY) ? 0.f : m_run * c;
+        const float mc = ((PARTIAL || WINDOW) && m_run == -INFINITY) ? 0.f : m_run * c;
         float psum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -534,10 +571,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
                                                    false, false);
         l_run = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     }
-    if (SPLIT) {
+    if (PARTIAL) {
         if (valid) {
-            const int64_t hrow = (((int64_t)b * n_split + split) * T_q + t) * H_q +
-                                 (int64_t)kv * G + g;
+            const int64_t hrow = (prow * T_q + t) * H_q + (int64_t)kv * G + g;
 #pragma unroll
             for (int db = 0; db < DBLK; ++db)
 #pragma unroll
@@ -588,7 +624,7 @@ static hipError_t launch_one(const PrefillArgs& a, int n_split, const DecodeWork
                        (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.T_q, a.S_kv, a.H_q,
                        a.H_kv, a.H_q / a.H_kv, c, a.q_offset, (int)n_mblk, n_split,
                        SPLIT ? ws->m : nullptr, SPLIT ? ws->l : nullptr, SPLIT ? ws->o : nullptr,
-                       a.window, a.sink);
+                       a.window, a.sink, NoPlan{});
     return hipGetLastError();
 }
 
@@ -614,6 +650,26 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
 hipError_t launch_prefill_split_bf16(const PrefillArgs& a, int n_split, const DecodeWorkspace& ws,
                                      hipStream_t stream) {
     return dispatch<true>(a, n_split, &ws, stream);
+}
+
+hipError_t launch_decode_rows_bf16(const void* q, const void* k, const void* v,
+                                   const DecodeWorkspace& ws, const DecodePlanChunk& plan,
+                                   int T_q, int H_q, int H_kv, int d, float scale,
+                                   hipStream_t stream) {
+    const int G = H_q / H_kv;
+    const int64_t n_mblk = prefill_row_blocks(T_q, G);
+    const int64_t grid = (int64_t)plan.units * n_mblk * H_kv;
+    if (grid < 1 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const float c = scale * kLog2e;
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, nullptr,
+                           nullptr, 1, T_q, 0, H_q, H_kv, G, c, 0, (int)n_mblk, 1, ws.m, ws.l,
+                           ws.o, 0, 0, plan);
+    };
+    if (d == 128) go(prefill_bf16_kernel<128, kMaskCausal, false, true>);
+    else go(prefill_bf16_kernel<64, kMaskCausal, false, true>);
+    return hipGetLastError();
 }
 
 }  // namespace gqa

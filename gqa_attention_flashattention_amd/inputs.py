@@ -72,6 +72,10 @@ WORKLOADS = {
                  kv_len_range=(1024, 32768), kv_bits=4),
         Workload("decode_t4_varlen_b16", "decode", "bf16", B=16, H_q=64, H_kv=8, d=128,
                  T_q=4, kv_len_range=(1024, 32768)),
+        Workload("decode_t16_varlen_b16", "decode", "bf16", B=16, H_q=64, H_kv=8, d=128,
+                 T_q=16, kv_len_range=(1024, 32768)),
+        Workload("decode_t32_varlen_b16", "decode", "bf16", B=16, H_q=64, H_kv=8, d=128,
+                 T_q=32, kv_len_range=(1024, 32768)),
         # the pccx base configuration: INT4 KV in an 8192-token hard-cap ring
         Workload("decode_ring_int4_b16", "decode", "bf16", B=16, H_q=64, H_kv=8, d=128,
                  kv_len_range=(1024, 32768), capacity=8192, window=8188, sink=4, kv_bits=4),

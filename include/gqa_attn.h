@@ -223,8 +223,12 @@ int gqa_attn_decode_noalloc(const void *q, const void *k, const void *v, void *o
  *                    once (two per compute unit).  A bf16 or ring cache
  *                    with at most 16 query rows per KV head (G * T_q <= 16)
  *                    takes one work-group per (split, KV head), which counts
- *                    twice above 128 keys (it holds the LDS of two); other
- *                    cases pair KV heads from 512 keys on.  Otherwise W is
+ *                    twice above 128 keys (it holds the LDS of two); a
+ *                    bf16 packed cache with at least 128 query rows per KV
+ *                    head (G * T_q >= 128, gqa_attn_decode_multi) takes one
+ *                    work-group per (split, block of 256 rows, KV head),
+ *                    counted twice; other cases pair KV heads from 512
+ *                    keys on.  Otherwise W is
  *                    about four per compute unit.  A positive integer in the
  *                    environment variable GQA_ATTN_SPLIT_LEN (read once per
  *                    process) replaces the automatic L for every decode entry

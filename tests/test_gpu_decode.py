@@ -150,6 +150,18 @@ def _as_multi(inp):
     return inp
 
 
+def _subset(inp, sel):
+    """The sequences `sel` of a packed decode case (q rows and their K/V rows)."""
+    import dataclasses
+    kv_len = np.asarray(inp.kv_len, np.int64)
+    off = np.concatenate([[0], np.cumsum(kv_len)])
+    k = np.concatenate([inp.k[off[b]:off[b + 1]] for b in sel])
+    v = np.concatenate([inp.v[off[b]:off[b + 1]] for b in sel])
+    return dataclasses.replace(inp, q=inp.q[sel], k=k, v=v, q_store=inp.q_store[sel],
+                               k_store=None, v_store=None,
+                               kv_len=np.asarray(inp.kv_len)[sel])
+
+
 def _oracle_multi(inp):
     """Per sequence: the oracle prefill of its T_q new tokens against its
     cache, causal with the new tokens at the end (q_offset = len - T_q)."""
@@ -218,6 +230,39 @@ def test_decode_multi_split_counts(num_splits):
     og, lg = _decode_multi(inp, num_splits)
     oref, lref = _oracle_multi(inp)
     assert_close(og, oref, lg, lref, name=f"decode_multi splits={num_splits}")
+
+
+@pytest.mark.parametrize("T_q,kv_len,Hq,Hkv,d,num_splits", [
+    (64, [64, 65, 1000], 64, 8, 128, 0),      # 512 rows: two row blocks of 256
+    (16, [1000, 16, 257], 64, 8, 128, 1),     # one split: ranges of any length
+    (16, [1000, 16, 257], 64, 8, 128, 7),     # splits ending inside the causal band
+    (16, [200, 17], 64, 8, 128, 1000),        # one-key splits
+    (43, [43, 44, 600], 12, 4, 128, 0),       # G = 3, 129 rows: one live row in the last wave
+    (7, [7, 300, 1500], 140, 7, 64, 5),       # G = 20, 140 rows, d = 64
+    (128, [128, 129], 16, 8, 128, 3),         # G = 2, 256 rows
+])
+def test_decode_multi_rows_path(T_q, kv_len, Hq, Hkv, d, num_splits):
+    """From 128 query rows per KV head, decode runs the prefill tile loop on
+    each split's key range: row blocks, ranges of any length and start,
+    ranges wholly in the future of some new tokens."""
+    inp = _as_multi(gin.random_case("decode", "bf16", B=len(kv_len), H_q=Hq, H_kv=Hkv, d=d,
+                                    T_q=T_q, kv_len=kv_len, seed=T_q * 77 + sum(kv_len)))
+    og, lg = _decode_multi(inp, num_splits)
+    oref, lref = _oracle_multi(inp)
+    assert_close(og, oref, lg, lref,
+                 name=f"decode_multi rows T_q={T_q} {kv_len} {Hq}/{Hkv} d={d} ns={num_splits}")
+
+
+@pytest.mark.parametrize("name", ["decode_t16_varlen_b16", "decode_t32_varlen_b16"])
+def test_decode_multi_wide_full_size(name):
+    """16 ragged sequences of 1k-32k keys with 16 / 32 new tokens: three whole
+    sequences (first, middle, last) against the oracle."""
+    inp = gin.make(name)
+    og, lg = _decode_multi(inp)
+    sel = [0, 7, 15]
+    sub = _subset(inp, sel)
+    oref, lref = _oracle_multi(sub)
+    assert_close(og[sel], oref, lg[sel], lref, name=name)
 
 
 def test_decode_multi_one_token_matches_decode():
