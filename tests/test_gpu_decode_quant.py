@@ -130,17 +130,24 @@ def test_quant_many_sequences_two_launches():
     assert_close(og, oref, lg, lref, name="int4 B=70")
 
 
+def scales_16bit(scale, rng):
+    """fp32 scales with 16 significant bits that are not bf16 values: a
+    random perturbation kept to the top 16 bits of the significand, with
+    some of bits 8-15 set.  code * scale (at most 8 + 16 bits) is still
+    exact in float32, so the oracle runs on the exact dequantised cache,
+    while a kernel that rounded a scale to bf16 would drop its low part."""
+    s = np.asarray(scale, np.float64) * (1.0 + rng.uniform(2.0**-8, 2.0**-7, size=scale.shape))
+    u = s.astype(np.float32).view(np.uint32) & np.uint32(0xFFFFFF00)
+    u |= np.uint32(0x100)          # bit 8 set: never a bf16 value
+    out = u.view(np.float32)
+    assert not np.any(gin.bf16_bits_to_f32(gin.bf16_round_bits(out)) == out)
+    return out
+
+
 def _full_fp32_scales(inp, seed):
-    """Replace the bf16-representable scales with fp32 values that use low
-    mantissa bits (none of them is a bf16 value): the generator's scales are
-    bf16 values so that code * scale is exact, which leaves any other scale
-    untested without this case."""
     rng = np.random.default_rng(seed)
-    for name in ("k_scale", "v_scale"):
-        s = getattr(inp, name).astype(np.float64)
-        s = (s * (1.0 + rng.uniform(2.0**-8, 2.0**-7, size=s.shape))).astype(np.float32)
-        assert not np.any(gin.bf16_bits_to_f32(gin.bf16_round_bits(s)) == s)
-        setattr(inp, name, s)
+    inp.k_scale = scales_16bit(inp.k_scale, rng)
+    inp.v_scale = scales_16bit(inp.v_scale, rng)
 
 
 @pytest.mark.parametrize("bits", [8, 4])

@@ -14,6 +14,7 @@ import oracle
 from gqa_attention_flashattention_amd import inputs as gin
 
 from gpu_util import assert_close, to_f64, to_gpu
+from test_gpu_decode_quant import scales_16bit
 
 pytestmark = pytest.mark.gpu
 
@@ -140,17 +141,14 @@ def test_ring_quant_deterministic_and_many_sequences():
 
 @pytest.mark.parametrize("bits", [8, 4])
 def test_ring_quant_fp32_scales(bits):
-    """Per-channel scales that are fp32 but not bf16 values against the fp64
-    oracle on those exact scales."""
+    """Per-channel fp32 scales that are not bf16 values (16 significant bits)
+    against the fp64 oracle on those exact scales."""
     rng = np.random.default_rng(90 + bits)
     kv_len = [3, 300, 1000]
     inp = gin.quant_case(B=3, H_q=64, H_kv=8, d=128, kv_len=kv_len, kv_bits=bits, T_q=2,
                          seed=91 + bits, capacity=256)
-    for name in ("k_scale", "v_scale"):
-        s = getattr(inp, name).astype(np.float64)
-        s = (s * (1.0 + rng.uniform(2.0**-8, 2.0**-7, size=s.shape))).astype(np.float32)
-        assert not np.any(gin.bf16_bits_to_f32(gin.bf16_round_bits(s)) == s)
-        setattr(inp, name, s)
+    inp.k_scale = scales_16bit(inp.k_scale, rng)
+    inp.v_scale = scales_16bit(inp.v_scale, rng)
     og, lg = _gpu(inp, 200, 4)
     oref, lref = _oracle(inp, 256, 200, 4)
     assert_close(og, oref, lg, lref, name=f"ring int{bits} fp32 scales")
