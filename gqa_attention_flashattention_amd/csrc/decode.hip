@@ -1290,7 +1290,8 @@ int64_t decode_workgroups_per_split(DecodeKind kind, int T_q, int G, int H_kv, i
     bool pairs = false;
     if (kind == DecodeKind::Bf16 && decode_use_rows(T_q, G)) {
         // 512 threads and 128 KiB of LDS: one work-group per compute unit
-        return prefill_row_blocks(T_q, G) * H_kv * kDecodeWorkgroupsPerCu;
+        return prefill_row_blocks(T_q, G) * (H_kv / decode_rows_heads_per_workgroup(T_q, G, H_kv)) *
+               kDecodeWorkgroupsPerCu;
     }
     if (kind == DecodeKind::Bf16 && decode_use_wide(T_q, G)) {
         n_hg = decode_column_groups(T_q, G);

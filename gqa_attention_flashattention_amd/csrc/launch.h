@@ -106,6 +106,9 @@ hipError_t launch_decode_ring_split(const void* q, const void* k, const void* v,
 // head) runs the prefill kernel's tile loop (32x32 MFMAs, 64-key tiles) on
 // the split's key range and writes partials like launch_decode_split_bf16.
 constexpr int kDecodeRowsMin = 128;
+// KV heads per work-group of that path: two when a head has at most 128 rows
+// (and H_kv is even), so both wave groups of the work-group have rows.
+int decode_rows_heads_per_workgroup(int T_q, int G, int H_kv);
 hipError_t launch_decode_rows_bf16(const void* q, const void* k, const void* v,
                                    const DecodeWorkspace& ws, const DecodePlanChunk& plan,
                                    int T_q, int H_q, int H_kv, int d, float scale,

@@ -96,36 +96,42 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
 
-// Issue this wave's direct-to-LDS loads of one K or V tile `tile` (keys
-// tile*64 ..) into the stage buffer dst.  The buffer resource spans only the
-// tile's rows below S_kv: rows past it read as zeros, their scores are masked
-// to -inf and their P is exactly 0.
-template <int D>
+// Issue this wave's direct-to-LDS loads of one K or V tile `tile` into the
+// stage buffer dst: 64 LDS rows, which are the keys tile*64 .. of one KV head
+// (HP = 1) or the keys tile*32 .. of two neighbouring KV heads, head-major
+// (HP = 2).  The buffer resource spans only the tile's keys below S_kv: rows
+// past it read as zeros, their scores are masked to -inf and their P is
+// exactly 0.
+template <int D, int HP>
 __device__ __forceinline__ void issue_half(uint16_t* dst, const uint16_t* __restrict__ base,
                                            int64_t row_stride, int tile, int S_kv, int wave,
                                            int lane) {
     using T = Tile<D>;
+    constexpr int TK = kBlockN / HP;   // keys per tile
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
         const int row0 = (wave * T::LOADS + i) * T::ROWS_PER_LOAD;
         const int r = row0 + lane / T::CPR;
         const int cc = (lane % T::CPR) ^ swz<D>(r);
-        const int rows = min(kBlockN, S_kv - tile * kBlockN);
+        const int rows = min(TK, S_kv - tile * TK);
         __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(base + (int64_t)tile * kBlockN * row_stride), (short)0,
+            (void*)(base + (int64_t)tile * TK * row_stride), (short)0,
             rows * (int)row_stride * 2, 0x00020000);
-        const int lo = (r * (int)row_stride + cc * 8) * 2;   // bytes
+        // (r < 64: LDS row r is key r of the head, or key r % 32 of head r / 32)
+        const int key = HP == 2 ? r & 31 : r;
+        const int head = HP == 2 ? r >> 5 : 0;
+        const int lo = (key * (int)row_stride + head * D + cc * 8) * 2;   // bytes
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + row0 * D), 16, lo, 0, 0, 0);
     }
 }
-template <int D>
+template <int D, int HP>
 __device__ __forceinline__ void issue_tile(uint16_t* kst, uint16_t* vst,
                                            const uint16_t* __restrict__ kbase,
                                            const uint16_t* __restrict__ vbase,
                                            int64_t row_stride, int tile, int S_kv, int wave,
                                            int lane) {
-    issue_half<D>(kst, kbase, row_stride, tile, S_kv, wave, lane);
-    issue_half<D>(vst, vbase, row_stride, tile, S_kv, wave, lane);
+    issue_half<D, HP>(kst, kbase, row_stride, tile, S_kv, wave, lane);
+    issue_half<D, HP>(vst, vbase, row_stride, tile, S_kv, wave, lane);
 }
 
 // Work-group barrier for LDS traffic only: this wave's LDS operations have
@@ -173,11 +179,17 @@ constexpr int kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2;
 // T_q new tokens, shifted to the range), and writes partials as SPLIT does,
 // at the plan's split index.  Blocks: KV head fastest, then row block, then
 // plan unit.
+//
+// HP = 2 (plan ranges of at most 128 query rows per KV head): a work-group
+// serves two neighbouring KV heads, waves 0-3 the rows of the first and
+// waves 4-7 those of the second, so both wave groups have rows to compute;
+// a tile is then 32 keys of both heads (the same 64 LDS rows), and each
+// group reads its own head's half.
 struct NoPlan {};
 template <bool PLAN>
 using PlanArg = typename std::conditional<PLAN, DecodePlanChunk, NoPlan>::type;
 
-template <int D, int MASK, bool SPLIT, bool PLAN = false>
+template <int D, int MASK, bool SPLIT, bool PLAN = false, int HP = 1>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int B,
@@ -185,6 +197,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     int n_split, float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
     int window, int sink, const PlanArg<PLAN> plan) {
     static_assert(!PLAN || (MASK == kMaskCausal && !SPLIT), "plan ranges are causal partials");
+    static_assert(HP == 1 || (PLAN && HP == 2), "two KV heads per work-group: plan ranges only");
+    constexpr int KB = 2 / HP;           // 32-key blocks of a tile per head
+    constexpr int TK = 32 * KB;          // keys per tile
     constexpr bool CAUSAL = MASK != kMaskNone;
     constexpr bool PARTIAL = SPLIT || PLAN;   // writes (m, l, O) partials
     constexpr bool WINDOW = MASK == kMaskWindow;
@@ -204,8 +219,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const int hh = lane >> 5;
 
     int bid = blockIdx.x;
-    const int kv = bid % H_kv;
-    bid /= H_kv;
+    const int kvg = bid % (H_kv / HP);               // KV head (group) of the work-group
+    bid /= H_kv / HP;
+    const int kv = kvg * HP + (HP == 2 ? wave >> 2 : 0);   // this wave's KV head
     int split = 0, b, mb;
     int64_t prow;   // partial (split) index of the work-group's rows
     // K/V row 0 of the keys this work-group walks (their count is S_kv, and
@@ -238,7 +254,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 
     const int rows_total = T_q * G;
     const int r0 = mb * kBlockM;
-    const int rw0 = r0 + wave * kRowsPerWave;          // first row of this wave
+    // first row of this wave
+    const int rw0 = r0 + (HP == 2 ? wave & 3 : wave) * kRowsPerWave;
     const int row = rw0 + lq;
     const bool valid = row < rows_total;
     // rows past the end read the last row's Q (loads are never predicated);
@@ -251,18 +268,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     // Key range of the work-group and of this wave.
     // (wave- and block-uniform values are pinned to scalar registers so the
     // branches on them are scalar branches)
-    const int t_hi = min(T_q - 1, (r0 + kBlockM - 1) / G);
+    const int t_hi = min(T_q - 1, (r0 + kBlockM / HP - 1) / G);
     // (a plan range can start after every key the block's tokens see)
     const int kend = CAUSAL ? max(0, min(S_kv, q_offset + t_hi + 1)) : S_kv;
-    int wg_tiles = (kend + kBlockN - 1) / kBlockN;
+    int wg_tiles = (kend + TK - 1) / TK;
     // window: tiles [0, sink_tiles) then [sink_tiles + gap, ...); the work-group
     // counts tiles in that compacted order (tile index = j + (j >= sink_tiles) * gap)
     int sink_tiles = 0, gap = 0;
     if (WINDOW) {
         const int t_lo = min(T_q - 1, r0 / G);
         const int p_lo = q_offset + t_lo;
-        sink_tiles = (min(sink, kend) + kBlockN - 1) / kBlockN;
-        const int w_tile0 = max(0, p_lo - window + 1) / kBlockN;
+        sink_tiles = (min(sink, kend) + TK - 1) / TK;
+        const int w_tile0 = max(0, p_lo - window + 1) / TK;
         gap = max(0, w_tile0 - sink_tiles);
         wg_tiles -= gap;
         sink_tiles = __builtin_amdgcn_readfirstlane(sink_tiles);
@@ -295,15 +312,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const int wave_win_all = __builtin_amdgcn_readfirstlane(WINDOW ? q_offset + wt_hi - window + 1 : 0);
 
     const int64_t row_stride = (int64_t)H_kv * D;
-    const uint16_t* kbase = k + (key_row0 * H_kv + kv) * D;
-    const uint16_t* vbase = v + (key_row0 * H_kv + kv) * D;
+    const uint16_t* kbase = k + (key_row0 * H_kv + kvg * HP) * D;
+    const uint16_t* vbase = v + (key_row0 * H_kv + kvg * HP) * D;
 
     // global tile of the work-group's compacted tile index j
     auto tile_of = [&](int j) { return WINDOW ? j + (j >= sink_tiles ? gap : 0) : j; };
     // loads of the work-group's tile j into LDS stage st; the first two tiles
     // start loading before anything else
     auto issue = [&](int j, int st) __attribute__((always_inline)) {
-        issue_tile<D>(ksm + st * T::ELEMS, vsm + st * T::ELEMS, kbase, vbase, row_stride,
+        issue_tile<D, HP>(ksm + st * T::ELEMS, vsm + st * T::ELEMS, kbase, vbase, row_stride,
                       tile_of(j_lo + j), S_kv, wave, lane);
     };
     // Q and O pass through LDS, each wave through its own 32-row area in the
@@ -347,13 +364,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     for (int ks = 0; ks < KSTEPS; ++ks)
         qf[ks] = *(const bf16x8*)(qo_lds + lq * D + (((2 * ks + hh) ^ swz<D>(lq)) << 3));
 
-    // Per-lane LDS read offsets (elements), fixed for the whole sweep.
+    // Per-lane LDS read offsets (elements), fixed for the whole sweep (with
+    // two heads, this wave's head's 32 rows of every tile).
     LaneOffsets<D> off;
     {
+        const int hofs = (HP == 2 ? wave >> 2 : 0) * 32 * D;
         const int kr = swap_bits23(lq);               // + 32 rows for the second key block
         const int kf = swz<D>(kr);
 #pragma unroll
-        for (int kst = 0; kst < KSTEPS; ++kst) off.k[kst] = kr * D + (((2 * kst + hh) ^ kf) << 3);
+        for (int kst = 0; kst < KSTEPS; ++kst)
+            off.k[kst] = hofs + kr * D + (((2 * kst + hh) ^ kf) << 3);
         const int L16 = lane & 15;
         const int dh = (lane >> 4) & 1;
 #pragma unroll
@@ -363,7 +383,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 #pragma unroll
             for (int db = 0; db < DBLK; ++db) {
                 const int col = 32 * db + 16 * dh + 4 * (L16 & 3);
-                off.v[th][db] = vr * D + (((col >> 3) ^ vf) << 3) + (col & 7);
+                off.v[th][db] = hofs + vr * D + (((col >> 3) ^ vf) << 3) + (col & 7);
             }
         }
     }
@@ -375,20 +395,21 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     float l_run = 0.f;
 
     auto needs = [&](int j) __attribute__((always_inline)) {
-        const int key0 = tile_of(j_lo + j) * kBlockN;
+        const int key0 = tile_of(j_lo + j) * TK;
         bool w = key0 < wave_kend;
-        if (WINDOW) w = w && (key0 < sink || key0 + kBlockN > wave_win_any);
+        if (WINDOW) w = w && (key0 < sink || key0 + TK > wave_win_any);
         return w;
     };
-    f32x16 s[2];
-    uint32_t pk[2][8];
+    f32x16 s[KB];
+    uint32_t pk[KB][8];
     // S^T = K Q^T of tile j (stage st); K operands read one group ahead
     auto qk = [&](int j, const uint16_t* kt) __attribute__((always_inline)) {
         if (!needs(j)) return;
-        s[0] = f32x16{};
-        s[1] = f32x16{};
-        constexpr int NQ = 2 * KSTEPS, QG = 4, NG = NQ / QG;
-        auto kread = [&](int n) { return *(const bf16x8*)(kt + (n & 1) * 32 * D + off.k[n >> 1]); };
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
+        // MFMA n: key block n % KB, head-dim step n / KB
+        constexpr int NQ = KB * KSTEPS, QG = 4, NG = NQ / QG;
+        auto kread = [&](int n) { return *(const bf16x8*)(kt + (n % KB) * 32 * D + off.k[n / KB]); };
         bf16x8 ka[2][QG];
 #pragma unroll
         for (int i = 0; i < QG; ++i) ka[0][i] = kread(i);
@@ -403,8 +424,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 #pragma unroll
             for (int i = 0; i < QG; ++i) {
                 const int n = g * QG + i;
-                s[n & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[g & 1][i], qf[n >> 1], s[n & 1],
-                                                                 0, 0, 0);
+                s[n % KB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[g & 1][i], qf[n / KB],
+                                                                   s[n % KB], 0, 0, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -412,13 +433,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     // mask, running max, lazy rescale, P (packed bf16) and its row sum
     auto softmax = [&](int j) __attribute__((always_inline)) {
         if (!needs(j)) return;
-        const int key0 = tile_of(j_lo + j) * kBlockN;
+        const int key0 = tile_of(j_lo + j) * TK;
         // element i of s[kb] is key key0 + 32 kb + 16 (i / 8) + 8 hh + (i % 8)
-        bool need_mask = key0 + kBlockN > wave_full;
-        if (WINDOW) need_mask = need_mask || (key0 + kBlockN > sink && key0 < wave_win_all);
+        bool need_mask = key0 + TK > wave_full;
+        if (WINDOW) need_mask = need_mask || (key0 + TK > sink && key0 < wave_win_all);
         if (need_mask) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int key = key0 + kb * 32 + (i >> 3) * 16 + hh * 8 + (i & 7);
@@ -427,14 +448,22 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
                     if (hide) s[kb][i] = -INFINITY;
                 }
         }
-        float mt0 = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
-        float mt1 = fmaxf(fmaxf(s[1][0], s[1][1]), s[1][2]);
+        float mt;
+        if constexpr (KB == 2) {
+            float mt0 = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+            float mt1 = fmaxf(fmaxf(s[1][0], s[1][1]), s[1][2]);
 #pragma unroll
-        for (int i = 3; i < 15; i += 2) {
-            mt0 = fmaxf(fmaxf(mt0, s[0][i]), s[0][i + 1]);
-            mt1 = fmaxf(fmaxf(mt1, s[1][i]), s[1][i + 1]);
+            for (int i = 3; i < 15; i += 2) {
+                mt0 = fmaxf(fmaxf(mt0, s[0][i]), s[0][i + 1]);
+                mt1 = fmaxf(fmaxf(mt1, s[1][i]), s[1][i + 1]);
+            }
+            mt = fmaxf(fmaxf(mt0, s[0][15]), fmaxf(mt1, s[1][15]));
+        } else {
+            mt = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+#pragma unroll
+            for (int i = 3; i < 15; i += 2) mt = fmaxf(fmaxf(mt, s[0][i]), s[0][i + 1]);
+            mt = fmaxf(mt, s[0][15]);
         }
-        float mt = fmaxf(fmaxf(mt0, s[0][15]), fmaxf(mt1, s[1][15]));
         {
             auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
                                                        false, false);
@@ -457,7 +486,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         const float mc = ((PARTIAL || WINDOW) && m_run == -INFINITY) ? 0.f : m_run * c;
         float psum = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; i += 2) {
                 const float p0 = fast_exp2(__builtin_fmaf(s[kb][i], c, -mc));
@@ -487,8 +516,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         for (int db = 0; db < DBLK; ++db) va[0][db] = vpre[db];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kst = 0; kst < 4; ++kst) {
-            if (kst + 1 < 4) {
+        for (int kst = 0; kst < 2 * KB; ++kst) {   // 16-key steps
+            if (kst + 1 < 2 * KB) {
 #pragma unroll
                 for (int db = 0; db < DBLK; ++db) va[(kst + 1) & 1][db] = vread(vt, kst + 1, db);
             }
@@ -630,6 +659,10 @@ static hipError_t launch_one(const PrefillArgs& a, int n_split, const DecodeWork
 
 int64_t prefill_row_blocks(int T_q, int G) { return ((int64_t)T_q * G + kBlockM - 1) / kBlockM; }
 
+int decode_rows_heads_per_workgroup(int T_q, int G, int H_kv) {
+    return ((int64_t)T_q * G <= kBlockM / 2 && H_kv % 2 == 0) ? 2 : 1;
+}
+
 template <bool SPLIT>
 static hipError_t dispatch(const PrefillArgs& a, int n_split, const DecodeWorkspace* ws,
                            hipStream_t stream) {
@@ -657,8 +690,9 @@ hipError_t launch_decode_rows_bf16(const void* q, const void* k, const void* v,
                                    int T_q, int H_q, int H_kv, int d, float scale,
                                    hipStream_t stream) {
     const int G = H_q / H_kv;
+    const int hp = decode_rows_heads_per_workgroup(T_q, G, H_kv);
     const int64_t n_mblk = prefill_row_blocks(T_q, G);
-    const int64_t grid = (int64_t)plan.units * n_mblk * H_kv;
+    const int64_t grid = (int64_t)plan.units * n_mblk * (H_kv / hp);
     if (grid < 1 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     const float c = scale * kLog2e;
     auto go = [&](auto kernel) {
@@ -667,8 +701,13 @@ hipError_t launch_decode_rows_bf16(const void* q, const void* k, const void* v,
                            nullptr, 1, T_q, 0, H_q, H_kv, G, c, 0, (int)n_mblk, 1, ws.m, ws.l,
                            ws.o, 0, 0, plan);
     };
-    if (d == 128) go(prefill_bf16_kernel<128, kMaskCausal, false, true>);
-    else go(prefill_bf16_kernel<64, kMaskCausal, false, true>);
+    if (d == 128) {
+        if (hp == 2) go(prefill_bf16_kernel<128, kMaskCausal, false, true, 2>);
+        else go(prefill_bf16_kernel<128, kMaskCausal, false, true, 1>);
+    } else {
+        if (hp == 2) go(prefill_bf16_kernel<64, kMaskCausal, false, true, 2>);
+        else go(prefill_bf16_kernel<64, kMaskCausal, false, true, 1>);
+    }
     return hipGetLastError();
 }
 

@@ -240,11 +240,14 @@ def test_decode_multi_split_counts(num_splits):
     (43, [43, 44, 600], 12, 4, 128, 0),       # G = 3, 129 rows: one live row in the last wave
     (7, [7, 300, 1500], 140, 7, 64, 5),       # G = 20, 140 rows, d = 64
     (128, [128, 129], 16, 8, 128, 3),         # G = 2, 256 rows
+    (8, [8, 600, 2000], 48, 3, 128, 0),       # 128 rows, odd H_kv: one head per work-group
+    (4, [4, 999], 64, 2, 128, 3),             # 128 rows, G = 32: one pair of heads
 ])
 def test_decode_multi_rows_path(T_q, kv_len, Hq, Hkv, d, num_splits):
     """From 128 query rows per KV head, decode runs the prefill tile loop on
     each split's key range: row blocks, ranges of any length and start,
-    ranges wholly in the future of some new tokens."""
+    ranges wholly in the future of some new tokens, two KV heads per
+    work-group at 128 rows (one with an odd number of heads)."""
     inp = _as_multi(gin.random_case("decode", "bf16", B=len(kv_len), H_q=Hq, H_kv=Hkv, d=d,
                                     T_q=T_q, kv_len=kv_len, seed=T_q * 77 + sum(kv_len)))
     og, lg = _decode_multi(inp, num_splits)
