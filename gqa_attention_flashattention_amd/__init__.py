@@ -10,8 +10,9 @@ from .binding import (GQAError, decode, decode_combine, decode_multi, decode_noa
                       decode_quant, decode_ring, decode_ring_quant,
                       decode_split,
                       decode_workspace_bytes, library_path, load_library, prefill,
-                      prefill_kvsplit, prefill_kvsplit_count, prefill_window)
+                      prefill_kvsplit, prefill_kvsplit_count, prefill_window,
+                      release_workspace)
 
 __all__ = ["GQAError", "prefill", "prefill_window", "prefill_kvsplit", "prefill_kvsplit_count", "decode", "decode_noalloc", "decode_multi", "decode_quant", "decode_ring", "decode_ring_quant", "decode_split", "decode_combine",
            "decode_plan",
-           "decode_workspace_bytes", "load_library", "library_path"]
+           "decode_workspace_bytes", "release_workspace", "load_library", "library_path"]

@@ -55,6 +55,8 @@ def load_library():
     lib.gqa_attn_decode.argtypes = [vp, vp, vp, vp, i, i, i, i, vp, f, i, i, vp]
     lib.gqa_attn_decode_noalloc.restype = i
     lib.gqa_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, vp, f, i, i, vp]
+    lib.gqa_attn_release_workspace.restype = i
+    lib.gqa_attn_release_workspace.argtypes = []
     lib.gqa_attn_decode_plan.restype = i
     lib.gqa_attn_decode_plan.argtypes = [i, i, i, i, vp, i, vp, vp, vp, vp, vp]
     lib.gqa_attn_decode_split.restype = i
@@ -327,6 +329,14 @@ def decode_noalloc(q, k, v, kv_len, *, scale: float | None = None, num_splits: i
                                                 _stream(q.device))
     _check(rc, "gqa_attn_decode_noalloc")
     return out
+
+
+def release_workspace():
+    """gqa_attn_release_workspace: wait for the current device and free the
+    library-owned workspace buffers (the current one and those retired by
+    growth).  Graphs captured from calls that used them must not be replayed
+    afterwards."""
+    _check(load_library().gqa_attn_release_workspace(), "gqa_attn_release_workspace")
 
 
 def decode_multi(q, k, v, kv_len, *, scale: float | None = None, num_splits: int = 0,

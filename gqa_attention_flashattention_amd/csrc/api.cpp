@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <vector>
 
 #include "gqa_attn.h"
 #include "launch.h"
@@ -238,16 +239,21 @@ struct HostPlan {
 // Per-device workspace owned by the library (the one-call decode entry
 // points and the KV-parallel prefills).  A call holds the workspace lock from
 // the moment it takes the buffer until its last kernel is queued (the
-// WorkspaceLease lives to the end of the entry point), so a call that needs a
-// larger buffer can only replace it once every call that took the old one has
-// queued its kernels; hipDeviceSynchronize then drains those kernels before
-// the old buffer is freed.  Calls on one stream therefore never see a freed or
-// foreign buffer; calls on different streams of one device still share the
-// buffer's contents and must be serialised by the caller.
+// WorkspaceLease lives to the end of the entry point), so two calls never
+// swap buffers under each other.  A call that needs a larger buffer allocates
+// one at least twice the size and retires the old one without freeing it:
+// kernels queued by earlier calls, and graphs captured from them, keep a
+// valid buffer, and growth neither waits for the device nor frees memory in
+// the middle of an asynchronous call.  Retired buffers (at most about the
+// size of the current one in total, by the doubling) are freed only by
+// gqa_attn_release_workspace.  Calls on different streams of one device
+// still share the current buffer's contents and must be serialised by the
+// caller.
 constexpr int kMaxDevices = 64;
 struct CachedWorkspace {
     void* ptr = nullptr;
     size_t bytes = 0;
+    std::vector<void*> retired;
 };
 std::mutex g_ws_mutex;
 CachedWorkspace g_ws[kMaxDevices];
@@ -263,24 +269,44 @@ int get_workspace(size_t bytes, WorkspaceLease* lease) {
     std::unique_lock<std::mutex> lock(g_ws_mutex);
     CachedWorkspace& w = g_ws[dev];
     if (w.bytes < bytes) {
-        if (w.ptr) {
-            // kernels queued by earlier calls may still read the old buffer
-            if (hipDeviceSynchronize() != hipSuccess) return GQA_ERR_HIP;
-            (void)hipFree(w.ptr);
-            w.ptr = nullptr;
-            w.bytes = 0;
-        }
         size_t want = bytes < (1u << 20) ? (1u << 20) : bytes;
-        if (hipMalloc(&w.ptr, want) != hipSuccess) {
-            w.ptr = nullptr;
-            return GQA_ERR_HIP;
+        if (want < 2 * w.bytes) want = 2 * w.bytes;
+        void* p = nullptr;
+        if (hipMalloc(&p, want) != hipSuccess) {
+            // the doubled size may not fit where the exact one does
+            (void)hipGetLastError();
+            want = bytes;
+            if (hipMalloc(&p, want) != hipSuccess) return GQA_ERR_HIP;
         }
+        if (w.ptr) w.retired.push_back(w.ptr);   // still read by queued kernels and graphs
+        w.ptr = p;
         w.bytes = want;
     }
     lease->ptr = w.ptr;
     lease->lock = std::move(lock);
     return GQA_OK;
 }
+
+}  // namespace
+
+extern "C" int gqa_attn_release_workspace(void) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GQA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    CachedWorkspace& w = g_ws[dev];
+    if (!w.ptr && w.retired.empty()) return GQA_OK;
+    if (hipDeviceSynchronize() != hipSuccess) return GQA_ERR_HIP;
+    int rc = GQA_OK;
+    for (void* p : w.retired)
+        if (hipFree(p) != hipSuccess) rc = GQA_ERR_HIP;
+    w.retired.clear();
+    if (w.ptr && hipFree(w.ptr) != hipSuccess) rc = GQA_ERR_HIP;
+    w.ptr = nullptr;
+    w.bytes = 0;
+    return rc;
+}
+
+namespace {
 
 int device_cus() {
     int dev = 0, n = 0;

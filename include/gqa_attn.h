@@ -38,8 +38,9 @@
  *    one library-owned workspace per device and process.  Each such call
  *    holds a lock on it from the moment it takes the buffer until its last
  *    kernel is queued, so calls from several host threads on ONE stream of
- *    a device are safe: a call that has to grow the buffer first waits for
- *    the kernels already queued against the old one.  Such calls on
+ *    a device are safe: a call that has to grow the buffer allocates a new
+ *    one (at least twice the size) and keeps the old one allocated for the
+ *    kernels already queued against it.  Such calls on
  *    DIFFERENT streams of one device may run their kernels at the same time
  *    and overwrite each other's partials: serialise them (e.g. with events)
  *    or use gqa_attn_decode_split / gqa_attn_decode_combine with a
@@ -48,12 +49,12 @@
  *    memset, copy or host synchronisation), so a call may be captured.  The
  *    library-owned workspace (gqa_attn_decode, _multi, _quant, _ring,
  *    _ring_quant and the KV-parallel prefills) grows on demand: a call that
- *    needs more than it holds synchronises the device, frees it and
- *    allocates a larger one, which capture forbids and which leaves a graph
- *    captured earlier pointing at freed memory.  Make the largest such call
- *    once before capturing and capture no call that needs more, or capture
+ *    needs more than it holds calls hipMalloc (which a capture may refuse),
+ *    never waits for the device and frees nothing, so graphs captured
+ *    earlier keep a valid buffer until gqa_attn_release_workspace.  Make the
+ *    largest such call once before capturing, or capture
  *    gqa_attn_decode_split / gqa_attn_decode_combine with a caller-owned
- *    workspace.
+ *    workspace, or gqa_attn_decode_noalloc.
  */
 #ifndef GQA_ATTN_H
 #define GQA_ATTN_H
@@ -173,8 +174,9 @@ int gqa_attn_prefill_kvsplit_count(int B, int T_q, int S_kv, int H_q, int H_kv, 
  * num_splits <= 0 lets the library choose.  Launches the
  * split kernel then the combine kernel on `stream`, using a workspace that the
  * library allocates on first use per device and grows on demand (a hipMalloc
- * may therefore happen inside this call; use gqa_attn_decode_split/_combine
- * with a caller-owned workspace to avoid that).
+ * may therefore happen inside this call, never a device synchronisation or a
+ * free; use gqa_attn_decode_split/_combine with a caller-owned workspace, or
+ * gqa_attn_decode_noalloc, to avoid the allocation).
  * Errors: GQA_ERR_NULL, GQA_ERR_SHAPE, GQA_ERR_UNSUPPORTED, GQA_ERR_HIP.
  */
 int gqa_attn_decode(const void *q, const void *k, const void *v, void *o, int B, int H_q,
@@ -202,6 +204,16 @@ int gqa_attn_decode(const void *q, const void *k, const void *v, void *o, int B,
  * Errors: as gqa_attn_decode, plus GQA_ERR_RANGE (scratch too small).
  */
 #define GQA_ATTN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+/*
+ * Workspace housekeeping, for callers that want the device memory of the
+ * library-owned workspace back (long-running servers after a burst of long
+ * sequences): waits for the current device (hipDeviceSynchronize), then
+ * frees the current workspace buffer and every buffer retired by growth.
+ * The next call that needs a workspace allocates a new one.  Graphs captured
+ * from calls that used the freed buffers must not be replayed afterwards.
+ * Errors: GQA_ERR_HIP.
+ */
+int gqa_attn_release_workspace(void);
 int gqa_attn_decode_noalloc(const void *q, const void *k, const void *v, void *o, int B,
                             int H_q, int H_kv, int d, const int32_t *kv_len, float scale,
                             int num_splits, int dtype, void *stream);

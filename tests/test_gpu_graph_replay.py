@@ -97,3 +97,55 @@ def test_graph_decode_ring_int4():
     _replay_matches_eager(
         lambda: gq.decode_ring_quant(q, kc, vc, ks, vs, inp.kv_len, kv_bits=4, window=window,
                                      sink=sink, out=o, lse=lse), [o, lse])
+
+
+def test_graph_survives_workspace_growth_and_release():
+    """A graph captured from a one-call decode keeps a valid workspace when a
+    later call grows the library-owned workspace (the old buffer is retired,
+    not freed): replays after the growth still give the eager call's bits.
+    gqa_attn_release_workspace then frees everything and the next call
+    allocates afresh."""
+    import gqa_attention_flashattention_amd as gq
+    import torch
+    gq.release_workspace()
+    small = gin.random_case("decode", "bf16", B=2, H_q=64, H_kv=8, d=128, kv_len=[900, 37],
+                            seed=86)
+    q, k, v = (to_gpu(x, "bf16") for x in (small.q_store, small.k_store, small.v_store))
+    o = torch.empty_like(q)
+    call = lambda: gq.decode(q, k, v, small.kv_len, out=o)
+    call()
+    torch.cuda.synchronize()
+    eager = o.clone()
+    oref, _ = oracle.decode(small.q, small.k, small.v, small.kv_len)
+    assert_close(to_f64(eager), oref, name="small decode")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+
+    # 4096 one-key splits of 64 heads: a workspace of about 136 MB
+    big = gin.random_case("decode", "bf16", B=1, H_q=64, H_kv=8, d=128, kv_len=[4096], seed=87)
+    qb, kb, vb = (to_gpu(x, "bf16") for x in (big.q_store, big.k_store, big.v_store))
+    need = gq.decode_workspace_bytes(1, 64, 8, 128, big.kv_len, 4096)
+    assert need > (64 << 20)
+    ob = gq.decode(qb, kb, vb, big.kv_len, num_splits=4096)
+    torch.cuda.synchronize()
+    obref, _ = oracle.decode(big.q, big.k, big.v, big.kv_len)
+    assert_close(to_f64(ob), obref, name="decode after growth")
+
+    for i in range(REPLAYS):
+        o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, eager), f"replay {i} after the growth differs from the eager call"
+        ob2 = gq.decode(qb, kb, vb, big.kv_len, num_splits=4096)   # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(ob2, ob)
+    del g
+    gq.release_workspace()
+    o.fill_(float("nan"))
+    call()
+    torch.cuda.synchronize()
+    assert torch.equal(o, eager)
+    gq.release_workspace()

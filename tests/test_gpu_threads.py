@@ -2,8 +2,8 @@
 
 Several Python threads (ctypes releases the GIL during each C call) issue
 gqa_attn_decode on the same device stream with split counts that grow from
-call to call, so the library has to replace its workspace while other
-threads have kernels queued against the old one.  Every output is checked
+call to call, so the library has to replace its workspace (retiring the old
+one) while other threads have kernels queued against the old one.  Every output is checked
 against the fp64 oracle; a call that launched into a freed or replaced
 buffer would show up as a wrong or non-finite result."""
 import threading
@@ -33,7 +33,7 @@ def test_threads_share_workspace_on_one_stream():
     torch.cuda.synchronize()
 
     # split caps that grow over the calls: the partials workspace grows from
-    # well under a megabyte to about 1 GB (4096 one-key splits of 64 heads)
+    # well under a megabyte to about 136 MB (4096 one-key splits of 64 heads)
     caps = [4, 32, 128, 512, 1024, 2048, 4096]
     n_threads = 4
     results = [[] for _ in range(n_threads)]
