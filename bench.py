@@ -493,7 +493,7 @@ def mfma_record(kernel: str, grid: int):
 # Launch geometry of the two headline kernels (threads per grid), to match
 # rocprofv3 records: the decode split kernel runs 256 threads per (split, KV
 # head) at G * T_q <= 16; the prefill kernel 512 threads per 256-row block.
-PREFILL_KERNEL = "prefill_bf16_kernel<128,1,false>"
+PREFILL_KERNEL = "prefill_bf16_kernel<128,1,false,false,1>"
 # bf16 splits of at least this many keys run two KV heads per work-group
 # (the library's rule; the kernel name and grid of the profiled launch follow it)
 DECODE_PAIR_MIN_SPLIT_LEN = 512

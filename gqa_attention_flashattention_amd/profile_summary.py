@@ -60,6 +60,7 @@ KERNEL_SOURCES = {
     "decode_stream_kernel": "csrc/decode.hip",
     "decode_wide_kernel": "csrc/decode.hip",
     "decode_combine_kernel": "csrc/decode.hip",
+    "decode_combine_rows_kernel": "csrc/decode.hip",
     "prefill_bf16_kernel": "csrc/prefill_bf16.hip",
     "prefill_f32_kernel": "csrc/prefill_f32.hip",
 }
