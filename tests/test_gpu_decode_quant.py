@@ -58,6 +58,8 @@ def _oracle(inp, seqs=None):
     (4, [4, 9, 700], 64, 8, 128),        # multi-token, two column blocks
     (3, [3, 250], 20, 1, 64),            # G = 20
     (2, [513, 2], 8, 8, 128),            # G = 1
+    (1, [50, 700], 6, 3, 128),           # odd H_kv
+    (2, [2, 333, 1500], 32, 8, 128),     # G = 4, two new tokens: 8 rows per KV head
 ])
 def test_quant_decode_parity(bits, T_q, kv_len, Hq, Hkv, d):
     inp = gin.quant_case(B=len(kv_len), H_q=Hq, H_kv=Hkv, d=d, kv_len=kv_len, kv_bits=bits,
