@@ -503,19 +503,21 @@ def decode_heads_per_wg(plan, w):
     return 2 if (w.H_kv % 2 == 0 and int(plan["split_len"]) >= DECODE_PAIR_MIN_SPLIT_LEN) else 1
 
 
-# bf16 caches with at most 16 query rows per KV head stream K/V into LDS, one
+# bf16 caches with at most 32 query rows per KV head stream K/V into LDS, one
 # KV head per work-group, with two LDS slots per wave above this many keys
+# (always with 17-32 rows: two column blocks)
 DECODE_STREAM_ONE_SLOT_KEYS = 128
 
 
 def decode_is_stream(w):
-    return w.G * w.T_q <= 16
+    return w.G * w.T_q <= 32
 
 
 def decode_split_kernel_name(plan, w):
     if decode_is_stream(w):
-        r = 2 if int(plan["split_len"]) > DECODE_STREAM_ONE_SLOT_KEYS else 1
-        return f"decode_stream_kernel<{w.d},{r},false>"
+        nh = 2 if w.G * w.T_q > 16 else 1
+        r = 2 if nh == 2 or int(plan["split_len"]) > DECODE_STREAM_ONE_SLOT_KEYS else 1
+        return f"decode_stream_kernel<{w.d},{r},false,{nh}>"
     return f"decode_split_kernel<{w.d},1,false,0,{decode_heads_per_wg(plan, w)}>"
 
 

@@ -569,6 +569,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // With R = 2 a work-group holds 128 KiB of LDS (one per compute unit); with
 // R = 1 (splits of at most 128 keys, one tile per wave) 64 KiB.
 constexpr int kStreamOneSlotKeys = kWaves * kTile;   // 128: one tile per wave
+// bf16 caches with up to 32 query rows per KV head take decode_stream_kernel
+__host__ __device__ inline bool decode_is_stream(int T_q, int G) { return T_q * G <= 2 * kCols; }
 
 // One wave-wide 16-byte-per-lane load from a buffer straight into LDS
 // (lane l's 16 bytes at lds_byte + 16 l).  Written as inline assembly so that
@@ -598,7 +600,11 @@ struct StreamSmem {
 template <int D>
 __device__ __forceinline__ int stream_swz(int r) { return r & (D / 8 - 1); }
 
-template <int D, int R, bool RING>
+// NH: 16-row column blocks of query rows per KV head (1, or 2 for 17-32 rows,
+// which always takes two slots per wave: with the Q area of 32 rows the
+// work-group holds 160 KiB of LDS).  Each K or V read from LDS feeds NH
+// MFMAs.
+template <int D, int R, bool RING, int NH = 1>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R == 1 ? 2 : 1))) void decode_stream_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ ws_m, float* __restrict__ ws_l,
@@ -612,9 +618,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R =
     constexpr int LOADS = kTile / ROWS_PER_LOAD;   // DMA instructions per K or V tile
     constexpr int LPT = 2 * LOADS;                 // per tile (K and V)
     static_assert(R == 1 || R == 2, "one or two slots per wave");
+    static_assert(NH == 1 || (NH == 2 && R == 2), "32 query rows: two slots per wave");
     __shared__ __attribute__((aligned(1024))) uint16_t slot0[kWaves * SM::SLOT_ELEMS];
     __shared__ __attribute__((aligned(1024))) uint16_t slot1[R > 1 ? kWaves * SM::SLOT_ELEMS : 8];
-    __shared__ __attribute__((aligned(1024))) uint16_t qlds[kWaves * kCols * D];   // per wave
+    __shared__ __attribute__((aligned(1024))) uint16_t qlds[kWaves * NH * kCols * D];   // per wave
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -655,28 +662,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R =
         rmap = RowMap{s_end, ring.sink, w_lo >= ring.sink ? (w_lo - ring.sink) % wrap : 0, wrap};
     }
 
-    // Q^T operand (column = query row)
-    const int fc = min(col, ncols - 1);            // columns past the end read a valid row
-    const int tq = fc / G;
-    const int hq = kv * G + fc % G;
-    const int pos = pos0 + tq;
-    int vis_end, wbeg = 0;
-    if (RING) {
-        vis_end = min(kend, pos < s_end ? pos + 1 : s_end + (pos - w_lo + 1));
-        wbeg = s_end + max(0, pos - ring.window + 1 - w_lo);
-    } else {
-        vis_end = min(kend, pos + 1);
+    // Q^T operand (column = query row; block h holds rows 16 h ..)
+    int vis_end[NH], wbeg[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        const int fc = min(h * kCols + col, ncols - 1);   // columns past the end read a valid row
+        const int pos = pos0 + fc / G;
+        if (RING) {
+            vis_end[h] = min(kend, pos < s_end ? pos + 1 : s_end + (pos - w_lo + 1));
+            wbeg[h] = s_end + max(0, pos - ring.window + 1 - w_lo);
+        } else {
+            vis_end[h] = min(kend, pos + 1);
+            wbeg[h] = 0;
+        }
     }
-    // Q rows of the 16 columns go into the wave's own Q area first (row c =
+    // Q rows of the 16 NH columns go into the wave's own Q area first (row c =
     // column c, chunks swizzled as the K rows), so that the wait for the
     // first tile covers them
-    uint16_t* qw = qlds + wave * kCols * D;
+    uint16_t* qw = qlds + wave * NH * kCols * D;
     {
         // based at the KV head's first query head of token 0; T_q * H_q * d * 2
         // bytes stay far below 2^31 (T_q <= 256)
         const i32x4 rs = buffer_rsrc(q + ((int64_t)b * T_q * H_q + (int64_t)kv * G) * D, 0x7ffffff0);
 #pragma unroll
-        for (int j = 0; j < kCols / ROWS_PER_LOAD; ++j) {
+        for (int j = 0; j < NH * kCols / ROWS_PER_LOAD; ++j) {
             const int r = j * ROWS_PER_LOAD + lane / CPR;           // column
             const int rc = min(r, ncols - 1);
             const int cc = (lane % CPR) ^ stream_swz<D>(r);
@@ -684,7 +693,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R =
                   (((rc / G) * H_q + rc % G) * D + cc * 8) * 2);
         }
     }
-    bf16x8 qf[KSTEPS];                             // read once its loads have landed
+    bf16x8 qf[NH][KSTEPS];                         // read once its loads have landed
     // walk indices before mask_from are visible to all tokens (apart from the
     // ring window starts, all below wbeg_max)
     const int mask_from = RING ? min(kend, pos0 < s_end ? pos0 + 1 : s_end + (pos0 - w_lo + 1))
@@ -747,72 +756,91 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R =
         }
     }
 
-    f32x4 oacc[DBLK];
+    f32x4 oacc[NH][DBLK];
+    float m_run[NH], l_run[NH];
 #pragma unroll
-    for (int j = 0; j < DBLK; ++j) oacc[j] = f32x4{};
-    float m_run = -INFINITY, l_run = 0.f;
+    for (int h = 0; h < NH; ++h) {
+#pragma unroll
+        for (int j = 0; j < DBLK; ++j) oacc[h][j] = f32x4{};
+        m_run[h] = -INFINITY;
+        l_run[h] = 0.f;
+    }
 
     // one tile from slot sl: S^T = K Q^T, mask, online softmax, O += P V
     auto process = [&](int i, int sl) __attribute__((always_inline)) {
         const int key0 = kbeg + (wave + kWaves * i) * kTile;
         const uint16_t* kt = wslot(sl);
         const uint16_t* vt = kt + SM::TILE_ELEMS;
-        f32x4 s[2];
+        f32x4 s[NH][2];
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
-            s[blk] = f32x4{};
+#pragma unroll
+            for (int h = 0; h < NH; ++h) s[h][blk] = f32x4{};
 #pragma unroll
             for (int st = 0; st < KSTEPS; ++st) {
                 const bf16x8 ka = *(const bf16x8*)(kt + koff[blk][st]);
-                s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[st], s[blk], 0, 0, 0);
+#pragma unroll
+                for (int h = 0; h < NH; ++h)
+                    s[h][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[h][st], s[h][blk],
+                                                                         0, 0, 0);
             }
         }
         if (key0 + kTile > mask_from || (RING && key0 + kTile > s_end && key0 < wbeg_max)) {
 #pragma unroll
+            for (int h = 0; h < NH; ++h)
+#pragma unroll
+                for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int key = key0 + g4 + 16 * blk + 4 * e;
+                        bool hide = key >= vis_end[h];
+                        if (RING) hide = hide || (key >= s_end && key < wbeg[h]);
+                        if (hide) s[h][blk][e] = -INFINITY;
+                    }
+        }
+        bf16x8 pb[NH];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            float mt = fmaxf(fmaxf(fmaxf(s[h][0][0], s[h][0][1]), fmaxf(s[h][0][2], s[h][0][3])),
+                             fmaxf(fmaxf(s[h][1][0], s[h][1][1]), fmaxf(s[h][1][2], s[h][1][3])));
+            mt = fmaxf(mt, xor16(mt));
+            mt = fmaxf(mt, xor32(mt));
+            // Lazy rescale: the reference max moves only when a column's tile
+            // max exceeds it by more than 2^8 in the exponentials (then O and
+            // l are rescaled); otherwise P <= 2^8 against the old reference,
+            // which the fp32 sums carry exactly as well.  The wave's first
+            // tile sets it.
+            if (i == 0) {
+                m_run[h] = mt;
+            } else if (__builtin_amdgcn_ballot_w64(mt * c > m_run[h] * c + 8.f) != 0) {
+                const float m_new = fmaxf(m_run[h], mt);
+                const float corr = (m_new == -INFINITY) ? 1.f : fast_exp2((m_run[h] - m_new) * c);
+                l_run[h] *= corr;
+#pragma unroll
+                for (int db = 0; db < DBLK; ++db) oacc[h][db] *= corr;
+                m_run[h] = m_new;
+            }
+            const float mc = (m_run[h] == -INFINITY) ? 0.f : m_run[h] * c;
+            float p[8];
+#pragma unroll
             for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int key = key0 + g4 + 16 * blk + 4 * e;
-                    bool hide = key >= vis_end;
-                    if (RING) hide = hide || (key >= s_end && key < wbeg);
-                    if (hide) s[blk][e] = -INFINITY;
-                }
+                for (int e = 0; e < 4; ++e)
+                    p[blk * 4 + e] = fast_exp2(__builtin_fmaf(s[h][blk][e], c, -mc));
+            l_run[h] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+            const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                              pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+            pb[h] = __builtin_bit_cast(bf16x8, pw);
         }
-        float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-        mt = fmaxf(mt, xor16(mt));
-        mt = fmaxf(mt, xor32(mt));
-        // Lazy rescale: the reference max moves only when a column's tile max
-        // exceeds it by more than 2^8 in the exponentials (then O and l are
-        // rescaled); otherwise P <= 2^8 against the old reference, which the
-        // fp32 sums carry exactly as well.  The wave's first tile sets it.
-        if (i == 0) {
-            m_run = mt;
-        } else if (__builtin_amdgcn_ballot_w64(mt * c > m_run * c + 8.f) != 0) {
-            const float m_new = fmaxf(m_run, mt);
-            const float corr = (m_new == -INFINITY) ? 1.f : fast_exp2((m_run - m_new) * c);
-            l_run *= corr;
-#pragma unroll
-            for (int db = 0; db < DBLK; ++db) oacc[db] *= corr;
-            m_run = m_new;
-        }
-        const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
-        float p[8];
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) p[blk * 4 + e] = fast_exp2(__builtin_fmaf(s[blk][e], c, -mc));
-        l_run += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-        const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                          pack_bf16x2(p[6], p[7])};
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) {
             const s16x4 lo = lds_read_tr16(vt + voff[0][db]);
             const s16x4 hi = lds_read_tr16(vt + voff[1][db]);
             const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a8), pb,
-                                                              oacc[db], 0, 0, 0);
+#pragma unroll
+            for (int h = 0; h < NH; ++h)
+                oacc[h][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, a8), pb[h], oacc[h][db], 0, 0, 0);
         }
     };
 
@@ -821,8 +849,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R =
     else if (n_w >= 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LPT) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int st = 0; st < KSTEPS; ++st)
-        qf[st] = *(const bf16x8*)(qw + col * D + (((st * 4 + g4) ^ stream_swz<D>(col)) << 3));
+    for (int h = 0; h < NH; ++h) {
+        const int r = h * kCols + col;
+#pragma unroll
+        for (int st = 0; st < KSTEPS; ++st)
+            qf[h][st] = *(const bf16x8*)(qw + r * D + (((st * 4 + g4) ^ stream_swz<D>(r)) << 3));
+    }
 
     // Tile j sits in slot j mod R; when it is processed the loads in flight
     // are those of the wave's tiles j .. min(j + R, n_w) - 1, oldest first, so
@@ -843,12 +875,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R =
     }
 
     // ---- merge the four wave partials ----
-    // Each wave puts its unnormalised partial (m, l, O) into its own slot-0
-    // area, which no other wave reads before the barrier; after it, every
-    // thread merges four waves' values for its outputs.
-    float lr = l_run;
-    lr += xor16(lr);
-    lr += xor32(lr);
+    // Each wave puts its unnormalised partial (m, l, O) of column block h into
+    // its own slot-h area, which no other wave reads before the barrier;
+    // after it, every thread merges four waves' values for its outputs.
     // no DMA write into this wave's slots may still be pending
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     // wave area: O [16][CS] (columns padded by 4 floats against bank
@@ -857,41 +886,51 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R =
     constexpr int AREA = kCols * CS + 2 * kCols;             // floats
     static_assert(AREA * 4 <= SM::SLOT_ELEMS * 2, "a wave's merge area fits its slot");
     constexpr int AREA_STRIDE = SM::SLOT_ELEMS / 2;          // floats between waves' areas
-    float* mw = (float*)(slot0 + wave * SM::SLOT_ELEMS);
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) *(f32x4*)(mw + col * CS + db * 16 + g4 * 4) = oacc[db];
-    if (g4 == 0) {
-        mw[kCols * CS + col] = lr;
-        mw[kCols * CS + kCols + col] = m_run;
+    for (int h = 0; h < NH; ++h) {
+        float lr = l_run[h];
+        lr += xor16(lr);
+        lr += xor32(lr);
+        float* mw = (float*)((h == 0 ? slot0 : slot1) + wave * SM::SLOT_ELEMS);
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) *(f32x4*)(mw + col * CS + db * 16 + g4 * 4) = oacc[h][db];
+        if (g4 == 0) {
+            mw[kCols * CS + col] = lr;
+            mw[kCols * CS + kCols + col] = m_run[h];
+        }
     }
     __syncthreads();
-    const float* mrg = (const float*)slot0;
     const int64_t pidx = (int64_t)plan.split_base + unit;
-    constexpr int PER = kCols * D / 4 / kThreads;  // f32x4 outputs per thread
+    constexpr int PER = kCols * D / 4 / kThreads;  // f32x4 outputs per thread and block
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int e = tid + u * kThreads;
-        const int cc = e / (D / 4), x = (e % (D / 4)) * 4;
-        if (cc >= ncols) continue;
-        float mwv[kWaves], mx = -INFINITY;
+    for (int h = 0; h < NH; ++h) {
+        const float* mrg = (const float*)(h == 0 ? slot0 : slot1);
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            mwv[w] = mrg[w * AREA_STRIDE + kCols * CS + kCols + cc];
-            mx = fmaxf(mx, mwv[w]);
-        }
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        float lsum = 0.f;
+        for (int u = 0; u < PER; ++u) {
+            const int e = tid + u * kThreads;
+            const int cl = e / (D / 4), x = (e % (D / 4)) * 4;
+            const int cc = h * kCols + cl;         // query row of the KV head
+            if (cc >= ncols) continue;
+            float mwv[kWaves], mx = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float sc = (mwv[w] == -INFINITY) ? 0.f : fast_exp2((mwv[w] - mx) * c);
-            acc += sc * *(const f32x4*)(mrg + w * AREA_STRIDE + cc * CS + x);
-            lsum += sc * mrg[w * AREA_STRIDE + kCols * CS + cc];
-        }
-        const int64_t hrow = (pidx * T_q + cc / G) * H_q + (int64_t)kv * G + cc % G;
-        *(f32x4*)(ws_o + hrow * D + x) = acc;
-        if (x == 0) {
-            ws_m[hrow] = mx * c;                   // base-2 units
-            ws_l[hrow] = lsum;
+            for (int w = 0; w < kWaves; ++w) {
+                mwv[w] = mrg[w * AREA_STRIDE + kCols * CS + kCols + cl];
+                mx = fmaxf(mx, mwv[w]);
+            }
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            float lsum = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float sc = (mwv[w] == -INFINITY) ? 0.f : fast_exp2((mwv[w] - mx) * c);
+                acc += sc * *(const f32x4*)(mrg + w * AREA_STRIDE + cl * CS + x);
+                lsum += sc * mrg[w * AREA_STRIDE + kCols * CS + cl];
+            }
+            const int64_t hrow = (pidx * T_q + cc / G) * H_q + (int64_t)kv * G + cc % G;
+            *(f32x4*)(ws_o + hrow * D + x) = acc;
+            if (x == 0) {
+                ws_m[hrow] = mx * c;               // base-2 units
+                ws_l[hrow] = lsum;
+            }
         }
     }
 }
@@ -1301,13 +1340,13 @@ int64_t decode_workgroups_per_split(DecodeKind kind, int T_q, int G, int H_kv, i
         pairs = kind == DecodeKind::Bf16 || kind == DecodeKind::Ring;
     }
     int hp = (pairs && H_kv % 2 == 0 && split_len >= kPairMinSplitLen) ? 2 : 1;
-    // bf16 caches with one column block stream K/V into LDS one KV head per
-    // work-group (decode_stream_kernel); with two slots per wave a
+    // bf16 caches with up to two column blocks stream K/V into LDS one KV
+    // head per work-group (decode_stream_kernel); with two slots per wave a
     // work-group holds the LDS of two, so it counts twice
     int occ = 1;
-    if ((kind == DecodeKind::Bf16 || kind == DecodeKind::Ring) && T_q * G <= kCols) {
+    if ((kind == DecodeKind::Bf16 || kind == DecodeKind::Ring) && decode_is_stream(T_q, G)) {
         hp = 1;
-        occ = split_len > kStreamOneSlotKeys ? 2 : 1;
+        occ = (T_q * G > kCols || split_len > kStreamOneSlotKeys) ? 2 : 1;
     }
     return n_hg * (H_kv / hp) * occ;
 }
@@ -1378,25 +1417,28 @@ static hipError_t split_dispatch(const void* q, const void* k, const void* v,
     const int hp = (KVF == kKvBf16 && H_kv % 2 == 0 && min_len >= kPairMinSplitLen) ? 2 : 1;
     const float c = scale * kLog2e;
     const int64_t uh = (int64_t)plan.units * n_hg;
-    if (KVF == kKvBf16 && T_q * G <= kCols &&
+    if (KVF == kKvBf16 && decode_is_stream(T_q, G) &&
         (!RING || (int64_t)ring.capacity * H_kv * d * 2 < 0x7fff0000)) {
         // one KV head per work-group, K/V streamed into LDS (decode_stream_kernel)
         int max_len = 0;
         for (int i = 0; i < plan.nseq; ++i)
             max_len = std::max(max_len, std::min((int)plan.split_len[i], (int)plan.len[i]));
         const dim3 sgrid((unsigned)(plan.units * H_kv));
-        const bool two = max_len > kStreamOneSlotKeys;
+        const bool wide = T_q * G > kCols;          // two column blocks (always two slots)
+        const bool two = wide || max_len > kStreamOneSlotKeys;
         auto go = [&](auto kernel) {
             hipLaunchKernelGGL(kernel, sgrid, dim3(kThreads), 0, stream, (const uint16_t*)q,
                                (const uint16_t*)k, (const uint16_t*)v, ws.m, ws.l, ws.o, plan, T_q,
                                H_q, H_kv, G, c, ring);
         };
         if (d == 128) {
-            if (two) go(decode_stream_kernel<128, 2, RING>);
-            else go(decode_stream_kernel<128, 1, RING>);
+            if (wide) go(decode_stream_kernel<128, 2, RING, 2>);
+            else if (two) go(decode_stream_kernel<128, 2, RING, 1>);
+            else go(decode_stream_kernel<128, 1, RING, 1>);
         } else {
-            if (two) go(decode_stream_kernel<64, 2, RING>);
-            else go(decode_stream_kernel<64, 1, RING>);
+            if (wide) go(decode_stream_kernel<64, 2, RING, 2>);
+            else if (two) go(decode_stream_kernel<64, 2, RING, 1>);
+            else go(decode_stream_kernel<64, 1, RING, 1>);
         }
         return hipGetLastError();
     }

@@ -233,9 +233,10 @@ int gqa_attn_decode_noalloc(const void *q, const void *k, const void *v, void *o
  *                    sequences, plus 8 * max_b n_b, W being the split
  *                    work-groups of a launch and R the number resident at
  *                    once (two per compute unit).  A bf16 or ring cache
- *                    with at most 16 query rows per KV head (G * T_q <= 16)
+ *                    with at most 32 query rows per KV head (G * T_q <= 32)
  *                    takes one work-group per (split, KV head), which counts
- *                    twice above 128 keys (it holds the LDS of two); a
+ *                    twice above 128 keys or above 16 rows (it holds the LDS
+ *                    of two); a
  *                    bf16 packed cache with at least 128 query rows per KV
  *                    head (G * T_q >= 128, gqa_attn_decode_multi) takes one
  *                    work-group per (split, block of 256 rows, KV head),
