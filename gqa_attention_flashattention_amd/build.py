@@ -33,7 +33,7 @@ CEIL_SOURCES = ["ceilings.hip"]
 # chain (about 1% faster on 8k causal prefill, same results bit for bit).
 EXTRA_FLAGS = {
     "prefill_bf16.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
-    "decode.hip": ["-fno-honor-nans"],
+    "decode.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-kernarg-preload-count=16"],
 }
 ARCH = os.environ.get("GQA_ATTN_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

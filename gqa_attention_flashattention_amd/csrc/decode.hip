@@ -605,11 +605,17 @@ __device__ __forceinline__ int stream_swz(int r) { return r & (D / 8 - 1); }
 // work-group holds 160 KiB of LDS).  Each K or V read from LDS feeds NH
 // MFMAs.
 template <int D, int R, bool RING, int NH = 1>
+// The first sixteen argument dwords (pointers to Q, K and V, the first
+// sequence's plan entry and the head counts) are everything a work-group of
+// a one-sequence launch needs before it issues its loads; the library is
+// built to preload them into scalar registers at dispatch, so those loads do
+// not wait for a kernel-argument fetch.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R == 1 ? 2 : 1))) void decode_stream_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, float* __restrict__ ws_m, float* __restrict__ ws_l,
-    float* __restrict__ ws_o, const DecodePlanChunk plan, int T_q, int H_q, int H_kv, int G,
-    float c, RingArgs ring) {
+    const uint16_t* __restrict__ v, int64_t key_off0, int nseq, int len0, int split_len0,
+    int seq0, int T_q, int H_q, int H_kv, int G, float* __restrict__ ws_m,
+    float* __restrict__ ws_l, float* __restrict__ ws_o, const DecodePlanChunk plan, float c,
+    RingArgs ring) {
     using SM = StreamSmem<D>;
     constexpr int KSTEPS = D / 32;
     constexpr int DBLK = D / 16;
@@ -631,13 +637,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R =
 
     const int kv = blockIdx.x % H_kv;
     const int unit = blockIdx.x / H_kv;
-    // plan entries: index 0 is loaded with the launch's other arguments; a
-    // launch of several sequences looks its own up
+    // plan entries: index 0 comes with the leading arguments (unit_base[0]
+    // is 0); a launch of several sequences looks its own up
     int sq = 0;
-    int len = plan.len[0], L = plan.split_len[0], ub = plan.unit_base[0];
-    int ntok = plan.ntok[0];
-    int64_t key_off = plan.key_off[0];
-    if (plan.nseq > 1) {
+    int len = len0, L = split_len0, ub = 0;
+    int ntok = RING ? plan.ntok[0] : len0;
+    int64_t key_off = key_off0;
+    if (nseq > 1) {
         while (sq + 1 < plan.nseq && plan.unit_base[sq + 1] <= unit) ++sq;
         len = plan.len[sq];
         L = plan.split_len[sq];
@@ -648,7 +654,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R =
     const int split = unit - ub;
     const int kbeg = split * L;
     const int kend = min(len, kbeg + L);
-    const int b = plan.seq0 + sq;
+    const int b = seq0 + sq;
     const int ncols = T_q * G;
     // walk index <-> position: [0, s_end) are positions 0.., then w_lo.. (ring);
     // a packed cache is the identity (s_end = w_lo = 0)
@@ -957,20 +963,23 @@ __device__ __forceinline__ void merge_lse(float& m, float& l, f32x4& o, float m2
 }
 
 template <int D, int NB>
+// (leading arguments: what a one-sequence launch needs before its loads,
+// preloaded into scalar registers like the stream kernel's)
 __global__ __launch_bounds__(64) void decode_combine_kernel(
     const float* __restrict__ ws_m, const float* __restrict__ ws_l,
-    const float* __restrict__ ws_o, uint16_t* __restrict__ o, float* __restrict__ lse,
-    const DecodePlanChunk plan, int T_q, int H_q) {
+    const float* __restrict__ ws_o, int nseq, int split_base, int units0, int seq0, int T_q,
+    int H_q, uint16_t* __restrict__ o, float* __restrict__ lse, const DecodePlanChunk plan) {
     constexpr int CHUNKS = D / 32;
     const int R = T_q * H_q;                                   // rows per sequence
     const int lane = threadIdx.x;
     const int item = blockIdx.x;   // (sequence, head, chunk)
-    if (item >= plan.nseq * R * CHUNKS) return;
+    if (item >= nseq * R * CHUNKS) return;
     const int chunk = item % CHUNKS;
     const int sh = item / CHUNKS;
     const int sq = sh / R, r = sh % R;                         // r = t * H_q + h
-    const int n = plan.unit_base[sq + 1] - plan.unit_base[sq];
-    const int64_t p0 = (int64_t)plan.split_base + plan.unit_base[sq];
+    // one sequence: its splits are the launch's units
+    const int n = nseq == 1 ? units0 : plan.unit_base[sq + 1] - plan.unit_base[sq];
+    const int64_t p0 = (int64_t)split_base + (nseq == 1 ? 0 : plan.unit_base[sq]);
 
     const int sg = lane >> 3, dq = lane & 7;
     const int dim = chunk * 32 + dq * 4;
@@ -1002,7 +1011,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
         merge_lse(m, l, acc, m2, l2, o2);
     }
     const float inv = 1.f / l;
-    const int b = plan.seq0 + sq;
+    const int b = seq0 + sq;
     if (sg == 0) {
         u32x2 w = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
         *(u32x2*)(o + ((int64_t)b * R + r) * D + dim) = w;
@@ -1428,8 +1437,9 @@ static hipError_t split_dispatch(const void* q, const void* k, const void* v,
         const bool two = wide || max_len > kStreamOneSlotKeys;
         auto go = [&](auto kernel) {
             hipLaunchKernelGGL(kernel, sgrid, dim3(kThreads), 0, stream, (const uint16_t*)q,
-                               (const uint16_t*)k, (const uint16_t*)v, ws.m, ws.l, ws.o, plan, T_q,
-                               H_q, H_kv, G, c, ring);
+                               (const uint16_t*)k, (const uint16_t*)v, plan.key_off[0], plan.nseq,
+                               (int)plan.len[0], (int)plan.split_len[0], plan.seq0, T_q, H_q, H_kv,
+                               G, ws.m, ws.l, ws.o, plan, c, ring);
         };
         if (d == 128) {
             if (wide) go(decode_stream_kernel<128, 2, RING, 2>);
@@ -1539,7 +1549,8 @@ hipError_t launch_decode_combine_bf16(const DecodeWorkspace& ws, const DecodePla
     const int nb = per_lane <= 1 ? 1 : per_lane <= 2 ? 2 : per_lane <= 4 ? 4 : 8;
     auto go = [&](auto kernel) {
         hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(64), 0, stream, ws.m, ws.l, ws.o,
-                           (uint16_t*)o, lse, plan, T_q, H_q);
+                           plan.nseq, plan.split_base, plan.units, plan.seq0, T_q, H_q,
+                           (uint16_t*)o, lse, plan);
     };
     if (d == 128) {
         if (nb == 1) go(decode_combine_kernel<128, 1>);
