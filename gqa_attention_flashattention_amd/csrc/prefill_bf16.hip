@@ -49,7 +49,11 @@
 //  * Lazy rescaling: the running max used for the exponentials is only moved
 //    when some row's tile max exceeds it by more than 8 (log2 units), so most
 //    tiles skip the O rescale; exact, since O and l always share the same
-//    reference max and P stays below 2^8.
+//    reference max and P stays below 2^8.  The tile's row max itself is only
+//    taken when needed: P is first computed against the current reference,
+//    and only if some lane's sum of P over the tile exceeds 2^8 (which any
+//    P above 2^8 implies) does the wave compute the row max, rescale if it
+//    grew by more than 8 and recompute P.
 #include <type_traits>
 
 #include "common.h"
@@ -448,52 +452,63 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
                     if (hide) s[kb][i] = -INFINITY;
                 }
         }
-        float mt;
-        if constexpr (KB == 2) {
-            float mt0 = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
-            float mt1 = fmaxf(fmaxf(s[1][0], s[1][1]), s[1][2]);
+        // exponentials against the current reference max first; a lane whose
+        // P sum exceeds 2^8 (infinite while a row with visible keys has no
+        // reference max yet) sends the wave through the row max and the
+        // rescale, then P is recomputed
+        auto expsum = [&](float mcv) __attribute__((always_inline)) {
+            float ps = 0.f;
 #pragma unroll
-            for (int i = 3; i < 15; i += 2) {
-                mt0 = fmaxf(fmaxf(mt0, s[0][i]), s[0][i + 1]);
-                mt1 = fmaxf(fmaxf(mt1, s[1][i]), s[1][i + 1]);
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; i += 2) {
+                    const float p0 = fast_exp2(__builtin_fmaf(s[kb][i], c, -mcv));
+                    const float p1 = fast_exp2(__builtin_fmaf(s[kb][i + 1], c, -mcv));
+                    pk[kb][i >> 1] = pack_bf16x2(p0, p1);
+                    ps += p0 + p1;
+                }
+            return ps;
+        };
+        float psum = expsum(fmaxf(m_run * c, -1e30f));
+        if (__builtin_amdgcn_ballot_w64(psum > 256.f) != 0) {
+            float mt;
+            if constexpr (KB == 2) {
+                float mt0 = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+                float mt1 = fmaxf(fmaxf(s[1][0], s[1][1]), s[1][2]);
+#pragma unroll
+                for (int i = 3; i < 15; i += 2) {
+                    mt0 = fmaxf(fmaxf(mt0, s[0][i]), s[0][i + 1]);
+                    mt1 = fmaxf(fmaxf(mt1, s[1][i]), s[1][i + 1]);
+                }
+                mt = fmaxf(fmaxf(mt0, s[0][15]), fmaxf(mt1, s[1][15]));
+            } else {
+                mt = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+#pragma unroll
+                for (int i = 3; i < 15; i += 2) mt = fmaxf(fmaxf(mt, s[0][i]), s[0][i + 1]);
+                mt = fmaxf(mt, s[0][15]);
             }
-            mt = fmaxf(fmaxf(mt0, s[0][15]), fmaxf(mt1, s[1][15]));
-        } else {
-            mt = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
-#pragma unroll
-            for (int i = 3; i < 15; i += 2) mt = fmaxf(fmaxf(mt, s[0][i]), s[0][i + 1]);
-            mt = fmaxf(mt, s[0][15]);
-        }
-        {
-            auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
-                                                       false, false);
-            mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        }
-        const bool grow = mt * c > m_run * c + kRescaleThreshold;
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-            const float m_new = fmaxf(m_run, mt);
-            // 0 on the first tile; a row with no visible key so far keeps corr = 1
-            const float corr = (m_new == -INFINITY) ? 1.f : fast_exp2((m_run - m_new) * c);
-            l_run *= corr;
-#pragma unroll
-            for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) oacc[db][i] *= corr;
-            m_run = m_new;
-        }
-        // a window or a split can start past the keys a row sees: its m stays
-        // -inf and P = 0
-        const float mc = ((PARTIAL || WINDOW) && m_run == -INFINITY) ? 0.f : m_run * c;
-        float psum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; i += 2) {
-                const float p0 = fast_exp2(__builtin_fmaf(s[kb][i], c, -mc));
-                const float p1 = fast_exp2(__builtin_fmaf(s[kb][i + 1], c, -mc));
-                psum += p0 + p1;
-                pk[kb][i >> 1] = pack_bf16x2(p0, p1);
+            {
+                auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
+                                                           false, false);
+                mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
             }
+            const bool grow = mt * c > m_run * c + kRescaleThreshold;
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                const float m_new = fmaxf(m_run, mt);
+                // 0 on the first tile; a row with no visible key so far keeps corr = 1
+                const float corr = (m_new == -INFINITY) ? 1.f : fast_exp2((m_run - m_new) * c);
+                l_run *= corr;
+#pragma unroll
+                for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) oacc[db][i] *= corr;
+                m_run = m_new;
+            }
+            // a window or a split can start past the keys a row sees: its m stays
+            // -inf and P = 0
+            const float mc = ((PARTIAL || WINDOW) && m_run == -INFINITY) ? 0.f : m_run * c;
+            psum = expsum(mc);
+        }
         l_run += psum;
     };
     // O^T += V^T P^T of tile j; V^T operands read one 16-key step ahead, the
