@@ -773,7 +773,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R =
     }
 
     // one tile from slot sl: S^T = K Q^T, mask, online softmax, O += P V
-    auto process = [&](int i, int sl) __attribute__((always_inline)) {
+    // (more: the wave's next tile is in flight behind this one; K is waited
+    // for before the call, V only before the P.V step)
+    auto process = [&](int i, int sl, bool more) __attribute__((always_inline)) {
         const int key0 = kbeg + (wave + kWaves * i) * kTile;
         const uint16_t* kt = wslot(sl);
         const uint16_t* vt = kt + SM::TILE_ELEMS;
@@ -838,6 +840,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R =
                               pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
             pb[h] = __builtin_bit_cast(bf16x8, pw);
         }
+        if (more) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LPT) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) {
             const s16x4 lo = lds_read_tr16(vt + voff[0][db]);
@@ -870,9 +874,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R =
         for (int sl = 0; sl < R; ++sl) {
             const int j = i + sl;
             if (j >= n_w) break;                   // wave-uniform
-            if (R == 2 && j + 1 < n_w) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LPT) : "memory");
-            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            process(j, sl);
+            // this tile's K rows (issued before its V rows) have landed
+            const bool more = R == 2 && j + 1 < n_w;
+            if (more) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LPT + LOADS) : "memory");
+            else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LOADS) : "memory");
+            process(j, sl, more);
             if (j + R < n_w) {
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the slot's LDS reads are done
                 issue(j + R, sl);
