@@ -146,6 +146,14 @@ __device__ __forceinline__ void issue_tile(uint16_t* kst, uint16_t* vst,
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+// Barrier of the tile loop: all waves meet, without waiting for this wave's
+// LDS reads first.  Every LDS read of a K/V stage in the loop feeds an MFMA
+// of the same phase, except the first V^T step read at the end of a softmax
+// phase for the next phase's P.V, and that stage is not refilled before two
+// more iterations; so no read is pending on a stage a DMA load issued after
+// the barrier writes (the Q rows staged before the loop are read before the
+// full lds_barrier that precedes it).
+__device__ __forceinline__ void loop_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Wait until at most N of this wave's vector-memory operations are pending.
 template <int N>
@@ -552,7 +560,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     auto end_iter = [&](int i) __attribute__((always_inline)) {
         if (i + 2 < n_tiles) wait_vmcnt<LOADS_PER_TILE>();
         else wait_vmcnt<0>();
-        lds_barrier();
+        loop_barrier();
     };
     // Iteration i (tile i in stage i & 3), i = 0 .. n_tiles: waves 0-3 run
     // [PV(i - 1), QK(i)] then [softmax(i)]; waves 4-7 run [softmax(i - 1)]
@@ -566,7 +574,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         if (i >= 1) pv(i - 1, vsm + ((st + 3) & 3) * T::ELEMS);
         if (i < n_tiles) qk(i, ksm + st * T::ELEMS);
         __builtin_amdgcn_s_setprio(0);
-        lds_barrier();
+        loop_barrier();
         if (i + 2 < n_tiles) issue(i + 2, (st + 2) & 3);
         if (i < n_tiles) {
             softmax(i);
@@ -580,7 +588,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
             softmax(i - 1);
             pv_pre(i - 1, vsm + ((st + 3) & 3) * T::ELEMS);
         }
-        lds_barrier();
+        loop_barrier();
         __builtin_amdgcn_s_setprio(1);
         if (i >= 1) pv(i - 1, vsm + ((st + 3) & 3) * T::ELEMS);
         if (i < n_tiles) qk(i, ksm + st * T::ELEMS);
