@@ -70,6 +70,7 @@ constexpr int kBlockN = 64;                      // keys per tile
 constexpr int kThreads = kWaves * 64;
 constexpr int kStages = 4;                       // LDS ring depth (tiles resident)
 constexpr float kRescaleThreshold = 8.f;         // log2 units
+constexpr int kCachePolicyNT = 2;                // buffer-load cache policy: non-temporal
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void global_void_t;
@@ -359,8 +360,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
             const int cc = (lane % T::CPR) ^ swz<D>(lr);
             const int rc = min(rw0 + lr, rows_total - 1);
             const int off = (int)((((int64_t)(rc / G - t0) * H_q + rc % G) * D + cc * 8) * 2);
+            // (non-temporal: each Q row is read once, the L2 is kept for K/V)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(qo_lds + i * QROWS * D), 16,
-                                                     off, 0, 0, 0);
+                                                     off, 0, 0, kCachePolicyNT);
         }
     }
     if (n_tiles > 0) issue(0, 0);
@@ -657,8 +659,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         const int lr = i * QROWS + lane / T::CPR;
         const int cp = lane % T::CPR;
         const u32x4 val = *(const u32x4*)(qo_lds + lr * D + cp * 8);
-        if (rw0 + lr < rows_total)
-            *(u32x4*)(o + row_off(rw0 + lr) + ((cp ^ swz<D>(lr)) << 3)) = val;
+        if (rw0 + lr < rows_total)   // (non-temporal, as the Q rows)
+            __builtin_nontemporal_store(val, (u32x4*)(o + row_off(rw0 + lr) + ((cp ^ swz<D>(lr)) << 3)));
     }
 }
 
