@@ -128,3 +128,45 @@ def test_full_size_sampled(name):
     oref, lref = oracle.prefill(inp.q, inp.k, inp.v, causal=w.causal, q_offset=w.q_offset,
                                 rows=rows)
     assert_close(og.reshape(-1, w.d)[rows], oref, lg.reshape(-1)[rows], lref, name=name)
+
+
+def _staircase_scores(levels, *, causal, T=192, Hq=16, Hkv=2, d=128, seed=21):
+    """Q along one axis and K scaled along it so that every query row sees the
+    scores `levels[j]` (base-2 units after the kernel's scale * log2(e)) on key
+    tile j (64 keys each): all rows share the same score staircase.  The
+    products alpha * beta are exact in fp32, so the oracle and the kernel see
+    the same scores."""
+    S = 64 * len(levels)
+    q_offset = S - T if causal else 0      # causal: the chunk ends at the last key
+    inp = gin.random_case("prefill", "bf16", B=1, H_q=Hq, H_kv=Hkv, d=d, T_q=T, S_kv=S, seed=seed)
+    c = (1.0 / np.sqrt(d)) * np.log2(np.e)
+    alpha = 8.0
+    qf = np.zeros(inp.q.shape, np.float32)
+    qf[..., 0] = alpha
+    beta = np.repeat(np.asarray(levels, np.float64) / (c * alpha), 64).astype(np.float32)
+    kf = np.zeros(inp.k.shape, np.float32)
+    kf[0, :, :, 0] = beta[:, None]
+    for name, arr in (("q", qf), ("k", kf)):
+        bits = gin.bf16_round_bits(arr)
+        getattr(inp, name + "_store")[...] = bits
+        getattr(inp, name)[...] = gin.bf16_bits_to_f32(bits)
+    og, lg = _run(inp, causal, q_offset)
+    oref, lref = oracle.prefill(inp.q, inp.k, inp.v, causal=causal, q_offset=q_offset)
+    return og, lg, oref, lref
+
+
+@pytest.mark.parametrize("levels", [
+    # tile 1: every P = 2^5 against the reference set by tile 0, so each
+    # lane's sum of P exceeds 2^8 with no row max grown by more than 8 (the
+    # row max is taken and P recomputed unchanged); tile 2 likewise just
+    # below the rescale threshold; tile 3 grows by 12 (rescale); tile 4 back
+    # under the reference (fast path); tile 5 grows again
+    [0.0, 5.0, 7.9, 12.0, 9.0, 24.0, 3.0],
+    # falling scores: the first tile sets the reference, every later tile
+    # takes the fast path
+    [10.0, 6.0, 2.0, -3.0, -8.0, -20.0],
+])
+@pytest.mark.parametrize("causal", [False, True])
+def test_softmax_reference_paths(levels, causal):
+    og, lg, oref, lref = _staircase_scores(levels, causal=causal)
+    assert_close(og, oref, lg, lref, name=f"score staircase {levels} causal={causal}")
