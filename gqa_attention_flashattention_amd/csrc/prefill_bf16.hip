@@ -260,7 +260,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         }
         b = bid % B;
         mb = bid / B;
-        if (CAUSAL) mb = n_mblk - 1 - mb;
+        // causal row blocks run longest-first; window blocks (all about as
+        // long) in ascending order, so a block's lowest window tiles, which
+        // it processes first, were loaded into the XCD's L2 by the blocks
+        // before it, and its new keys come last, behind the tile read-ahead
+        if (CAUSAL && !WINDOW) mb = n_mblk - 1 - mb;
         key_row0 = (int64_t)b * S_kv;
         prow = (int64_t)b * n_split + split;
     }
@@ -452,15 +456,32 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         bool need_mask = key0 + TK > wave_full;
         if (WINDOW) need_mask = need_mask || (key0 + TK > sink && key0 < wave_win_all);
         if (need_mask) {
+            if constexpr (WINDOW) {
+                // element i of s[kb] is key key0 + 8 hh + cc, cc = 32 kb + 16
+                // (i / 8) + i % 8: hidden past the row's last key or inside
+                // [sink, win_lo) (one unsigned range compare), written
+                // branch-free so that the compiler emits compares and selects
+                // (the short-circuit form became a branch per element)
+                const int lim = last_key - key0 - 8 * hh;
+                const int wbase = key0 + 8 * hh - sink;
+                const unsigned wlen = (unsigned)max(win_lo - sink, 0);
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = key0 + kb * 32 + (i >> 3) * 16 + hh * 8 + (i & 7);
-                    bool hide = key > last_key;
-                    if (WINDOW) hide = hide || (key >= sink && key < win_lo);
-                    if (hide) s[kb][i] = -INFINITY;
-                }
+                    for (int i = 0; i < 16; ++i) {
+                        const int cc = kb * 32 + (i >> 3) * 16 + (i & 7);
+                        const bool hide = (cc > lim) | ((unsigned)(wbase + cc) < wlen);
+                        s[kb][i] = hide ? -INFINITY : s[kb][i];
+                    }
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = key0 + kb * 32 + (i >> 3) * 16 + hh * 8 + (i & 7);
+                        if (key > last_key) s[kb][i] = -INFINITY;
+                    }
+            }
         }
         // exponentials against the current reference max first; a lane whose
         // P sum exceeds 2^8 (infinite while a row with visible keys has no
@@ -479,8 +500,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
                 }
             return ps;
         };
-        float psum = expsum(fmaxf(m_run * c, -1e30f));
-        if (__builtin_amdgcn_ballot_w64(psum > 256.f) != 0) {
+        // (the first tile has no reference max in any row: take the row max
+        // directly; O and l are still zero, so there is nothing to rescale)
+        // (window blocks are short: their first tile takes the row max
+        // directly, with nothing to rescale since O and l are still zero)
+        const bool first = WINDOW && j == 0;
+        float psum = first ? 0.f : expsum(fmaxf(m_run * c, -1e30f));
+        if (first || __builtin_amdgcn_ballot_w64(psum > 256.f) != 0) {
             float mt;
             if constexpr (KB == 2) {
                 float mt0 = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
@@ -502,10 +528,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
                                                            false, false);
                 mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
             }
-            const bool grow = mt * c > m_run * c + kRescaleThreshold;
-            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            if (first) {
+                m_run = mt;
+            } else if (__builtin_amdgcn_ballot_w64(mt * c > m_run * c + kRescaleThreshold) != 0) {
                 const float m_new = fmaxf(m_run, mt);
-                // 0 on the first tile; a row with no visible key so far keeps corr = 1
+                // 0 for a row's first visible keys; a row with no visible key
+                // so far keeps corr = 1
                 const float corr = (m_new == -INFINITY) ? 1.f : fast_exp2((m_run - m_new) * c);
                 l_run *= corr;
 #pragma unroll
