@@ -432,9 +432,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int key = key0 + g4 + 16 * blk + 4 * i;
-                        bool hide = key >= vis_end[h];
-                        if (RING) hide = hide || (key >= s_end && key < wbeg[h]);
-                        if (hide) s[h][blk][i] = -INFINITY;
+                        if constexpr (RING) {
+                            // branch-free: past the visible end, or in the ring's
+                            // gap [s_end, wbeg) (one unsigned range compare)
+                            const bool hide =
+                                (key >= vis_end[h]) |
+                                ((unsigned)(key - s_end) < (unsigned)max(wbeg[h] - s_end, 0));
+                            s[h][blk][i] = hide ? -INFINITY : s[h][blk][i];
+                        } else {
+                            if (key >= vis_end[h]) s[h][blk][i] = -INFINITY;
+                        }
                     }
         }
         float corr[NH];
@@ -801,9 +808,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, R =
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int key = key0 + g4 + 16 * blk + 4 * e;
-                        bool hide = key >= vis_end[h];
-                        if (RING) hide = hide || (key >= s_end && key < wbeg[h]);
-                        if (hide) s[h][blk][e] = -INFINITY;
+                        if constexpr (RING) {
+                            // branch-free: past the visible end, or in the ring's
+                            // gap [s_end, wbeg) (one unsigned range compare)
+                            const bool hide =
+                                (key >= vis_end[h]) |
+                                ((unsigned)(key - s_end) < (unsigned)max(wbeg[h] - s_end, 0));
+                            s[h][blk][e] = hide ? -INFINITY : s[h][blk][e];
+                        } else {
+                            if (key >= vis_end[h]) s[h][blk][e] = -INFINITY;
+                        }
                     }
         }
         bf16x8 pb[NH];
