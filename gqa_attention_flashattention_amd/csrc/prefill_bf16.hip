@@ -550,29 +550,38 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         l_run += psum;
     };
     // O^T += V^T P^T of tile j; V^T operands read one 16-key step ahead, the
-    // first step's at the end of the preceding softmax phase (vpre)
+    // first two steps' at the end of the preceding softmax phase (vpre): an
+    // LDS read issued between the MFMAs of the MFMA phase delays the next
+    // MFMA issue (the phase runs at ~42 cycles per 32-cycle MFMA with its
+    // operand reads, ~33 with operands from registers), while the softmax
+    // phase beside it on the SIMD has room for them.
     auto vread = [&](const uint16_t* vt, int kst, int db) __attribute__((always_inline)) {
         const s16x4 lo = lds_read_tr16(vt + kst * 16 * D + off.v[0][db]);
         const s16x4 hi = lds_read_tr16(vt + kst * 16 * D + off.v[1][db]);
         return s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
-    s16x8 vpre[DBLK];
+    constexpr int NPRE = 2;   // 16-key steps of V^T read ahead (32 VGPRs)
+    s16x8 vpre[NPRE][DBLK];
     auto pv_pre = [&](int j, const uint16_t* vt) __attribute__((always_inline)) {
         if (!needs(j)) return;
 #pragma unroll
-        for (int db = 0; db < DBLK; ++db) vpre[db] = vread(vt, 0, db);
+        for (int ps = 0; ps < NPRE; ++ps)
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db) vpre[ps][db] = vread(vt, ps, db);
     };
     auto pv = [&](int j, const uint16_t* vt) __attribute__((always_inline)) {
         if (!needs(j)) return;
         s16x8 va[2][DBLK];
 #pragma unroll
-        for (int db = 0; db < DBLK; ++db) va[0][db] = vpre[db];
+        for (int db = 0; db < DBLK; ++db) va[0][db] = vpre[0][db];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kst = 0; kst < 2 * KB; ++kst) {   // 16-key steps
             if (kst + 1 < 2 * KB) {
 #pragma unroll
-                for (int db = 0; db < DBLK; ++db) va[(kst + 1) & 1][db] = vread(vt, kst + 1, db);
+                for (int db = 0; db < DBLK; ++db)
+                    va[(kst + 1) & 1][db] = kst + 1 < NPRE ? vpre[kst + 1 < NPRE ? kst + 1 : 0][db]
+                                                           : vread(vt, kst + 1, db);
             }
             __builtin_amdgcn_sched_barrier(0);
             const int kb = kst >> 1, half = kst & 1;
